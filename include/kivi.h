@@ -1,0 +1,175 @@
+/*
+ * kivi.h -- C ABI of a KIVI-style low-bit KV cache for MI355X (gfx950).
+ *
+ * The method (the KIVI explainer page, "ICML 2024論文解説: KIVI — チューニング不要の
+ * KVキャッシュ2bit非対称量子化"):
+ *   - section 量子化アルゴリズム: b-bit asymmetric uniform quantization,
+ *     Q(X) = clamp(round((X - z) / s), 0, 2^b - 1), D(X^) = s X^ + z, with
+ *     s = (max - min) / (2^b - 1) and z = min over each group;
+ *   - section Per-Channel量子化（Key Cache）: keys take their statistics per
+ *     channel (here: per channel over each block of k_block = 32 tokens);
+ *   - section Per-Token量子化（Value Cache）: values take theirs per token (here:
+ *     per token over each group of v_group = 32 channels), quantized once a
+ *     group of tokens has accumulated;
+ *   - section 残差バッファ（Residual Buffer）: the newest tokens stay fp16 and
+ *     decode attention is one softmax over [D(K_quant); K_res] and
+ *     [D(V_quant); V_res], scaled by 1/sqrt(head_dim);
+ *   - section アルゴリズム (QuantConfig): b = 2, group sizes 32, residual 128.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative kivi_status. Nothing aborts.
+ *   - Arguments are validated before anything is launched; a call that fails
+ *     validation changes no state. kivi_last_error() then describes the fault.
+ *   - Device pointers are plain HIP device addresses; `stream` is a hipStream_t
+ *     (NULL = the default stream). Calls only enqueue work on that stream and
+ *     never synchronise. Host-side counters advance when the call returns.
+ *   - The caller owns every device buffer (the cache memory, inputs, outputs);
+ *     inputs must stay valid until the stream has executed the call.
+ *   - A handle is not thread-safe; distinct handles are independent.
+ *   - A launch failure (KIVI_E_DEVICE) leaves the handle unusable: later calls
+ *     on it return KIVI_E_STATE. kivi_cache_reset() clears that condition.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KIVI_ABI_VERSION 1
+
+typedef enum {
+    KIVI_OK = 0,
+    KIVI_E_INVAL = -1,       /* bad argument or shape */
+    KIVI_E_UNSUPPORTED = -2, /* bits / head_dim / group sizes outside the supported set */
+    KIVI_E_NOMEM = -3,       /* the memory given to kivi_cache_create is too small */
+    KIVI_E_CAPACITY = -4,    /* the append would exceed max_tokens */
+    KIVI_E_EMPTY = -5,       /* attention on a cache holding no token */
+    KIVI_E_DEVICE = -6,      /* a HIP launch failed (message from hipGetErrorString) */
+    KIVI_E_STATE = -7        /* the handle saw an earlier device failure */
+} kivi_status;
+
+enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
+
+/* Shape and quantization settings of one cache (one attention layer).
+ * Supported: head_dim in {64, 128, 256}; bits in {2, 4}; k_block = v_group = 32;
+ * residual a multiple of k_block (0 allowed); n_q_heads a multiple of
+ * n_kv_heads; max_tokens >= 1; max_splits = 0 (library default, 256) or
+ * 2..4096. Every sequence of the batch holds the same number of tokens. */
+typedef struct {
+    int32_t batch;       /* B */
+    int32_t n_kv_heads;  /* Hkv; a "unit" is one (batch row, KV head): unit = b * Hkv + h */
+    int32_t n_q_heads;   /* Hq; query head i reads KV head i / (Hq / Hkv) */
+    int32_t head_dim;    /* d */
+    int32_t bits;        /* b */
+    int32_t k_block;     /* G: tokens per key statistics block */
+    int32_t v_group;     /* channels per value statistics group */
+    int32_t residual;    /* R: tokens kept fp16 after a flush */
+    int32_t max_tokens;  /* capacity of every sequence */
+    int32_t max_splits;  /* split-K partial slots per query head (0 = default) */
+} kivi_config;
+
+/* Device-memory layout of a cache, a pure function of the config. All offsets
+ * are in bytes from the start of the cache memory and are multiples of 256.
+ *
+ * Quantized blocks: unit u, key block j (tokens [jG, jG+G)) is one record at
+ *   off_blocks + u * unit_stride + j * block_bytes, holding in order:
+ *     kcode [G][W] uint32   W = head_dim * bits / 32; row t = token jG+t
+ *     vcode [G][W] uint32
+ *     ksz   [head_dim][2] float32   (scale, zero) of each channel over the block
+ *     vsz   [G][head_dim / v_group][2] float32   (scale, zero) of each token's groups
+ *   at record offsets rec_kcode, rec_vcode, rec_ksz, rec_vsz. In a code row,
+ *   word w holds channels [w*32/b, (w+1)*32/b); channel w*32/b + i sits at
+ *   bits [b*i, b*i + b).
+ * Residual ring: unit u, slot r (token t lives in slot t mod ring_slots) is
+ *   off_ring + u * ring_unit_stride + r * 4 * head_dim: the token's fp16 key
+ *   row (head_dim halves) followed by its fp16 value row.
+ * Split-K partials: off_partial + ((b * Hq + i) * max_splits + s) * partial_stride,
+ *   float32 [head_dim] weighted value sum, then the running maximum (base-2
+ *   log domain) and the weight sum. Scratch for kivi_attend_decode. */
+typedef struct {
+    size_t total_bytes;
+    size_t off_blocks, unit_stride, block_bytes;
+    size_t rec_kcode, rec_vcode, rec_ksz, rec_vsz;
+    int64_t max_blocks; /* key blocks a unit can hold = floor(max_tokens / G) */
+    size_t off_ring, ring_unit_stride;
+    int64_t ring_slots; /* R + G */
+    size_t off_partial, partial_stride;
+    int32_t max_splits;
+} kivi_layout;
+
+/* Counters of a cache. Tokens [0, n_quant) are quantized, [n_quant, n_tokens)
+ * are the fp16 residual (n_resid of them); n_quant is a multiple of G. */
+typedef struct {
+    int64_t n_tokens, n_quant, n_resid;
+} kivi_state;
+
+typedef struct kivi_cache kivi_cache;
+
+/* Bytes of device memory a cache with this config needs. */
+int kivi_cache_bytes(const kivi_config* cfg, size_t* bytes);
+
+/* The layout above for this config. */
+int kivi_cache_layout(const kivi_config* cfg, kivi_layout* layout);
+
+/* Make a handle over caller-owned device memory `dev_mem` of `bytes` bytes
+ * (at least kivi_cache_bytes; 256-byte aligned). Launches nothing. The cache
+ * starts empty. dev_mem must outlive the handle. */
+int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_cache** out);
+
+/* Frees the host handle only (the device memory stays the caller's). */
+int kivi_cache_destroy(kivi_cache* cache);
+
+/* Empty the cache (host counters only; launches nothing). */
+int kivi_cache_reset(kivi_cache* cache);
+
+/* Append ntok >= 1 tokens to every sequence. k, v: device fp16 [B][Hkv][ntok][d],
+ * contiguous. The result is defined token by token: the ring holds R + G
+ * slots, and a token arriving when it is full first quantizes the oldest G
+ * residual tokens (per-channel key blocks, per-token value groups). Tokens
+ * that leave the residual within this call are quantized straight from `k`
+ * and `v`; the rest are copied into the ring. KIVI_E_CAPACITY if n_tokens + ntok
+ * would exceed max_tokens. */
+int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, void* stream);
+
+/* Quantize the oldest floor((n_resid - R) / G) * G residual tokens (none if
+ * n_resid < R + G); *n_flushed (may be NULL) receives that count. */
+int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
+
+/* Decode attention of one query per head over every cached token:
+ * out[b][i] = sum_t softmax_t(q[b][i] . k_t / sqrt(d)) v_t, with k_t, v_t the
+ * dequantized (s * code + z, in fp32) or residual fp16 rows of KV head
+ * i / (Hq / Hkv). q: device [B][Hq][d] of q_dtype (KIVI_F16 / KIVI_BF16);
+ * out: device float32 [B][Hq][d]. Split-K over key blocks, then a
+ * log-sum-exp merge. KIVI_E_EMPTY on an empty cache. */
+int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
+
+/* Current counters. */
+int kivi_cache_query(const kivi_cache* cache, kivi_state* state);
+
+/* Counters the cache would have after kivi_append(ntok) (host only). */
+int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after);
+
+/* Split plan kivi_attend_decode would use now: *n_split work items per unit
+ * (key-block splits plus one residual split when n_resid > 0), and the key
+ * blocks per split. */
+int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split);
+
+/* Force the number of key-block splits per unit (0 = automatic). Results are
+ * the same up to fp32 rounding for every choice; for tests and tuning. */
+int kivi_set_attend_splits(kivi_cache* cache, int32_t n_key_splits);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* kivi_last_error(void);
+
+/* KIVI_ABI_VERSION of the loaded library. */
+int kivi_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

@@ -1,0 +1,58 @@
+// launch.hpp -- arguments of the gfx950 kernels and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kivi {
+
+// Geometry shared by every kernel of one cache.
+struct CacheGeom {
+    uint8_t* base;            // start of the cache memory
+    size_t off_blocks, unit_stride, block_bytes;
+    size_t rec_kcode, rec_vcode, rec_ksz, rec_vsz;
+    size_t off_ring, ring_unit_stride;
+    int64_t ring_slots;
+    size_t off_partial, partial_stride;  // partial_stride in bytes
+    int32_t max_splits;
+    int32_t batch, n_kv_heads, n_q_heads, head_dim, bits;
+};
+
+// Quantize key blocks [j0, j1) of every unit. Token t of a block comes from
+// the ring when t < ring_end, else from input row t - ring_end of k / v
+// ([units][ntok][d] fp16).
+struct QuantArgs {
+    CacheGeom g;
+    int64_t j0, j1;
+    int64_t ring_end;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t ntok;
+};
+
+// Copy tokens [t0, t1) of every unit from input rows (t - in_t0) into the ring.
+struct RingArgs {
+    CacheGeom g;
+    int64_t t0, t1, in_t0;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t ntok;
+};
+
+struct AttendArgs {
+    CacheGeom g;
+    const uint16_t* q;
+    int32_t q_bf16;
+    float* out;
+    int64_t n_tokens, n_quant, n_blocks;
+    int32_t n_key_splits, blocks_per_split, n_split;
+    float scale_log2;  // log2(e) / sqrt(d)
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_ring_write(const RingArgs& a, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace kivi

@@ -1,0 +1,151 @@
+// planner.hpp -- host-side layout and scheduling of the KIVI cache.
+//
+// Pure C++ (no HIP): validation of a kivi_config, the device-memory layout,
+// and the bookkeeping of the fp16 residual ring (which tokens a call
+// quantizes, which it copies into the ring), plus the split-K plan of the
+// decode attention. Everything here runs on the host before any launch.
+//
+// Ring semantics follow the KIVI explainer page ("ICML 2024論文解説: KIVI"),
+// section 残差バッファ（Residual Buffer） and section Per-Token量子化（Value Cache）:
+// the newest tokens stay fp16 and a whole group of G tokens is quantized once
+// it leaves the newest R. Reading used here: a ring of R + G slots; a token
+// arriving at a full ring first quantizes the oldest G residual tokens; an
+// explicit flush quantizes floor((n_res - R) / G) * G of them. The closed forms
+// below give the same counters as that token-by-token rule.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "kivi.h"
+
+namespace kivi {
+
+constexpr int32_t kDefaultMaxSplits = 256;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Returns KIVI_OK or an error code with a message in `err`.
+inline int validate_config(const kivi_config* c, std::string& err) {
+    if (!c) { err = "config is NULL"; return KIVI_E_INVAL; }
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1) {
+        err = "batch, n_kv_heads, n_q_heads and max_tokens must be >= 1";
+        return KIVI_E_INVAL;
+    }
+    if (c->n_q_heads % c->n_kv_heads != 0) {
+        err = "n_q_heads must be a multiple of n_kv_heads";
+        return KIVI_E_INVAL;
+    }
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
+        err = "head_dim must be 64, 128 or 256";
+        return KIVI_E_UNSUPPORTED;
+    }
+    if (c->bits != 2 && c->bits != 4) { err = "bits must be 2 or 4"; return KIVI_E_UNSUPPORTED; }
+    if (c->k_block != 32 || c->v_group != 32) {
+        err = "k_block and v_group must be 32";
+        return KIVI_E_UNSUPPORTED;
+    }
+    if (c->residual < 0 || c->residual % c->k_block != 0) {
+        err = "residual must be a non-negative multiple of k_block";
+        return KIVI_E_INVAL;
+    }
+    if (c->max_splits != 0 && (c->max_splits < 2 || c->max_splits > 4096)) {
+        err = "max_splits must be 0 or in [2, 4096]";
+        return KIVI_E_INVAL;
+    }
+    // units index grid dimension y of the launches (at most 65535)
+    int64_t units = (int64_t)c->batch * c->n_kv_heads;
+    if (units > 65535 || (int64_t)c->batch * c->n_q_heads > ((int64_t)1 << 30)) {
+        err = "batch * n_kv_heads must be <= 65535";
+        return KIVI_E_INVAL;
+    }
+    return KIVI_OK;
+}
+
+inline void compute_layout(const kivi_config* c, kivi_layout* L) {
+    const size_t d = (size_t)c->head_dim, G = (size_t)c->k_block;
+    const size_t W = d * (size_t)c->bits / 32;
+    const int64_t units = (int64_t)c->batch * c->n_kv_heads;
+    L->rec_kcode = 0;
+    L->rec_vcode = G * W * 4;
+    L->rec_ksz = L->rec_vcode + G * W * 4;
+    L->rec_vsz = L->rec_ksz + d * 8;
+    L->block_bytes = L->rec_vsz + G * (d / (size_t)c->v_group) * 8;
+    L->max_blocks = c->max_tokens / c->k_block;
+    L->off_blocks = 0;
+    L->unit_stride = align_up((size_t)L->max_blocks * L->block_bytes);
+    L->ring_slots = (int64_t)c->residual + c->k_block;
+    L->off_ring = align_up(L->off_blocks + (size_t)units * L->unit_stride);
+    L->ring_unit_stride = align_up((size_t)L->ring_slots * 4 * d);
+    L->off_partial = align_up(L->off_ring + (size_t)units * L->ring_unit_stride);
+    L->max_splits = c->max_splits ? c->max_splits : kDefaultMaxSplits;
+    L->partial_stride = (d + 4) * 4;
+    L->total_bytes = align_up(L->off_partial + (size_t)c->batch * c->n_q_heads *
+                                                   (size_t)L->max_splits * L->partial_stride);
+}
+
+// What one kivi_append(ntok) does, as closed forms of the token-by-token rule.
+struct AppendPlan {
+    int64_t nt0, nq0;   // counters before
+    int64_t nt1, nq1;   // counters after
+    int64_t ring_t0;    // tokens [ring_t0, nt1) are copied into the ring
+};
+
+inline AppendPlan plan_append(int64_t nt, int64_t nq, int64_t ntok, int64_t R, int64_t G) {
+    const int64_t C = R + G;
+    const int64_t total = (nt - nq) + ntok;  // residual tokens if nothing were flushed
+    // each implicit flush removes G tokens and happens only while the ring is full,
+    // so the count is the fewest flushes that bring the residual back to <= C
+    const int64_t flushes = total > C ? (total - C + G - 1) / G : 0;
+    AppendPlan p;
+    p.nt0 = nt;
+    p.nq0 = nq;
+    p.nt1 = nt + ntok;
+    p.nq1 = nq + flushes * G;
+    p.ring_t0 = p.nq1 > nt ? p.nq1 : nt;
+    return p;
+}
+
+// Tokens an explicit flush quantizes.
+inline int64_t plan_flush(int64_t nt, int64_t nq, int64_t R, int64_t G) {
+    const int64_t n_res = nt - nq;
+    return n_res < R ? 0 : ((n_res - R) / G) * G;
+}
+
+struct AttendPlan {
+    int32_t n_key_splits;     // splits over the quantized blocks
+    int32_t blocks_per_split;
+    int32_t n_split;          // n_key_splits + (residual present)
+};
+
+// Split-K plan: enough work-groups to fill the chip (about 2048 in total),
+// every key split non-empty, at most max_splits partials per query head.
+inline AttendPlan plan_attend(int64_t units, int64_t n_blocks, int64_t n_res, int32_t max_splits,
+                              int32_t forced_key_splits) {
+    AttendPlan p{0, 0, 0};
+    const int32_t res = n_res > 0 ? 1 : 0;
+    if (n_blocks > 0) {
+        int64_t want;
+        if (forced_key_splits > 0) {
+            want = forced_key_splits;
+        } else {
+            const int64_t target_wgs = 2048;
+            want = (target_wgs + units - 1) / units;
+            const int64_t min_blocks = 4;  // one per wave of a work-group
+            int64_t cap = (n_blocks + min_blocks - 1) / min_blocks;
+            if (want > cap) want = cap;
+        }
+        if (want > max_splits - res) want = max_splits - res;
+        if (want < 1) want = 1;
+        if (want > n_blocks) want = n_blocks;
+        int64_t bps = (n_blocks + want - 1) / want;
+        p.blocks_per_split = (int32_t)bps;
+        p.n_key_splits = (int32_t)((n_blocks + bps - 1) / bps);
+    }
+    p.n_split = p.n_key_splits + res;
+    return p;
+}
+
+}  // namespace kivi

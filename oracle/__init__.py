@@ -49,6 +49,7 @@ def lib():
         l.or_quant_group.argtypes = [P, i32, i32, P, P, P]
         l.or_pack_row.argtypes = [P, i32, i32, P]
         l.or_unpack_row.argtypes = [P, i32, i32, P]
+        l.or_pack_rows.argtypes = [P, i64, i32, i32, P]
         l.or_cache_new.restype = P
         l.or_cache_new.argtypes = [i32] * 9
         l.or_cache_free.argtypes = [P]
@@ -111,6 +112,15 @@ def pack_row(codes, bits: int) -> np.ndarray:
     d = codes.size
     words = np.empty(d * bits // 32, np.uint32)
     lib().or_pack_row(_ptr(codes), d, bits, _ptr(words))
+    return words
+
+
+def pack_rows(codes, bits: int) -> np.ndarray:
+    """[rows, d] codes -> [rows, d*bits/32] words."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rows, d = codes.shape
+    words = np.empty((rows, d * bits // 32), np.uint32)
+    lib().or_pack_rows(_ptr(codes), rows, d, bits, _ptr(words))
     return words
 
 

@@ -91,6 +91,10 @@ void or_pack_row(const uint8_t* codes, int d, int bits, uint32_t* words) {
     }
 }
 
+void or_pack_rows(const uint8_t* codes, int64_t rows, int d, int bits, uint32_t* words) {
+    for (int64_t r = 0; r < rows; ++r) or_pack_row(codes + r * d, d, bits, words + r * (d * bits / 32));
+}
+
 void or_unpack_row(const uint32_t* words, int d, int bits, uint8_t* codes) {
     int per = 32 / bits;
     uint32_t mask = (1u << bits) - 1u;

@@ -54,6 +54,8 @@ void or_quant_group(const float* x, int n, int bits, uint8_t* codes, float* s, f
  * code i of the word at bits [bits*i, bits*i+bits). */
 void or_pack_row(const uint8_t* codes, int d, int bits, uint32_t* words);
 void or_unpack_row(const uint32_t* words, int d, int bits, uint8_t* codes);
+/* or_pack_row over `rows` consecutive rows. */
+void or_pack_rows(const uint8_t* codes, int64_t rows, int d, int bits, uint32_t* words);
 
 /* The cache: B sequences x Hkv heads ("units"), each with its full fp16 history. */
 typedef struct or_cache or_cache;

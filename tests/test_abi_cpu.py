@@ -1,0 +1,278 @@
+"""CPU checks of the C ABI and of the host planner (no GPU needed).
+
+* libkivi.so loads and exports every function include/kivi.h declares;
+* argument validation returns the documented error codes before anything
+  would be launched;
+* the layout matches its closed form;
+* the host planner (planner.hpp, built here with g++ through a small shim)
+  reproduces the oracle's token-by-token residual ring on call sequences.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+
+
+@pytest.fixture(scope="module")
+def native():
+    from kv_cache_compression_kivi_amd import _native
+    if not os.path.exists(_native.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _native
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(native):
+    lib = native.load_library()
+    declared = _declared_functions()
+    assert "kivi_attend_decode" in declared and "kivi_append" in declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(native.EXPORTED)
+    assert native.kivi_abi_version() == 1
+    nm = subprocess.run(["nm", "-D", "--defined-only", native.library_path()], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(r"\bT " + name + r"\b", nm), name
+
+
+def _cfg(native, **kw):
+    base = dict(batch=2, n_kv_heads=4, n_q_heads=8, head_dim=128, bits=2, max_tokens=1000)
+    base.update(kw)
+    return native.make_config(**base)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=96), "KIVI_E_UNSUPPORTED"),
+    (dict(bits=3), "KIVI_E_UNSUPPORTED"),
+    (dict(k_block=16), "KIVI_E_UNSUPPORTED"),
+    (dict(v_group=64), "KIVI_E_UNSUPPORTED"),
+    (dict(n_q_heads=6), "KIVI_E_INVAL"),
+    (dict(batch=0), "KIVI_E_INVAL"),
+    (dict(residual=100), "KIVI_E_INVAL"),
+    (dict(max_splits=1), "KIVI_E_INVAL"),
+    (dict(batch=70000, n_kv_heads=1, n_q_heads=1), "KIVI_E_INVAL"),
+])
+def test_config_validation(native, bad, status):
+    with pytest.raises(native.KiviError) as e:
+        native.kivi_cache_bytes(_cfg(native, **bad))
+    assert e.value.status == status
+    assert native.kivi_last_error()
+
+
+@pytest.mark.parametrize("bits,d", [(2, 128), (4, 128), (2, 64), (4, 256)])
+def test_layout_closed_form(native, bits, d):
+    cfg = _cfg(native, bits=bits, head_dim=d, max_tokens=4096)
+    L = native.kivi_cache_layout(cfg)
+    G, W = 32, d * bits // 32
+    assert (L.rec_kcode, L.rec_vcode, L.rec_ksz, L.rec_vsz) == (0, G * W * 4, 2 * G * W * 4, 2 * G * W * 4 + d * 8)
+    assert L.block_bytes == 2 * G * W * 4 + d * 8 + G * (d // 32) * 8
+    if d == 128:
+        assert L.block_bytes == {2: 4096, 4: 6144}[bits]
+    assert L.max_blocks == 128 and L.ring_slots == 160
+    units = 2 * 4
+    for off in (L.off_blocks, L.off_ring, L.off_partial, L.unit_stride, L.ring_unit_stride, L.total_bytes):
+        assert off % 256 == 0
+    assert L.off_ring >= units * L.max_blocks * L.block_bytes
+    assert L.off_partial >= L.off_ring + units * 160 * 4 * d
+    assert L.partial_stride == (d + 4) * 4 and L.max_splits == 256
+    assert L.total_bytes >= L.off_partial + 2 * 8 * 256 * L.partial_stride
+    assert native.kivi_cache_bytes(cfg) == L.total_bytes
+
+
+def test_create_and_host_only_calls(native):
+    cfg = _cfg(native)
+    n = native.kivi_cache_bytes(cfg)
+    fake = 1 << 40  # never dereferenced: create and the planning calls launch nothing
+    with pytest.raises(native.KiviError) as e:
+        native.kivi_cache_create(cfg, fake, n - 1)
+    assert e.value.status == "KIVI_E_NOMEM"
+    with pytest.raises(native.KiviError) as e:
+        native.kivi_cache_create(cfg, fake + 16, n)
+    assert e.value.status == "KIVI_E_INVAL"
+    h = native.kivi_cache_create(cfg, fake, n)
+    try:
+        st = native.kivi_cache_query(h)
+        assert (st.n_tokens, st.n_quant, st.n_resid) == (0, 0, 0)
+        st = native.kivi_plan_append(h, 1000)
+        assert (st.n_tokens, st.n_quant, st.n_resid) == (1000, 864, 136)
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_plan_append(h, 1001)
+        assert e.value.status == "KIVI_E_CAPACITY"
+        # validation failures happen before any launch and leave the state alone
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append(h, fake, fake, 1001)
+        assert e.value.status == "KIVI_E_CAPACITY"
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append(h, 0, fake, 1)
+        assert e.value.status == "KIVI_E_INVAL"
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append(h, fake, fake, 0)
+        assert e.value.status == "KIVI_E_INVAL"
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_attend_decode(h, fake, 0, fake)
+        assert e.value.status == "KIVI_E_EMPTY"
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_attend_decode(h, fake, 7, fake)
+        assert e.value.status == "KIVI_E_INVAL"
+        assert native.kivi_flush(h) == 0  # nothing to flush: no launch
+        st = native.kivi_cache_query(h)
+        assert (st.n_tokens, st.n_quant) == (0, 0)
+        native.kivi_set_attend_splits(h, 3)
+        with pytest.raises(native.KiviError):
+            native.kivi_set_attend_splits(h, 256)
+    finally:
+        native.kivi_cache_destroy(h)
+
+
+# ---------------------------------------------------------------- host planner
+
+SHIM = r"""
+#include "planner.hpp"
+extern "C" {
+void shim_plan_append(int64_t nt, int64_t nq, int64_t ntok, int64_t R, int64_t G, int64_t* out) {
+    kivi::AppendPlan p = kivi::plan_append(nt, nq, ntok, R, G);
+    out[0] = p.nt1; out[1] = p.nq1; out[2] = p.ring_t0;
+}
+int64_t shim_plan_flush(int64_t nt, int64_t nq, int64_t R, int64_t G) { return kivi::plan_flush(nt, nq, R, G); }
+void shim_plan_attend(int64_t units, int64_t nb, int64_t nres, int32_t max_splits, int32_t forced, int32_t* out) {
+    kivi::AttendPlan p = kivi::plan_attend(units, nb, nres, max_splits, forced);
+    out[0] = p.n_key_splits; out[1] = p.blocks_per_split; out[2] = p.n_split;
+}
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    d = tmp_path_factory.mktemp("planner")
+    src = d / "shim.cpp"
+    src.write_text(SHIM)
+    so = d / "libshim.so"
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-fPIC", "-shared",
+                           "-I", os.path.join(ROOT, "include"),
+                           "-I", os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc"),
+                           str(src), "-o", str(so)])
+    lib = ctypes.CDLL(str(so))
+    i64 = ctypes.c_int64
+    lib.shim_plan_append.argtypes = [i64] * 5 + [ctypes.c_void_p]
+    lib.shim_plan_flush.argtypes = [i64] * 4
+    lib.shim_plan_flush.restype = i64
+    lib.shim_plan_attend.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    return lib
+
+
+def _plan_append(lib, nt, nq, ntok, R, G=32):
+    out = np.zeros(3, np.int64)
+    lib.shim_plan_append(nt, nq, ntok, R, G, out.ctypes.data_as(ctypes.c_void_p))
+    return tuple(int(x) for x in out)
+
+
+@pytest.mark.parametrize("R", [128, 0, 64])
+def test_planner_matches_oracle_sequences(planner, oracle_mod, R):
+    """Random append/flush sequences: the planner's closed forms give the same
+    counters as the oracle's token-by-token ring after every call."""
+    rng = np.random.default_rng(R + 1)
+    d, G = 32, 32
+    for trial in range(6):
+        T = 3000
+        oc = oracle_mod.OracleCache(1, 1, 1, d, 2, max_tokens=T, residual=R)
+        nt, nq = 0, 0
+        while nt < T - 300:
+            if rng.random() < 0.3:
+                k = int(planner.shim_plan_flush(nt, nq, R, G))
+                assert k == oc.flush()
+                nq += k
+            else:
+                ntok = int(rng.choice([1, 1, 1, 2, 31, 32, 33, 100, 160, 161, 250]))
+                nt1, nq1, ring_t0 = _plan_append(planner, nt, nq, ntok, R)
+                x = np.zeros((1, 1, ntok, d), np.float16)
+                oc.append(x, x)
+                assert (nt1, nq1) == oc.state(), (nt, nq, ntok)
+                assert ring_t0 == max(nq1, nt)
+                assert 0 <= nt1 - nq1 <= R + G
+                nt, nq = nt1, nq1
+
+
+def test_planner_config_states(planner):
+    """Prefill append(T) + flush gives n_q = floor((T - R) / G) * G for the workloads' T."""
+    for T, want in [(1024, 896), (4096, 3968), (8192, 8064), (131072, 130944)]:
+        nt, nq, _ = _plan_append(planner, 0, 0, T, 128)
+        nq += int(planner.shim_plan_flush(nt, nq, 128, 32))
+        assert nq == want
+
+
+def test_attend_plan(planner):
+    out = np.zeros(3, np.int32)
+    p = out.ctypes.data_as(ctypes.c_void_p)
+    for units, nb, nres in [(1, 28, 128), (256, 124, 128), (32, 4092, 128), (512, 255, 150), (1024, 124, 128),
+                            (3, 0, 5), (7, 1, 0), (1, 5000, 1)]:
+        for forced in (0, 1, 3, 17):
+            planner.shim_plan_attend(units, nb, nres, 256, forced, p)
+            nks, bps, nsplit = (int(x) for x in out)
+            assert nsplit == nks + (1 if nres > 0 else 0) <= 256
+            if nb:
+                assert nks >= 1 and bps >= 1
+                assert (nks - 1) * bps < nb <= nks * bps  # every key split non-empty, all blocks covered
+            else:
+                assert nks == 0
+
+
+SANITIZED_MAIN = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "planner.hpp"
+int main() {
+    // random append/flush walks under ASan/UBSan: counters stay consistent
+    unsigned x = 12345;
+    for (int R = 0; R <= 256; R += 32) {
+        int64_t nt = 0, nq = 0;
+        for (int step = 0; step < 20000; ++step) {
+            x = x * 1103515245u + 12345u;
+            if ((x >> 16) % 4 == 0) {
+                nq += kivi::plan_flush(nt, nq, R, 32);
+            } else {
+                int64_t ntok = 1 + (x >> 8) % 200;
+                kivi::AppendPlan p = kivi::plan_append(nt, nq, ntok, R, 32);
+                if (p.nq1 % 32 || p.nt1 - p.nq1 > R + 32 || p.nt1 - p.nq1 < 0 || p.ring_t0 < p.nq1) return 1;
+                nt = p.nt1; nq = p.nq1;
+            }
+            kivi::AttendPlan a = kivi::plan_attend(1 + (x >> 4) % 2000, nq / 32, nt - nq, 256, (x >> 3) % 5);
+            if (a.n_split > 256 || (nq > 0 && (int64_t)(a.n_key_splits - 1) * a.blocks_per_split >= nq / 32)) return 2;
+        }
+    }
+    kivi_config c{8, 32, 32, 128, 2, 32, 32, 128, 4096, 0};
+    std::string err;
+    if (kivi::validate_config(&c, err) != KIVI_OK) return 3;
+    kivi_layout L;
+    kivi::compute_layout(&c, &L);
+    std::printf("ok %zu\n", L.total_bytes);
+    return 0;
+}
+"""
+
+
+def test_planner_under_sanitizers(tmp_path):
+    src = tmp_path / "main.cpp"
+    src.write_text(SANITIZED_MAIN)
+    exe = tmp_path / "planner_san"
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=all",
+                           "-I", os.path.join(ROOT, "include"),
+                           "-I", os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc"),
+                           str(src), "-o", str(exe)])
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok ")
