@@ -1,0 +1,339 @@
+"""Benchmark of the KIVI cache hot path on one MI355X.
+
+Metric: decode-attention effective HBM GB/s (and % of the 8 TB/s peak), plus
+quantize-append tokens/s.
+
+A timed step is one decode step of the whole path over one batch: append one
+token per sequence (residual ring), flush when a whole 32-token group lies
+beyond the newest 128 (quantize-and-pack keys per channel, values per token),
+and the fused split-K decode attention over the packed cache and the fp16
+residual. `value` is the algorithmic bytes of those steps (attention reads of
+codes, scales, zeros and residual rows, query in, output out; the append and
+flush bytes) divided by the wall time of the K timed steps. Inputs are
+resident in HBM before the timed region starts.
+
+The 256 MB Infinity Cache would hold a whole llama2_7b_layer cache (147 MB),
+so steps rotate over independent caches whose total exceeds 1 GiB.
+
+Also measured in the same run:
+  * the attention kernel alone (one launch per kivi_attend_decode), timed with
+    HIP events on the stream it runs on, for the roofline entry;
+  * prefill quantize-append (append(T) + flush into an empty cache): tokens/s;
+  * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode-attention effective HBM GB/s (% of peak) + quantize-append tokens/s"
+
+
+# ---------------------------------------------------------------- byte accounting
+
+def bytes_per_quant_token(d, bits, G=32, vg=32):
+    """Key codes + value codes + key (s, z) share + value (s, z), per token per KV head."""
+    return 2 * d * bits // 8 + 8 * d // G + 8 * d // vg
+
+
+def attend_bytes(units, rows, d, bits, n_quant, n_resid):
+    """Algorithmic bytes of one decode attention: the packed part, the fp16
+    residual (key + value rows), each query head's fp16 query and fp32 output."""
+    return units * (n_quant * bytes_per_quant_token(d, bits) + n_resid * 4 * d) + rows * (2 * d + 4 * d)
+
+
+def append_bytes(units, d, ntok):
+    """fp16 key + value rows read and written into the ring."""
+    return units * ntok * 4 * d * 2
+
+
+def flush_bytes(units, d, bits, ntok):
+    """fp16 rows read from the ring, packed codes + statistics written."""
+    return units * ntok * (4 * d + bytes_per_quant_token(d, bits))
+
+
+def prefill_bytes(units, d, bits, T, n_quant):
+    """append(T) + flush into an empty cache: fp16 input read once; the packed
+    part and the residual written."""
+    return units * (T * 4 * d + n_quant * bytes_per_quant_token(d, bits) + (T - n_quant) * 4 * d)
+
+
+# ---------------------------------------------------------------- helpers
+
+def _kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc", "kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != _kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def _cpu_baseline(cfg, seconds=8.0):
+    """The oracle as it is, on the host cores: prefill-quantize and attention
+    over one batch row (all KV heads) of the workload, attention repeated until
+    about `seconds` have passed. Reported in the same units as the GPU line."""
+    import torch
+
+    import oracle
+    from kivi_inputs import KVWorkload
+
+    Hkv, Hq, d, T, bits = cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"], cfg.get("bits", 2)
+    wl = KVWorkload(1, Hkv, d, seed=cfg["seed"], device="cpu")
+    k, v = wl.kv(0, T)
+    q = wl.q(Hq)
+    oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
+    t0 = time.perf_counter()
+    oc.append(k, v)
+    oc.flush()
+    t_prefill = time.perf_counter() - t0
+    nt, nq = oc.state()
+    nbytes = attend_bytes(Hkv, Hq, d, bits, nq, nt - nq)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oc.attend(q)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    del torch
+    return {
+        "value": round(nbytes * n / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"1 batch row x {Hkv} KV heads x {T} tokens of the workload; attention repeated {n} times "
+                  f"in {el:.1f} s; prefill-quantize of the same sample {Hkv * T / t_prefill:.0f} tokens/s",
+        "quantize_append_tokens_per_s": round(Hkv * T / t_prefill, 1),
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_7b_layer",
+                    choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the KV cache units are independent per (batch row, KV head), "
+              "so a multi-GPU run would shard them with no communication; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_compression_kivi_amd as kv
+    from kivi_inputs import CONFIGS, KVWorkload
+
+    kv.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = dict(CONFIGS[args.workload])
+    B, Hkv, Hq, d, T = cfg["batch"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"]
+    units, rows = B * Hkv, B * Hq
+    layers = cfg.get("layers", 1)
+    layer_bits = cfg.get("layer_bits", [cfg.get("bits", 2)] * layers)
+    q_dtype = torch.bfloat16 if cfg.get("q_dtype") == "bf16" else torch.float16
+    total_steps = args.warmup + args.steps
+
+    # one cache per layer; rotate over copies when a step's working set would sit in the Infinity Cache
+    per_step_bytes = sum(attend_bytes(units, rows, d, b, ((T - 128) // 32) * 32, 128) for b in layer_bits)
+    n_rot = 1 if per_step_bytes >= (1 << 30) else min(16, int(-(-(1 << 30) // per_step_bytes)))
+    n_caches = n_rot * layers
+    max_tokens = T + -(-total_steps // n_rot) + 64
+    print(f"[bench] workload {args.workload}: {layers} layer(s) x {n_rot} rotation(s), "
+          f"{per_step_bytes / 1e6:.1f} MB per step", file=sys.stderr, flush=True)
+
+    caches = []
+    prefill_inputs = {}
+    for r in range(n_rot):
+        for layer in range(layers):
+            bits = layer_bits[layer]
+            wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], layer=layer + 1000 * r, device=dev)
+            k, v = wl.kv(0, T)
+            c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev)
+            c.append(k, v)
+            c.flush()
+            caches.append(c)
+            if r == 0 and layer in (0, layers - 1):
+                prefill_inputs[layer] = (k, v)
+            del k, v
+    torch.cuda.synchronize()
+
+    # decode inputs, resident before timing: a pool of new tokens and queries
+    wl0 = KVWorkload(B, Hkv, d, seed=cfg["seed"], device=dev)
+    pool = 32
+    new_kv = [wl0.kv(T + i, 1) for i in range(pool)]
+    queries = [wl0.q(Hq, step=i, dtype=q_dtype) for i in range(pool)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    s_ptr = stream.cuda_stream
+
+    lib = kv.load_library()
+    import ctypes
+    qd = kv.KIVI_BF16 if q_dtype == torch.bfloat16 else kv.KIVI_F16
+    nfl = ctypes.c_int32()
+    kvp = [(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr())) for a, b in new_kv]
+    qp = [ctypes.c_void_p(x.data_ptr()) for x in queries]
+    outp = ctypes.c_void_p(out.data_ptr())
+    sp = ctypes.c_void_p(s_ptr)
+    handles = [ctypes.c_void_p(c.handle) for c in caches]
+
+    def run_step(i):
+        r = i % n_rot
+        for layer in range(layers):
+            kp, vp = kvp[i % pool]
+            rc = lib.kivi_decode_step(handles[r * layers + layer], kp, vp, qp[i % pool], qd, outp, sp,
+                                      ctypes.byref(nfl))
+            if rc != 0:
+                raise kv.KiviError(rc, kv.kivi_last_error())
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    # the bytes of each step follow from the host counters alone: replay the
+    # counter arithmetic before timing (checked against the caches afterwards)
+    bytes_total = 0
+    sim_state = [c.state() for c in caches]
+    for i in range(args.warmup, total_steps):
+        r = i % n_rot
+        for layer in range(layers):
+            ci = r * layers + layer
+            nt, nq, nr = sim_state[ci]
+            nt, nr = nt + 1, nr + 1
+            b = append_bytes(units, d, 1)
+            if nr >= 128 + 32:
+                b += flush_bytes(units, d, layer_bits[layer], 32)
+                nq, nr = nq + 32, nr - 32
+            b += attend_bytes(units, rows, d, layer_bits[layer], nq, nr)
+            bytes_total += b
+            sim_state[ci] = (nt, nq, nr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        run_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ci, c in enumerate(caches):
+        assert c.state() == sim_state[ci], (c.state(), sim_state[ci])
+    ms_per_step = wall / args.steps * 1e3
+    value = bytes_total / wall / 1e9
+
+    # the attention kernel alone, HIP events on its stream, one cache per call
+    n_att = max(2 * n_caches, min(200, 20 * n_caches))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_att)]
+    att_bytes = []
+    for i in range(n_att):
+        c = caches[i % n_caches]
+        nt, nq, nr = c.state()
+        att_bytes.append(attend_bytes(units, rows, d, c.cfg.bits, nq, nr))
+    for i in range(min(n_caches, 8)):  # warm the launch path
+        caches[i].attend(queries[0], out=out)
+    torch.cuda.synchronize()
+    for i in range(n_att):
+        c = caches[i % n_caches]
+        evs[i][0].record(stream)
+        rc = lib.kivi_attend_decode(handles[i % n_caches], qp[i % pool], qd, outp, sp)
+        evs[i][1].record(stream)
+        if rc != 0:
+            raise kv.KiviError(rc, kv.kivi_last_error())
+    torch.cuda.synchronize()
+    att_ms = [a.elapsed_time(b) for a, b in evs]
+    att_avg_ms = sum(att_ms) / len(att_ms)
+    att_bytes_avg = sum(att_bytes) / len(att_bytes)
+    att_gbs = att_bytes_avg / (att_avg_ms * 1e-3) / 1e9
+
+    # prefill quantize-append: append(T) + flush into an empty cache
+    n_pf = min(len(caches), max(4, n_rot))
+    pf_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_pf)]
+    pf_bytes = 0
+    for i in range(n_pf):
+        c = caches[i]
+        layer = i % layers
+        k, v = prefill_inputs.get(layer, prefill_inputs[0])
+        c.reset()
+        pf_ev[i][0].record(stream)
+        c.append(k, v)
+        c.flush()
+        pf_ev[i][1].record(stream)
+        nt, nq, nr = c.state()
+        pf_bytes += prefill_bytes(units, d, c.cfg.bits, T, nq)
+    torch.cuda.synchronize()
+    pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
+    pf_tok_s = n_pf * B * Hkv * T / (pf_ms * 1e-3)
+    pf_gbs = pf_bytes / (pf_ms * 1e-3) / 1e9
+
+    traffic = _traffic_from_profile(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "n_kv_heads": Hkv, "n_q_heads": Hq, "head_dim": d,
+                   "tokens": T, "bits": layer_bits if layers > 1 else layer_bits[0], "layers": layers,
+                   "k_block": 32, "v_group": 32, "residual": 128, "q_dtype": str(q_dtype).replace("torch.", ""),
+                   "step": "append 1 token + flush when due + decode attention, per layer",
+                   "rotating_caches": n_rot},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "quantize_append_tokens_per_s": round(pf_tok_s, 1),
+        "quantize_append_gbs": round(pf_gbs, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kivi_attend_decode = attend_kernel (split-K partials) + combine_kernel (merge)",
+            "achieved": round(att_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(att_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(att_bytes_avg),
+            "avg_launch_us": round(att_avg_ms * 1e3, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            line["cpu_baseline"] = _cpu_baseline(cfg, seconds=args.cpu_seconds)
+        except Exception as e:  # the GPU line stands on its own
+            line["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -144,8 +144,19 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
  * dequantized (s * code + z, in fp32) or residual fp16 rows of KV head
  * i / (Hq / Hkv). q: device [B][Hq][d] of q_dtype (KIVI_F16 / KIVI_BF16);
  * out: device float32 [B][Hq][d]. Split-K over key blocks, then a
- * log-sum-exp merge. KIVI_E_EMPTY on an empty cache. */
+ * log-sum-exp merge of the splits. Concurrent calls on one cache (several
+ * streams) are not allowed: they share the split partials.
+ * KIVI_E_EMPTY on an empty cache. */
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
+
+/* One decode step in one call: kivi_append of one token per sequence (k, v:
+ * device fp16 [B][Hkv][1][d]), then kivi_flush if a whole group of G tokens
+ * lies beyond the newest R (so the residual cycles through R .. R+G-1 tokens
+ * at attention time), then kivi_attend_decode. *n_flushed (may be NULL)
+ * receives the tokens the flush quantized. Same contract and errors as the
+ * three calls; validation of all three happens before the first launch. */
+int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
+                     void* stream, int32_t* n_flushed);
 
 /* Current counters. */
 int kivi_cache_query(const kivi_cache* cache, kivi_state* state);

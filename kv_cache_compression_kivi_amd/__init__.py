@@ -26,6 +26,7 @@ from ._native import (  # noqa: F401
     kivi_cache_query,
     kivi_cache_reset,
     kivi_config,
+    kivi_decode_step,
     kivi_flush,
     kivi_last_error,
     kivi_layout,

@@ -67,6 +67,7 @@ _SIGS = {
     "kivi_plan_append": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(kivi_state)]),
     "kivi_plan_attend": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "kivi_set_attend_splits": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "kivi_decode_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -146,6 +147,15 @@ def kivi_flush(h: int, stream: int = 0) -> int:
 def kivi_attend_decode(h: int, q_ptr: int, q_dtype: int, out_ptr: int, stream: int = 0) -> None:
     _check(load_library().kivi_attend_decode(ctypes.c_void_p(h), ctypes.c_void_p(q_ptr), q_dtype,
                                              ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+
+def kivi_decode_step(h: int, k_ptr: int, v_ptr: int, q_ptr: int, q_dtype: int, out_ptr: int,
+                     stream: int = 0) -> int:
+    n = ctypes.c_int32()
+    _check(load_library().kivi_decode_step(ctypes.c_void_p(h), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                           ctypes.c_void_p(q_ptr), q_dtype, ctypes.c_void_p(out_ptr),
+                                           ctypes.c_void_p(stream), ctypes.byref(n)))
+    return n.value
 
 
 def kivi_cache_query(h: int) -> kivi_state:
@@ -246,6 +256,24 @@ class KiviCache:
             raise ValueError("out must be a contiguous float32 tensor shaped like q")
         kivi_attend_decode(self.handle, q.data_ptr(), KIVI_BF16 if q.dtype == torch.bfloat16 else KIVI_F16,
                            out.data_ptr(), self._stream(stream))
+        return out
+
+    def decode_step(self, k, v, q, out=None, stream=None) -> int:
+        """append(1) + flush when a full group is past the residual + attend; returns tokens flushed."""
+        import torch
+        self._check_kv(k, v)
+        c = self.cfg
+        if k.shape[2] != 1:
+            raise ValueError("decode_step appends exactly one token per sequence")
+        if q.dtype not in (torch.float16, torch.bfloat16) or not q.is_contiguous() or \
+                tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+            raise ValueError("q must be a contiguous fp16/bf16 [batch, n_q_heads, head_dim] tensor")
+        if out is None:
+            out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=q.device)
+        n = kivi_decode_step(self.handle, k.data_ptr(), v.data_ptr(), q.data_ptr(),
+                             KIVI_BF16 if q.dtype == torch.bfloat16 else KIVI_F16, out.data_ptr(),
+                             self._stream(stream))
+        self.last_flushed = n
         return out
 
     def state(self):

@@ -418,6 +418,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
         }
     }
     __syncthreads();
+    const size_t pstride = g.partial_stride / 4;
+    float* pbase = reinterpret_cast<float*>(g.base + g.off_partial);
     for (int idx = threadIdx.x; idx < QG * D; idx += 256) {
         const int gq = idx / D, c = idx % D;
         float M = sm[0][gq];
@@ -432,34 +434,37 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
                 O = fmaf(so[wv][gq][c], f, O);
             }
         }
-        float* rec = reinterpret_cast<float*>(
-            g.base + g.off_partial +
-            (((size_t)b * g.n_q_heads + qh0 + gq) * g.max_splits + split) * g.partial_stride);
+        float* rec = pbase + (((size_t)b * g.n_q_heads + qh0 + gq) * g.max_splits + split) * pstride;
         rec[c] = O;
         if (c == 0) {
             rec[D] = M;
             rec[D + 1] = L;
         }
     }
+
 }
 
-// Log-sum-exp merge of the splits of one (batch row, query head).
+// Log-sum-exp merge of the splits of one (batch row, query head), in split
+// order (deterministic). A separate launch: the kernel boundary makes every
+// split's partial visible, where an in-kernel merge would need device-scope
+// fences (full L2 write-back and invalidate on a multi-XCD part) in every
+// work-group.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
     const CacheGeom& g = a.g;
     const size_t row = blockIdx.x;
     const int c = threadIdx.x;
     const size_t stride = g.partial_stride / 4;
-    const float* base = reinterpret_cast<const float*>(g.base + g.off_partial) + row * g.max_splits * stride;
+    const float* rb = reinterpret_cast<const float*>(g.base + g.off_partial) + row * g.max_splits * stride;
     float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * stride + D]);
+    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, rb[s * stride + D]);
     float L = 0.f, O = 0.f;
     for (int s = 0; s < a.n_split; ++s) {
-        const float ms = base[s * stride + D];
+        const float ms = rb[s * stride + D];
         if (ms != -INFINITY) {
             const float f = exp2f(ms - M);
-            L = fmaf(base[s * stride + D + 1], f, L);
-            O = fmaf(base[s * stride + c], f, O);
+            L = fmaf(rb[s * stride + D + 1], f, L);
+            O = fmaf(rb[s * stride + c], f, O);
         }
     }
     a.out[row * D + c] = O / L;

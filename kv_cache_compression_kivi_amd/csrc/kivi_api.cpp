@@ -275,4 +275,23 @@ int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float*
     return KIVI_OK;
 }
 
+int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
+                     void* stream, int32_t* n_flushed) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
+    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
+    rc = kivi_append(cache, k, v, 1, stream);  // validates k, v and the capacity before launching
+    if (rc != KIVI_OK) return rc;
+    int32_t flushed = 0;
+    const int64_t n_res = cache->n_tokens - cache->n_quant;
+    if (n_res >= (int64_t)cache->cfg.residual + cache->cfg.k_block) {
+        rc = kivi_flush(cache, stream, &flushed);
+        if (rc != KIVI_OK) return rc;
+    }
+    if (n_flushed) *n_flushed = flushed;
+    return kivi_attend_decode(cache, q, q_dtype, out, stream);
+}
+
 }  // extern "C"
