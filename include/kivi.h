@@ -164,14 +164,16 @@ int kivi_cache_query(const kivi_cache* cache, kivi_state* state);
 /* Counters the cache would have after kivi_append(ntok) (host only). */
 int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after);
 
-/* Split plan kivi_attend_decode would use now: *n_split work items per unit
- * (key-block splits plus one residual split when n_resid > 0), and the key
- * blocks per split. */
+/* Split plan kivi_attend_decode would use now: *n_split work-groups per
+ * (unit, query-head chunk) along the tokens (the last also takes the fp16
+ * residual; with more than one, a merge kernel follows), and about
+ * *blocks_per_split key blocks in each. */
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split);
 
-/* Force the number of key-block splits per unit (0 = automatic). Results are
- * the same up to fp32 rounding for every choice; for tests and tuning. */
-int kivi_set_attend_splits(kivi_cache* cache, int32_t n_key_splits);
+/* Force the split count of kivi_attend_decode (0 = automatic, else
+ * 1..max_splits). Results agree up to fp32 rounding for every choice; for
+ * tests and tuning. */
+int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split);
 
 /* Message describing the last failing call on this thread ("" if none). */
 const char* kivi_last_error(void);

@@ -1,0 +1,183 @@
+// codec.hip -- gfx950 kernels that write the KIVI cache: quantize-and-pack of
+// key blocks and value tokens, and the fp16 residual-ring append.
+//
+// The arithmetic follows the KIVI explainer page ("ICML 2024論文解説: KIVI —
+// チューニング不要のKVキャッシュ2bit非対称量子化"):
+//   section 量子化アルゴリズム: Q(X) = clamp(round((X - z)/s), 0, 2^b - 1),
+//     D(X^) = s X^ + z, s = (max - min)/(2^b - 1), z = min per group;
+//   section Per-Channel量子化 / Per-Token量子化: keys per channel (over a block
+//     of 32 tokens here), values per token (over 32-channel groups here);
+//   section アルゴリズム: s floored at 1e-8, round then clamp;
+//   section 残差バッファ: the newest tokens stay fp16 in the ring.
+//
+// The codec runs in IEEE fp32 (correctly rounded division, round-half-even,
+// no contraction: the library is built with -ffp-contract=off), so its bytes
+// are reproducible on any IEEE machine.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace kivi {
+namespace {
+
+constexpr int kG = 32;   // tokens per key block
+constexpr int kVG = 32;  // channels per value group
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return __half2float(__ushort_as_half(h));
+}
+
+// ------------------------------------------------------------------ codec
+
+// One group of N values -> (s, z) and codes written to out[i * stride].
+template <int N, int BITS>
+__device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float& z, uint8_t* out,
+                                            int stride) {
+    constexpr float kQmax = float((1 << BITS) - 1);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        mn = x[i] < mn ? x[i] : mn;
+        mx = x[i] > mx ? x[i] : mx;
+    }
+    s = (mx - mn) / kQmax;
+    if (!(s >= 1e-8f)) s = 1e-8f;
+    z = mn + 0.0f;  // -0 -> +0
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float r = __builtin_rintf((x[i] - z) / s);
+        r = r < 0.0f ? 0.0f : r;
+        r = r > kQmax ? kQmax : r;
+        out[i * stride] = (uint8_t)r;
+    }
+}
+
+// One work-group per (key block j, unit): 2*D threads. Threads [0, D) take
+// one key channel each over the block's 32 tokens; threads [D, 2D) take one
+// (token, 32-channel value group) each. Then all threads pack words.
+template <int D, int BITS>
+__global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
+    constexpr int NG = D / kVG;
+    constexpr int W = D * BITS / 32;
+    constexpr int PER = 32 / BITS;
+    constexpr int NT = 2 * D;
+    constexpr int CPR = D / 8;  // 16-byte chunks per fp16 row
+    __shared__ __align__(16) uint16_t sk[kG * D];
+    __shared__ __align__(16) uint16_t sv[kG * D];
+    __shared__ __align__(16) uint8_t ck[kG * D];
+    __shared__ __align__(16) uint8_t cv[kG * D];
+
+    const CacheGeom& g = a.g;
+    const int tid = threadIdx.x;
+    const int64_t j = a.j0 + blockIdx.x;
+    const int64_t u = blockIdx.y;
+
+    for (int idx = tid; idx < kG * CPR; idx += NT) {
+        const int t = idx / CPR, c16 = idx % CPR;
+        const int64_t tok = j * kG + t;
+        const uint4 *ks, *vs;
+        if (tok < a.ring_end) {
+            const uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
+                                  (size_t)(tok % g.ring_slots) * 4 * D;
+            ks = reinterpret_cast<const uint4*>(slot) + c16;
+            vs = reinterpret_cast<const uint4*>(slot + 2 * D) + c16;
+        } else {
+            const int64_t row = u * a.ntok + (tok - a.ring_end);
+            ks = reinterpret_cast<const uint4*>(a.k + row * D) + c16;
+            vs = reinterpret_cast<const uint4*>(a.v + row * D) + c16;
+        }
+        reinterpret_cast<uint4*>(sk)[idx] = *ks;
+        reinterpret_cast<uint4*>(sv)[idx] = *vs;
+    }
+    __syncthreads();
+
+    uint8_t* rec = g.base + g.off_blocks + (size_t)u * g.unit_stride + (size_t)j * g.block_bytes;
+    if (tid < D) {
+        const int c = tid;
+        float x[kG];
+#pragma unroll
+        for (int t = 0; t < kG; ++t) x[t] = half_bits_to_float(sk[t * D + c]);
+        float s, z;
+        quant_group<kG, BITS>(x, s, z, &ck[c], D);
+        reinterpret_cast<float2*>(rec + g.rec_ksz)[c] = make_float2(s, z);
+    } else {
+        const int idx = tid - D;
+        const int t = idx / NG, grp = idx % NG;
+        float x[kVG];
+#pragma unroll
+        for (int i = 0; i < kVG; ++i) x[i] = half_bits_to_float(sv[t * D + grp * kVG + i]);
+        float s, z;
+        quant_group<kVG, BITS>(x, s, z, &cv[t * D + grp * kVG], 1);
+        reinterpret_cast<float2*>(rec + g.rec_vsz)[t * NG + grp] = make_float2(s, z);
+    }
+    __syncthreads();
+
+    uint32_t* kw = reinterpret_cast<uint32_t*>(rec + g.rec_kcode);
+    uint32_t* vw = reinterpret_cast<uint32_t*>(rec + g.rec_vcode);
+    for (int idx = tid; idx < 2 * kG * W; idx += NT) {
+        const bool isv = idx >= kG * W;
+        const int r = isv ? idx - kG * W : idx;  // r = t * W + w
+        const int t = r / W, w = r % W;
+        const uint8_t* cs = (isv ? cv : ck) + t * D + w * PER;
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i] << (BITS * i);
+        (isv ? vw : kw)[r] = word;
+    }
+}
+
+// Copy tokens [t0, t1) of every unit into their ring slots: one thread per
+// 16-byte chunk of a key or value row.
+template <int D>
+__global__ __launch_bounds__(256) void ring_write_kernel(const RingArgs a) {
+    constexpr int CPR = D / 8;
+    const CacheGeom& g = a.g;
+    const int64_t u = blockIdx.y;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n = (a.t1 - a.t0) * 2 * CPR;
+    if (idx >= n) return;
+    const int c16 = (int)(idx % CPR);
+    const int kv = (int)((idx / CPR) & 1);
+    const int64_t tok = a.t0 + idx / (2 * CPR);
+    const int64_t row = u * a.ntok + (tok - a.in_t0);
+    const uint4* src = reinterpret_cast<const uint4*>((kv ? a.v : a.k) + row * D) + c16;
+    uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
+                    (size_t)(tok % g.ring_slots) * 4 * D + (size_t)kv * 2 * D;
+    reinterpret_cast<uint4*>(slot)[c16] = *src;
+}
+
+template <int D>
+hipError_t quantize_d(const QuantArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.j1 - a.j0), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
+    if (a.g.bits == 2)
+        quantize_kernel<D, 2><<<grid, 2 * D, 0, s>>>(a);
+    else
+        quantize_kernel<D, 4><<<grid, 2 * D, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+    switch (a.g.head_dim) {
+        case 64: return quantize_d<64>(a, s);
+        case 128: return quantize_d<128>(a, s);
+        default: return quantize_d<256>(a, s);
+    }
+}
+
+hipError_t launch_ring_write(const RingArgs& a, hipStream_t s) {
+    const int64_t n = (a.t1 - a.t0) * 2 * (a.g.head_dim / 8);
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
+    switch (a.g.head_dim) {
+        case 64: ring_write_kernel<64><<<grid, 256, 0, s>>>(a); break;
+        case 128: ring_write_kernel<128><<<grid, 256, 0, s>>>(a); break;
+        default: ring_write_kernel<256><<<grid, 256, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kivi

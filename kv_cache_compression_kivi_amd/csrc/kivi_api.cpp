@@ -19,7 +19,7 @@ struct kivi_cache {
     size_t bytes;
     int64_t n_tokens;
     int64_t n_quant;
-    int32_t forced_key_splits;
+    int32_t forced_splits;
     bool poisoned;
 };
 
@@ -135,7 +135,7 @@ int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_
     c->bytes = bytes;
     c->n_tokens = 0;
     c->n_quant = 0;
-    c->forced_key_splits = 0;
+    c->forced_splits = 0;
     c->poisoned = false;
     *out = c;
     return KIVI_OK;
@@ -227,22 +227,26 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed) {
     return KIVI_OK;
 }
 
+namespace {
+kivi::AttendPlan attend_plan(const kivi_cache* c) {
+    return kivi::plan_attend((int64_t)c->cfg.batch * c->cfg.n_kv_heads, c->cfg.n_q_heads / c->cfg.n_kv_heads,
+                             c->cfg.head_dim, c->n_quant / c->cfg.k_block, c->L.max_splits, c->forced_splits);
+}
+}  // namespace
+
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
-    const int64_t units = (int64_t)cache->cfg.batch * cache->cfg.n_kv_heads;
-    kivi::AttendPlan p = kivi::plan_attend(units, cache->n_quant / cache->cfg.k_block,
-                                           cache->n_tokens - cache->n_quant, cache->L.max_splits,
-                                           cache->forced_key_splits);
+    kivi::AttendPlan p = attend_plan(cache);
     if (n_split) *n_split = p.n_split;
     if (blocks_per_split) *blocks_per_split = p.blocks_per_split;
     return KIVI_OK;
 }
 
-int kivi_set_attend_splits(kivi_cache* cache, int32_t n_key_splits) {
+int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
-    if (n_key_splits < 0 || n_key_splits > cache->L.max_splits - 1)
-        return fail(KIVI_E_INVAL, "n_key_splits must be in [0, max_splits - 1]");
-    cache->forced_key_splits = n_key_splits;
+    if (n_split < 0 || n_split > cache->L.max_splits)
+        return fail(KIVI_E_INVAL, "n_split must be in [0, max_splits]");
+    cache->forced_splits = n_split;
     return KIVI_OK;
 }
 
@@ -253,10 +257,7 @@ int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float*
     if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
     if (cache->n_tokens == 0) return fail(KIVI_E_EMPTY, "attention on an empty cache");
-    const int64_t units = (int64_t)cache->cfg.batch * cache->cfg.n_kv_heads;
-    const int64_t nb = cache->n_quant / cache->cfg.k_block;
-    kivi::AttendPlan p = kivi::plan_attend(units, nb, cache->n_tokens - cache->n_quant, cache->L.max_splits,
-                                           cache->forced_key_splits);
+    kivi::AttendPlan p = attend_plan(cache);
     kivi::AttendArgs a;
     a.g = geom(cache);
     a.q = static_cast<const uint16_t*>(q);
@@ -264,10 +265,10 @@ int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float*
     a.out = out;
     a.n_tokens = cache->n_tokens;
     a.n_quant = cache->n_quant;
-    a.n_blocks = nb;
-    a.n_key_splits = p.n_key_splits;
-    a.blocks_per_split = p.blocks_per_split;
+    a.n_blocks = cache->n_quant / cache->cfg.k_block;
     a.n_split = p.n_split;
+    a.qg = p.qg;
+    a.nwaves = p.nwaves;
     a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
     (void)hipGetLastError();
     hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));

@@ -41,13 +41,19 @@ struct RingArgs {
     int64_t ntok;
 };
 
+// Decode attention. Work-group (split s, unit u, query chunk z) covers the
+// unit's key blocks [floor(s*C/n), floor((s+1)*C/n)) clipped to n_blocks,
+// where C = n_blocks + (residual chunk cost) * (residual chunks) and
+// n = n_split; the last split also takes the residual. qg query heads per
+// work-group, nwaves waves per work-group.
 struct AttendArgs {
     CacheGeom g;
     const uint16_t* q;
     int32_t q_bf16;
     float* out;
     int64_t n_tokens, n_quant, n_blocks;
-    int32_t n_key_splits, blocks_per_split, n_split;
+    int32_t n_split;
+    int32_t qg, nwaves;
     float scale_log2;  // log2(e) / sqrt(d)
 };
 

@@ -115,36 +115,46 @@ inline int64_t plan_flush(int64_t nt, int64_t nq, int64_t R, int64_t G) {
 }
 
 struct AttendPlan {
-    int32_t n_key_splits;     // splits over the quantized blocks
-    int32_t blocks_per_split;
-    int32_t n_split;          // n_key_splits + (residual present)
+    int32_t n_split;          // work-groups per (unit, query chunk) along the tokens
+    int32_t blocks_per_split; // key blocks per split, about (informational)
+    int32_t qg;               // query heads per work-group
+    int32_t nwaves;           // waves per work-group
 };
 
-// Split-K plan: enough work-groups to fill the chip (about 2048 in total),
-// every key split non-empty, at most max_splits partials per query head.
-inline AttendPlan plan_attend(int64_t units, int64_t n_blocks, int64_t n_res, int32_t max_splits,
-                              int32_t forced_key_splits) {
-    AttendPlan p{0, 0, 0};
-    const int32_t res = n_res > 0 ? 1 : 0;
-    if (n_blocks > 0) {
-        int64_t want;
-        if (forced_key_splits > 0) {
-            want = forced_key_splits;
-        } else {
-            const int64_t target_wgs = 2048;
-            want = (target_wgs + units - 1) / units;
-            const int64_t min_blocks = 4;  // one per wave of a work-group
-            int64_t cap = (n_blocks + min_blocks - 1) / min_blocks;
-            if (want > cap) want = cap;
-        }
-        if (want > max_splits - res) want = max_splits - res;
-        if (want < 1) want = 1;
-        if (want > n_blocks) want = n_blocks;
-        int64_t bps = (n_blocks + want - 1) / want;
-        p.blocks_per_split = (int32_t)bps;
-        p.n_key_splits = (int32_t)((n_blocks + bps - 1) / bps);
+// Query heads per work-group: the largest of 4, 2, 1 dividing the GQA group
+// (the kernel keeps qg x 16 accumulators per lane); fewer waves per
+// work-group as qg or head_dim grows, to keep the register budget per lane
+// (512 / waves-per-SIMD registers).
+inline void attend_shape(int32_t group, int32_t head_dim, int32_t* qg, int32_t* nwaves) {
+    *qg = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+    if (head_dim <= 128)
+        *nwaves = *qg == 1 ? 16 : (*qg == 2 ? 8 : 4);
+    else
+        *nwaves = *qg == 1 ? 8 : 4;
+}
+
+// Split-K plan. About 16 waves per compute unit in one round over 256 CUs,
+// at least 2 key blocks per wave in every split, at most max_splits
+// partials per query head; no split (and no merge launch) when the units
+// alone fill the chip. forced > 0 fixes the split count instead.
+inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, int64_t n_blocks,
+                              int32_t max_splits, int32_t forced) {
+    AttendPlan p;
+    attend_shape(group, head_dim, &p.qg, &p.nwaves);
+    const int64_t wgs_per_split = units * (group / p.qg);
+    int64_t n;
+    if (forced > 0) {
+        n = forced;
+    } else {
+        const int64_t target_waves = 256 * 16;
+        n = (target_waves + wgs_per_split * p.nwaves - 1) / (wgs_per_split * p.nwaves);
+        const int64_t cap = n_blocks / (2 * p.nwaves);
+        if (n > cap) n = cap;
     }
-    p.n_split = p.n_key_splits + res;
+    if (n > max_splits) n = max_splits;
+    if (n < 1) n = 1;
+    p.n_split = (int32_t)n;
+    p.blocks_per_split = (int32_t)((n_blocks + n - 1) / n);
     return p;
 }
 

@@ -132,7 +132,7 @@ def test_create_and_host_only_calls(native):
         assert (st.n_tokens, st.n_quant) == (0, 0)
         native.kivi_set_attend_splits(h, 3)
         with pytest.raises(native.KiviError):
-            native.kivi_set_attend_splits(h, 256)
+            native.kivi_set_attend_splits(h, 257)
     finally:
         native.kivi_cache_destroy(h)
 
@@ -141,15 +141,23 @@ def test_create_and_host_only_calls(native):
 
 SHIM = r"""
 #include "planner.hpp"
+#include "split.hpp"
 extern "C" {
 void shim_plan_append(int64_t nt, int64_t nq, int64_t ntok, int64_t R, int64_t G, int64_t* out) {
     kivi::AppendPlan p = kivi::plan_append(nt, nq, ntok, R, G);
     out[0] = p.nt1; out[1] = p.nq1; out[2] = p.ring_t0;
 }
 int64_t shim_plan_flush(int64_t nt, int64_t nq, int64_t R, int64_t G) { return kivi::plan_flush(nt, nq, R, G); }
-void shim_plan_attend(int64_t units, int64_t nb, int64_t nres, int32_t max_splits, int32_t forced, int32_t* out) {
-    kivi::AttendPlan p = kivi::plan_attend(units, nb, nres, max_splits, forced);
-    out[0] = p.n_key_splits; out[1] = p.blocks_per_split; out[2] = p.n_split;
+void shim_plan_attend(int64_t units, int32_t group, int32_t d, int64_t nb, int32_t max_splits, int32_t forced,
+                      int32_t* out) {
+    kivi::AttendPlan p = kivi::plan_attend(units, group, d, nb, max_splits, forced);
+    out[0] = p.n_split; out[1] = p.blocks_per_split; out[2] = p.qg; out[3] = p.nwaves;
+}
+void shim_split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n, int64_t s, int64_t* out) {
+    kivi::split_range(nb, nrc, cost, n, s, &out[0], &out[1]);
+}
+int64_t shim_wave_start(int64_t nbw, int64_t rc, int64_t cost, int64_t nw, int64_t w) {
+    return kivi::wave_start(nbw, rc, cost, nw, w);
 }
 }
 """
@@ -170,7 +178,11 @@ def planner(tmp_path_factory):
     lib.shim_plan_append.argtypes = [i64] * 5 + [ctypes.c_void_p]
     lib.shim_plan_flush.argtypes = [i64] * 4
     lib.shim_plan_flush.restype = i64
-    lib.shim_plan_attend.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    i32 = ctypes.c_int32
+    lib.shim_plan_attend.argtypes = [i64, i32, i32, i64, i32, i32, ctypes.c_void_p]
+    lib.shim_split_range.argtypes = [i64] * 5 + [ctypes.c_void_p]
+    lib.shim_wave_start.argtypes = [i64] * 5
+    lib.shim_wave_start.restype = i64
     return lib
 
 
@@ -215,25 +227,60 @@ def test_planner_config_states(planner):
 
 
 def test_attend_plan(planner):
-    out = np.zeros(3, np.int32)
+    out = np.zeros(4, np.int32)
     p = out.ctypes.data_as(ctypes.c_void_p)
-    for units, nb, nres in [(1, 28, 128), (256, 124, 128), (32, 4092, 128), (512, 255, 150), (1024, 124, 128),
-                            (3, 0, 5), (7, 1, 0), (1, 5000, 1)]:
-        for forced in (0, 1, 3, 17):
-            planner.shim_plan_attend(units, nb, nres, 256, forced, p)
-            nks, bps, nsplit = (int(x) for x in out)
-            assert nsplit == nks + (1 if nres > 0 else 0) <= 256
-            if nb:
-                assert nks >= 1 and bps >= 1
-                assert (nks - 1) * bps < nb <= nks * bps  # every key split non-empty, all blocks covered
-            else:
-                assert nks == 0
+    # (units, group, head_dim, key blocks) -> the automatic split count of the five workloads
+    for args, want in [((1, 1, 128, 28), 1), ((256, 1, 128, 124), 1), ((32, 1, 128, 4092), 8),
+                       ((512, 4, 128, 255), 2), ((1024, 4, 128, 124), 1)]:
+        planner.shim_plan_attend(*args, 256, 0, p)
+        assert int(out[0]) == want, (args, out)
+    for units, group, d in [(1, 1, 128), (7, 2, 64), (3, 4, 256), (2, 3, 128)]:
+        for nb in (0, 1, 31, 4092):
+            for forced in (0, 1, 3, 17, 300):
+                planner.shim_plan_attend(units, group, d, nb, 256, forced, p)
+                n, bps, qg, nw = (int(x) for x in out)
+                assert 1 <= n <= 256 and group % qg == 0 and nw in (4, 8, 16)
+                if forced:
+                    assert n == min(forced, 256)
+
+
+@pytest.mark.parametrize("cost", [4, 3])
+def test_split_and_wave_ranges_cover_every_block_once(planner, cost):
+    """The attention kernel's division of a unit's work: every key block goes
+    to exactly one wave of one split, the residual to the last split, and the
+    per-wave cost stays within one item of the mean whenever the mean allows."""
+    buf = np.zeros(2, np.int64)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    rng = np.random.default_rng(cost)
+    cases = [(124, 4, 1, 16), (4092, 4, 8, 16), (28, 4, 1, 16), (0, 5, 1, 16), (3, 5, 2, 8), (255, 5, 1, 4)]
+    cases += [(int(rng.integers(0, 5000)), int(rng.integers(0, 6)), int(rng.integers(1, 40)),
+               int(rng.choice([4, 8, 16]))) for _ in range(200)]
+    for nb, nrc, n, nw in cases:
+        seen = np.zeros(nb, np.int64)
+        prev_end = 0
+        for s in range(n):
+            planner.shim_split_range(nb, nrc, cost, n, s, p)
+            b0, b1 = int(buf[0]), int(buf[1])
+            assert b0 == prev_end and b0 <= b1
+            prev_end = b1
+            rc = nrc if s == n - 1 else 0
+            starts = [int(planner.shim_wave_start(b1 - b0, rc, cost, nw, w)) for w in range(nw + 1)]
+            assert starts[0] == 0 and starts[-1] == b1 - b0 and all(x <= y for x, y in zip(starts, starts[1:]))
+            for w in range(nw):
+                seen[b0 + starts[w]:b0 + starts[w + 1]] += 1
+            total = (b1 - b0) + cost * rc
+            if total >= nw * (cost + 1):
+                loads = [starts[w + 1] - starts[w] + cost * len(range(w, rc, nw)) for w in range(nw)]
+                assert max(loads) <= total / nw + cost + 1, (nb, nrc, n, nw, loads)
+        assert prev_end == nb
+        assert np.all(seen == 1)
 
 
 SANITIZED_MAIN = r"""
 #include <cstdio>
 #include <cstdlib>
 #include "planner.hpp"
+#include "split.hpp"
 int main() {
     // random append/flush walks under ASan/UBSan: counters stay consistent
     unsigned x = 12345;
@@ -249,8 +296,16 @@ int main() {
                 if (p.nq1 % 32 || p.nt1 - p.nq1 > R + 32 || p.nt1 - p.nq1 < 0 || p.ring_t0 < p.nq1) return 1;
                 nt = p.nt1; nq = p.nq1;
             }
-            kivi::AttendPlan a = kivi::plan_attend(1 + (x >> 4) % 2000, nq / 32, nt - nq, 256, (x >> 3) % 5);
-            if (a.n_split > 256 || (nq > 0 && (int64_t)(a.n_key_splits - 1) * a.blocks_per_split >= nq / 32)) return 2;
+            kivi::AttendPlan a = kivi::plan_attend(1 + (x >> 4) % 2000, 1 << ((x >> 2) % 4), 128, nq / 32, 256,
+                                                   (x >> 3) % 5);
+            if (a.n_split < 1 || a.n_split > 256) return 2;
+            int64_t b0, b1, prev = 0;
+            for (int s = 0; s < a.n_split; ++s) {
+                kivi::split_range(nq / 32, (nt - nq + 31) / 32, 4, a.n_split, s, &b0, &b1);
+                if (b0 != prev || b1 < b0) return 4;
+                prev = b1;
+            }
+            if (prev != nq / 32) return 5;
         }
     }
     kivi_config c{8, 32, 32, 128, 2, 32, 32, 128, 4096, 0};
