@@ -71,10 +71,16 @@ def prefill_bytes(units, d, bits, T, n_quant):
 
 # ---------------------------------------------------------------- helpers
 
+ATTEND_SOURCES = ("attend.hip", "split.hpp", "launch.hpp", "planner.hpp")
+
+
 def _kernel_source_hash():
+    """Hash of the sources the attention kernels are built from: a counter
+    summary taken before any of them changed no longer describes the kernel."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc", "kernels.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -132,6 +138,33 @@ def _cpu_baseline(cfg, seconds=8.0):
     }
 
 
+def _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows, d, q0, out, n_att=None):
+    """The attention launches alone: n_att back-to-back kivi_attend_decode
+    calls over the rotating caches, bracketed by one pair of HIP events on the
+    stream they run on. Returns (ms per call, algorithmic bytes per call, n)."""
+    import torch
+
+    n_caches = len(caches)
+    if n_att is None:
+        n_att = max(2 * n_caches, min(200, 20 * n_caches))
+    att_bytes = 0
+    for i in range(n_att):
+        nt, nq, nr = caches[i % n_caches].state()
+        att_bytes += attend_bytes(units, rows, d, caches[i % n_caches].cfg.bits, nq, nr)
+    for i in range(min(n_caches, 8)):  # warm the launch path
+        caches[i].attend(q0, out=out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n_att):
+        rc = lib.kivi_attend_decode(handles[i % n_caches], qp[i % len(qp)], qd, outp, sp)
+        if rc != 0:
+            raise kv.KiviError(rc, kv.kivi_last_error())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n_att, att_bytes / n_att, n_att
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -143,6 +176,10 @@ def main():
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--profile", action="store_true",
+                    help="for hardware-counter runs: the decode steps and attention launches of the default "
+                         "run, then a plain 256 MiB device copy (the counters' calibration); no prefill "
+                         "timing, no CPU baseline, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the KV cache units are independent per (batch row, KV head), "
@@ -248,29 +285,18 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = bytes_total / wall / 1e9
 
-    # the attention kernel alone, HIP events on its stream, one cache per call
-    n_att = max(2 * n_caches, min(200, 20 * n_caches))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_att)]
-    att_bytes = []
-    for i in range(n_att):
-        c = caches[i % n_caches]
-        nt, nq, nr = c.state()
-        att_bytes.append(attend_bytes(units, rows, d, c.cfg.bits, nq, nr))
-    for i in range(min(n_caches, 8)):  # warm the launch path
-        caches[i].attend(queries[0], out=out)
-    torch.cuda.synchronize()
-    for i in range(n_att):
-        c = caches[i % n_caches]
-        evs[i][0].record(stream)
-        rc = lib.kivi_attend_decode(handles[i % n_caches], qp[i % pool], qd, outp, sp)
-        evs[i][1].record(stream)
-        if rc != 0:
-            raise kv.KiviError(rc, kv.kivi_last_error())
-    torch.cuda.synchronize()
-    att_ms = [a.elapsed_time(b) for a, b in evs]
-    att_avg_ms = sum(att_ms) / len(att_ms)
-    att_bytes_avg = sum(att_bytes) / len(att_bytes)
+    att_avg_ms, att_bytes_avg, n_att = _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows, d,
+                                                    queries[0], out)
     att_gbs = att_bytes_avg / (att_avg_ms * 1e-3) / 1e9
+    if args.profile:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)  # known traffic: 256 MiB read + 256 MiB written per copy
+        torch.cuda.synchronize()
+        print(f"[bench] profile: the last {n_att} attention calls carry {att_bytes_avg:.0f} algorithmic bytes "
+              f"each ({att_avg_ms * 1e3:.2f} us); then 3 copies of {256 << 20} bytes", file=sys.stderr, flush=True)
+        return
 
     # prefill quantize-append: append(T) + flush into an empty cache
     n_pf = min(len(caches), max(4, n_rot))
