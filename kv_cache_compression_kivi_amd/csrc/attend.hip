@@ -14,10 +14,24 @@
 // key blocks and the fp16 residual of the work-group's share of the tokens;
 // splits of a unit are merged by a log-sum-exp kernel afterwards.
 //
+// Codes are never converted one by one. One AND of a packed word with a mask
+// leaves one code in each 16-bit half, inside the mantissa field of an fp16
+// subnormal, so the half reads exactly as code * 2^(b*j - 24) for the code's
+// bit position b*j in the half; v_fma_mix_f32 takes that half as an operand
+// of an fp32 FMA (the half widens exactly, one rounding as in an fp32 FMA).
+// Half the positions of a half-word are masked in place and half after one
+// shift right by 8 bits, so b*j < 8 and the code never reaches the exponent
+// field. The powers of two go into the query (key side: q_c 2^(-b j(c)), and
+// 2^24 into the score scale) and into the output (value side: 2^(24 - b j(c))
+// per channel once at the end).
+//
 // Lane layout inside a wave: lane = tl * NW + w. Column w owns channels
 // [16w, 16w + 16) (one code word at b = 2, two at b = 4); token lane tl owns
 // tokens tl, tl + TL, ... of every 32-token chunk. Reductions use DPP inside
 // rows of 16 lanes and permlane swaps across rows: VALU only, no LDS traffic.
+// Block records are read with buffer loads: the unit's records are one
+// buffer, the block offset is a scalar and each lane's offsets are constants,
+// so no vector instruction goes to address arithmetic.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -127,74 +141,101 @@ struct BlockRegs {
     float2 vsz[TPL];          // (s, z) of each token's value group that holds this column
 };
 
+// A lane's byte offsets inside any record: its key-code word of token tl
+// (the value code follows at Rec::vcode, token tl + TL*i at i*TL*W*4 more),
+// its key (s, z) and its value (s, z) of token tl.
+struct LaneOffsets {
+    int code, ksz, vsz;
+};
+
 template <int D, int BITS>
-__device__ __forceinline__ void load_block(const uint8_t* rec, int lane, int w, int tl, BlockRegs<D, BITS>& r) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int w, int tl) {
     using B = BlockRegs<D, BITS>;
     using L = Rec<D, BITS>;
-    const float* kszp = reinterpret_cast<const float*>(rec + L::ksz) + lane * 2 * B::CPL;
+    LaneOffsets o;
+    o.code = (tl * L::W + w * B::NWORD) * 4;
+    o.ksz = L::ksz + lane * 2 * B::CPL * 4;
+    o.vsz = L::vsz + (tl * (D / kVG) + (w >> 1)) * 8;
+    return o;
+}
+
+// The unit's records as one buffer (offsets past `bytes` read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t records(const uint8_t* base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n, 0x00020000);
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, uint32_t soff, const LaneOffsets& lo,
+                                           BlockRegs<D, BITS>& r) {
+    using B = BlockRegs<D, BITS>;
+    using L = Rec<D, BITS>;
+    const int so = __builtin_amdgcn_readfirstlane((int)soff);  // uniform: the block's offset
     if constexpr (B::CPL == 1) {
-        const float2 v = *reinterpret_cast<const float2*>(kszp);
-        r.ksz[0] = v.x;
-        r.ksz[1] = v.y;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.ksz, so, 2);
+        r.ksz[0] = __uint_as_float(v[0]);
+        r.ksz[1] = __uint_as_float(v[1]);
     } else {
 #pragma unroll
         for (int k = 0; k < B::CPL / 2; ++k) {
-            const float4 v = reinterpret_cast<const float4*>(kszp)[k];
-            r.ksz[4 * k] = v.x;
-            r.ksz[4 * k + 1] = v.y;
-            r.ksz[4 * k + 2] = v.z;
-            r.ksz[4 * k + 3] = v.w;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.ksz + 16 * k, so, 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.ksz[4 * k + e] = __uint_as_float(v[e]);
         }
     }
-    const uint32_t* kc = reinterpret_cast<const uint32_t*>(rec + L::kcode);
-    const uint32_t* vc = reinterpret_cast<const uint32_t*>(rec + L::vcode);
-    const float2* vsz = reinterpret_cast<const float2*>(rec + L::vsz);
 #pragma unroll
     for (int i = 0; i < B::TPL; ++i) {
-        const int t = tl + B::TL * i;
+        const int toff = i * B::TL * L::W * 4;
         if constexpr (B::NWORD == 1) {
-            r.kc[i][0] = kc[t * L::W + w];
-            r.vc[i][0] = vc[t * L::W + w];
+            r.kc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.code + toff, so, 2);
+            r.vc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.code + L::vcode + toff, so, 2);
         } else {
-            const uint2 kk = *reinterpret_cast<const uint2*>(kc + t * L::W + 2 * w);
-            const uint2 vv = *reinterpret_cast<const uint2*>(vc + t * L::W + 2 * w);
-            r.kc[i][0] = kk.x;
-            r.kc[i][1] = kk.y;
-            r.vc[i][0] = vv.x;
-            r.vc[i][1] = vv.y;
+            const auto kk = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.code + toff, so, 2);
+            const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.code + L::vcode + toff, so, 2);
+            r.kc[i][0] = kk[0];
+            r.kc[i][1] = kk[1];
+            r.vc[i][0] = vv[0];
+            r.vc[i][1] = vv[1];
         }
-        r.vsz[i] = vsz[t * (D / kVG) + (w >> 1)];
+        const auto sz = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.vsz + i * B::TL * (D / kVG) * 8, so, 2);
+        r.vsz[i] = make_float2(__uint_as_float(sz[0]), __uint_as_float(sz[1]));
     }
 }
 
-// Hides a value's bits from the optimizer, so that the byte conversions below
-// stay one v_cvt_f32_ubyte{0..3} per code instead of a bit-field extract plus
-// a conversion per code.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-    asm("" : "+v"(x));
-    return x;
-}
+// ------------------------------------------------------------ codes as fp16 halves
 
-// The 16 codes of one lane's column for one token, as floats in channel order:
-// one mask isolates 4 codes, one per byte, then each byte converts directly.
+// Where the code of column channel ch sits once masked: codes per 16-bit half
+// PH = 16 / b; the first ND = PH / 2 of a half are masked in place, the rest
+// after a shift right by 8, so the code lands at bit b * jpos(ch) of its half.
 template <int BITS>
-__device__ __forceinline__ void unpack16(const uint32_t* wd, float (&cf)[16]) {
-    if constexpr (BITS == 2) {
+struct CodePos {
+    static constexpr int PH = 16 / BITS;
+    static constexpr int ND = PH / 2;
+    static constexpr int NWORD = BITS / 2;
+    __device__ static constexpr int jpos(int ch) { return (ch % PH) % ND; }
+};
+
+__device__ __forceinline__ float half_lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)); }
+
+// The 16 codes of one lane's column for one token: cf[ch] = code * 2^(b * jpos(ch) - 24),
+// exact. Word k holds column channels [2 PH k, 2 PH (k + 1)), channel 2 PH k + i at
+// bits [b i, b i + b). Each cf feeds an FMA directly (v_fma_mix_f32 reads the half).
+template <int BITS>
+__device__ __forceinline__ void code_halves(const uint32_t* wd, float (&cf)[16]) {
+    using P = CodePos<BITS>;
+    constexpr uint32_t M = (1u << BITS) - 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t e = opaque((wd[0] >> (2 * j)) & 0x03030303u);
+    for (int k = 0; k < P::NWORD; ++k) {
+        const uint32_t sh = wd[k] >> 8;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) cf[4 * k + j] = (float)((e >> (8 * k)) & 0xffu);
-        }
-    } else {
-#pragma unroll
-        for (int wi = 0; wi < 2; ++wi) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t e = opaque((wd[wi] >> (4 * j)) & 0x0f0f0f0fu);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) cf[8 * wi + 2 * k + j] = (float)((e >> (8 * k)) & 0xffu);
-            }
+        for (int p = 0; p < P::PH; ++p) {
+            const int j = p % P::ND;
+            const uint32_t x = (p < P::ND ? wd[k] : sh) & ((M << (BITS * j)) | (M << (16 + BITS * j)));
+            cf[2 * P::PH * k + p] = half_lo(x);
+            cf[2 * P::PH * k + P::PH + p] = half_hi(x);
         }
     }
 }
@@ -231,19 +272,26 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 
 // ------------------------------------------------------------ kernel
 
+// Key blocks each wave keeps in registers: the one being computed and PF - 1
+// in flight (measured on MI355X: 3 with one query head per work-group of 8
+// waves; more buys nothing once the HBM queue is full).
+constexpr int attend_prefetch(int D, int QG) { return QG == 1 && D <= 128 ? 3 : 2; }
+
 template <int D, int BITS, int QG, int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a) {
     using B = BlockRegs<D, BITS>;
+    using P = CodePos<BITS>;
+    using L = Rec<D, BITS>;
     constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPL = B::CPL;
     constexpr int NT = 64 * NWAVES;
-    __shared__ __align__(16) float s_q[QG][D];             // the query heads, fp32
-    __shared__ __align__(16) float s_qt[NWAVES][QG][D];    // each wave's folded query q*s
+    __shared__ __align__(16) float s_q[QG][D];           // the query heads, fp32
+    __shared__ __align__(16) float s_qt[NWAVES][QG][D];  // each wave's folded query q 2^(-b j) s
     __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG];
 
     const CacheGeom& g = a.g;
     const int lane = threadIdx.x & 63;
     // the wave index is uniform across the wave: keep it (and every block
-    // address derived from it) in scalar registers
+    // offset derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = lane % NW, tl = lane / NW;
     const int split = blockIdx.x;
@@ -253,27 +301,70 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int h = (int)(u % g.n_kv_heads);
     const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)blockIdx.z * QG;
     const float scale = a.scale_log2;
+    const float scale_q = ldexpf(a.scale_log2, 24);  // for scores summed in units of 2^-24
+
+    // this work-group's and this wave's share of the tokens (kernel arguments only)
+    const int64_t nres = a.n_tokens - a.n_quant;
+    const int64_t nrc = (nres + kG - 1) / kG;
+    const int64_t cost = residual_chunk_cost(BITS);
+    int64_t b0, b1;
+    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
+    const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
+    // this wave's key blocks: j0, j0 + NWAVES, ... below j1 (round robin). Block
+    // indices of a unit fit in 32 bits (its records are one buffer of < 4 GiB);
+    // readfirstlane keeps them, and each block offset, in scalar registers
+    const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
+    const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
+
+    // the first PF - 1 key blocks and the first residual chunk go in flight
+    // before anything waits
+    constexpr int PF = attend_prefetch(D, QG);
+    const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
+    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
+    const LaneOffsets lo = lane_offsets<D, BITS>(lane, w, tl);
+    B rr[PF];
+#pragma unroll
+    for (int k = 0; k < PF - 1; ++k)
+        if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
+
+    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
+    const int ring = (int)g.ring_slots;
+    const int slot0 = (int)(a.n_quant % g.ring_slots);
+    uint4 kraw[TPL][2], vraw[TPL][2];
+    bool valid[TPL];
+    auto load_chunk = [&](int ck) {  // key and value rows of residual chunk ck, this lane's column
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int idx = ck * kG + tl + TL * i;
+            valid[i] = idx < (int)nres;
+            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
+            slot -= slot >= ring ? ring : 0;
+            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            const uint4* vp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 2 * D + 32 * w);
+            kraw[i][0] = kp[0];
+            kraw[i][1] = kp[1];
+            vraw[i][0] = vp[0];
+            vraw[i][1] = vp[1];
+        }
+    };
+    const int ck0 = NWAVES - 1 - wave;  // this wave's residual chunks: ck0, ck0 + NWAVES, ...
 
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
         s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
     }
     __syncthreads();
-    float qf[QG][CPL];  // query at this lane's fold channels
+    // the query at this lane's fold channels, pre-scaled for the code halves
+    // (key scales) and into units of 2^-24 (key zeros)
+    float qf[QG][CPL], qz[QG][CPL];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) qf[gq][k] = s_q[gq][lane * CPL + k];
-
-    // this work-group's and this wave's share of the tokens
-    const int64_t nres = a.n_tokens - a.n_quant;
-    const int64_t nrc = (nres + kG - 1) / kG;
-    const int64_t cost = residual_chunk_cost(BITS);
-    int64_t b0, b1;
-    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
-    const int64_t rc = split == a.n_split - 1 ? nrc : 0;
-    const int64_t j0 = b0 + wave_start(b1 - b0, rc, cost, NWAVES, wave);
-    const int64_t j1 = b0 + wave_start(b1 - b0, rc, cost, NWAVES, wave + 1);
+        for (int k = 0; k < CPL; ++k) {
+            const int c = lane * CPL + k;
+            qf[gq][k] = ldexpf(s_q[gq][c], -BITS * P::jpos(c % 16));
+            qz[gq][k] = ldexpf(s_q[gq][c], -24);
+        }
 
     float m[QG], l[QG], zacc[QG], o[QG][16];
 #pragma unroll
@@ -285,26 +376,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         for (int c = 0; c < 16; ++c) o[gq][c] = 0.f;
     }
 
-    const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
-    B ra, rb;
-    if (j0 < j1) load_block<D, BITS>(ubase + (size_t)j0 * Rec<D, BITS>::bytes, lane, w, tl, ra);
-
-    // residual chunks: fp16 rows from the ring, in token order
-    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
-    for (int64_t ck = wave; ck < rc; ck += NWAVES) {
-        uint4 kraw[TPL][2];
-        bool valid[TPL];
-        const uint8_t* rows[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int64_t idx = ck * kG + tl + TL * i;
-            valid[i] = idx < nres;
-            const int64_t slot = (a.n_quant + (valid[i] ? idx : 0)) % g.ring_slots;
-            rows[i] = rbase + (size_t)slot * 4 * D + 32 * w;
-            const uint4* kp = reinterpret_cast<const uint4*>(rows[i]);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
-        }
+    // residual chunks: fp16 rows from the ring, in token order (o in true units here)
+    for (int ck = ck0; ck < rc; ck += NWAVES) {
+        load_chunk(ck);
         float sc[QG][TPL];
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) {
@@ -327,13 +401,6 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 sc[gq][i] = valid[i] ? acc : -INFINITY;
             }
         }
-        uint4 vraw[TPL][2];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const uint4* vp = reinterpret_cast<const uint4*>(rows[i] + 2 * D);
-            vraw[i][0] = vp[0];
-            vraw[i][1] = vp[1];
-        }
         float p[QG][TPL];
         softmax_update<QG, TPL, NW>(sc, p, m, l, zacc, o);
 #pragma unroll
@@ -347,9 +414,15 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             }
         }
     }
+    // from here on channel c of o holds its value times 2^(b jpos(c) - 24), the
+    // factor the value code halves carry (exact scaling by a power of two)
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[gq][c] = ldexpf(o[gq][c], BITS * P::jpos(c) - 24);
 
-    // key blocks: two register sets alternate, so the loads of the next block
-    // are in flight while the current one is computed
+    // key blocks: a ring of PF register sets, the loads of the next PF - 1
+    // blocks in flight while one is computed
     auto block_math = [&](const B& r) {
         float Z[QG];
 #pragma unroll
@@ -358,7 +431,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 s_qt[wave][gq][lane * CPL + k] = qf[gq][k] * r.ksz[2 * k];
-                zp = fmaf(qf[gq][k], r.ksz[2 * k + 1], zp);
+                zp = fmaf(qz[gq][k], r.ksz[2 * k + 1], zp);
             }
             Z[gq] = wave_sum(zp);
         }
@@ -378,11 +451,11 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 float cf[16];
-                unpack16<BITS>(r.kc[i], cf);
+                code_halves<BITS>(r.kc[i], cf);
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) acc = fmaf(qt[c], cf[c], acc);
-                sc[gq][i] = (sum_cols<NW>(acc) + Z[gq]) * scale;
+                sc[gq][i] = (sum_cols<NW>(acc) + Z[gq]) * scale_q;
             }
         }
         wave_lds_order();
@@ -391,7 +464,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             float cf[16];
-            unpack16<BITS>(r.vc[i], cf);
+            code_halves<BITS>(r.vc[i], cf);
 #pragma unroll
             for (int gq = 0; gq < QG; ++gq) {
                 const float pt = p[gq][i] * r.vsz[i].x;
@@ -401,20 +474,25 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             }
         }
     };
-    for (int64_t j = j0; j < j1; j += 2) {
-        if (j + 1 < j1) load_block<D, BITS>(ubase + (size_t)(j + 1) * Rec<D, BITS>::bytes, lane, w, tl, rb);
-        block_math(ra);
-        if (j + 1 >= j1) break;
-        if (j + 2 < j1) load_block<D, BITS>(ubase + (size_t)(j + 2) * Rec<D, BITS>::bytes, lane, w, tl, ra);
-        block_math(rb);
+    for (int j = j0; j < j1; j += PF * NWAVES) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int jj = j + k * NWAVES;
+            if (jj >= j1) break;
+            const int jn = jj + (PF - 1) * NWAVES;
+            if (jn < j1) load_block<D, BITS>(rs, (uint32_t)(jn * L::bytes), lo, rr[(k + PF - 1) % PF]);
+            block_math(rr[k]);
+        }
     }
 
-    // per-wave totals: the value zeros join their channels, then the token lanes sum
+    // per-wave totals: channels back to true units, the value zeros join their
+    // channels, then the token lanes sum
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
         l[gq] = tok_sum<NW>(l[gq]);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) o[gq][c] = tok_sum<NW>(o[gq][c] + zacc[gq]);
+        for (int c = 0; c < 16; ++c)
+            o[gq][c] = tok_sum<NW>(fmaf(o[gq][c], ldexpf(1.0f, 24 - BITS * P::jpos(c)), zacc[gq]));
     }
     __syncthreads();  // every wave is done with s_qt
     if (tl == 0) {
@@ -492,12 +570,11 @@ hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
 
 template <int D, int BITS>
 hipError_t attend_db(const AttendArgs& a, hipStream_t s) {
-    switch (a.nwaves * 8 + a.qg) {
-        case 4 * 8 + 4: return attend_launch<D, BITS, 4, 4>(a, s);
-        case 4 * 8 + 2: return attend_launch<D, BITS, 2, 4>(a, s);
-        case 8 * 8 + 2: return attend_launch<D, BITS, 2, 8>(a, s);
-        case 8 * 8 + 1: return attend_launch<D, BITS, 1, 8>(a, s);
-        default: return attend_launch<D, BITS, 1, 16>(a, s);
+    // the host plans (qg, nwaves) with the same attend_waves()
+    switch (a.qg) {
+        case 4: return attend_launch<D, BITS, 4, attend_waves(4, D)>(a, s);
+        case 2: return attend_launch<D, BITS, 2, attend_waves(2, D)>(a, s);
+        default: return attend_launch<D, BITS, 1, attend_waves(1, D)>(a, s);
     }
 }
 

@@ -19,6 +19,7 @@
 #include <string>
 
 #include "kivi.h"
+#include "split.hpp"
 
 namespace kivi {
 
@@ -60,6 +61,14 @@ inline int validate_config(const kivi_config* c, std::string& err) {
     if (units > 65535 || (int64_t)c->batch * c->n_q_heads > ((int64_t)1 << 30)) {
         err = "batch * n_kv_heads must be <= 65535";
         return KIVI_E_INVAL;
+    }
+    // the attention kernel addresses one sequence's key-block records as one
+    // buffer with 32-bit offsets
+    const int64_t W = (int64_t)c->head_dim * c->bits / 32;
+    const int64_t block_bytes = 2 * 32 * W * 4 + (int64_t)c->head_dim * 8 + 32 * (c->head_dim / 32) * 8;
+    if ((int64_t)(c->max_tokens / c->k_block) * block_bytes > (int64_t)0xffffffff) {
+        err = "max_tokens too large: one sequence's quantized blocks must fit in 4 GiB";
+        return KIVI_E_UNSUPPORTED;
     }
     return KIVI_OK;
 }
@@ -122,21 +131,18 @@ struct AttendPlan {
 };
 
 // Query heads per work-group: the largest of 4, 2, 1 dividing the GQA group
-// (the kernel keeps qg x 16 accumulators per lane); fewer waves per
-// work-group as qg or head_dim grows, to keep the register budget per lane
-// (512 / waves-per-SIMD registers).
+// (the kernel keeps qg x 16 accumulators per lane); waves per work-group from
+// attend_waves(), which the kernel's dispatch uses too.
 inline void attend_shape(int32_t group, int32_t head_dim, int32_t* qg, int32_t* nwaves) {
     *qg = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-    if (head_dim <= 128)
-        *nwaves = *qg == 1 ? 16 : (*qg == 2 ? 8 : 4);
-    else
-        *nwaves = *qg == 1 ? 8 : 4;
+    *nwaves = attend_waves(*qg, head_dim);
 }
 
-// Split-K plan. About 16 waves per compute unit in one round over 256 CUs,
-// at least 2 key blocks per wave in every split, at most max_splits
-// partials per query head; no split (and no merge launch) when the units
-// alone fill the chip. forced > 0 fixes the split count instead.
+// Split-K plan. Enough work-groups for one round over the 256 CUs (one
+// 8-wave work-group per CU, or four 4-wave ones), at least 2 key blocks per
+// wave in every split, at most max_splits partials per query head; no split
+// (and no merge launch) when the units alone fill the chip. forced > 0 fixes
+// the split count instead.
 inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, int64_t n_blocks,
                               int32_t max_splits, int32_t forced) {
     AttendPlan p;
@@ -146,7 +152,7 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
     if (forced > 0) {
         n = forced;
     } else {
-        const int64_t target_waves = 256 * 16;
+        const int64_t target_waves = 256 * (p.nwaves == 8 ? 8 : 16);
         n = (target_waves + wgs_per_split * p.nwaves - 1) / (wgs_per_split * p.nwaves);
         const int64_t cap = n_blocks / (2 * p.nwaves);
         if (n > cap) n = cap;

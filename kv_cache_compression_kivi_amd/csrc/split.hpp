@@ -3,9 +3,8 @@
 // kernel and the host-side tests, so both use one definition.
 //
 // Work items are the unit's key blocks (G = 32 quantized tokens each) and its
-// residual chunks (up to 32 fp16 tokens each). A residual chunk moves about
-// four times the bytes of a 2-bit block (16 KB against 4 KB at d = 128), so
-// items are balanced by cost, and the residual goes to the last split.
+// residual chunks (up to 32 fp16 tokens each). Splits are balanced by cost,
+// and the residual goes to the last split.
 #pragma once
 
 #include <cstdint>
@@ -18,8 +17,10 @@
 
 namespace kivi {
 
-// Cost of one residual chunk, in key blocks of the given bit width.
-KIVI_HD inline int64_t residual_chunk_cost(int bits) { return bits == 2 ? 4 : 3; }
+// Cost of one residual chunk, in key blocks: a chunk of 32 fp16 tokens moves
+// 16 KB (four 2-bit blocks at d = 128) but runs no decoding; measured on
+// MI355X it takes about as long as 1.5 packed blocks.
+KIVI_HD inline int64_t residual_chunk_cost(int bits) { return bits == 2 ? 2 : 2; }
 
 // Key blocks [*b0, *b1) of split s (of n) for a unit with nb key blocks and
 // nrc residual chunks; the last split (which also owns the residual) ends at nb.
@@ -32,21 +33,19 @@ KIVI_HD inline void split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n
     *b1 = s == n - 1 ? nb : (hi < nb ? hi : nb);
 }
 
-// A work-group of nw waves holds nbw key blocks and rc residual chunks;
-// residual chunk k goes to wave k mod nw. Wave w takes key blocks
-// [wave_start(w), wave_start(w + 1)), so that every wave carries about the
-// same cost. Non-decreasing in w, wave_start(0) = 0, wave_start(nw) = nbw.
-KIVI_HD inline int64_t wave_start(int64_t nbw, int64_t rc, int64_t cost, int64_t nw, int64_t w) {
-    if (w >= nw) return nbw;
-    const int64_t total = nbw + cost * rc;
-    int64_t best = 0;
-    for (int64_t v = 1; v <= w; ++v) {
-        const int64_t r = rc % nw;
-        const int64_t chunks_before = (rc / nw) * v + (r < v ? r : v);  // chunks held by waves [0, v)
-        const int64_t f = v * total / nw - cost * chunks_before;
-        if (f > best) best = f;
-    }
-    return best < nbw ? best : nbw;
-}
+// Inside a work-group of nw waves, wave w takes the split's key blocks
+// b0 + w, b0 + w + nw, b0 + w + 2 nw, ... (round robin), so the waves sweep
+// the split's records together, and residual chunk c goes to wave
+// residual_wave(c, nw): the last waves first, which hold one block fewer
+// whenever nw does not divide the split's block count.
+KIVI_HD inline int64_t residual_wave(int64_t c, int64_t nw) { return nw - 1 - c % nw; }
+
+// Waves per work-group of the attention kernel for qg query heads per
+// work-group: 8 with one or two query heads (registers for a 3-deep ring of
+// block records with one), 4 with four (their accumulators fill the registers).
+KIVI_HD constexpr int attend_waves(int qg, int head_dim) { return qg == 4 ? 4 : (qg == 2 && head_dim > 128 ? 4 : 8); }
+
+// Key blocks wave w of nw holds out of nbw.
+KIVI_HD inline int64_t wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return nbw / nw + (w < nbw % nw ? 1 : 0); }
 
 }  // namespace kivi

@@ -156,8 +156,9 @@ void shim_plan_attend(int64_t units, int32_t group, int32_t d, int64_t nb, int32
 void shim_split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n, int64_t s, int64_t* out) {
     kivi::split_range(nb, nrc, cost, n, s, &out[0], &out[1]);
 }
-int64_t shim_wave_start(int64_t nbw, int64_t rc, int64_t cost, int64_t nw, int64_t w) {
-    return kivi::wave_start(nbw, rc, cost, nw, w);
+int64_t shim_wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return kivi::wave_blocks(nbw, nw, w); }
+int64_t shim_residual_wave(int64_t c, int64_t nw) {
+    return kivi::residual_wave(c, nw);
 }
 }
 """
@@ -181,8 +182,10 @@ def planner(tmp_path_factory):
     i32 = ctypes.c_int32
     lib.shim_plan_attend.argtypes = [i64, i32, i32, i64, i32, i32, ctypes.c_void_p]
     lib.shim_split_range.argtypes = [i64] * 5 + [ctypes.c_void_p]
-    lib.shim_wave_start.argtypes = [i64] * 5
-    lib.shim_wave_start.restype = i64
+    lib.shim_wave_blocks.argtypes = [i64] * 3
+    lib.shim_wave_blocks.restype = i64
+    lib.shim_residual_wave.argtypes = [i64] * 2
+    lib.shim_residual_wave.restype = i64
     return lib
 
 
@@ -244,11 +247,12 @@ def test_attend_plan(planner):
                     assert n == min(forced, 256)
 
 
-@pytest.mark.parametrize("cost", [4, 3])
+@pytest.mark.parametrize("cost", [2, 4])
 def test_split_and_wave_ranges_cover_every_block_once(planner, cost):
     """The attention kernel's division of a unit's work: every key block goes
     to exactly one wave of one split, the residual to the last split, and the
-    per-wave cost stays within one item of the mean whenever the mean allows."""
+    per-wave cost (blocks plus residual chunks at their cost) within cost + 1
+    of the mean."""
     buf = np.zeros(2, np.int64)
     p = buf.ctypes.data_as(ctypes.c_void_p)
     rng = np.random.default_rng(cost)
@@ -264,14 +268,21 @@ def test_split_and_wave_ranges_cover_every_block_once(planner, cost):
             assert b0 == prev_end and b0 <= b1
             prev_end = b1
             rc = nrc if s == n - 1 else 0
-            starts = [int(planner.shim_wave_start(b1 - b0, rc, cost, nw, w)) for w in range(nw + 1)]
-            assert starts[0] == 0 and starts[-1] == b1 - b0 and all(x <= y for x, y in zip(starts, starts[1:]))
+            # round robin inside the work-group: wave w holds blocks b0 + w + k * nw
+            counts = [int(planner.shim_wave_blocks(b1 - b0, nw, w)) for w in range(nw)]
+            assert sum(counts) == b1 - b0
             for w in range(nw):
-                seen[b0 + starts[w]:b0 + starts[w + 1]] += 1
+                for j in range(b0 + w, b1, nw):
+                    seen[j] += 1
+                assert counts[w] == len(range(b0 + w, b1, nw))
+            chunks = [0] * nw
+            for c in range(rc):
+                wv = int(planner.shim_residual_wave(c, nw))
+                assert 0 <= wv < nw
+                chunks[wv] += 1
             total = (b1 - b0) + cost * rc
-            if total >= nw * (cost + 1):
-                loads = [starts[w + 1] - starts[w] + cost * len(range(w, rc, nw)) for w in range(nw)]
-                assert max(loads) <= total / nw + cost + 1, (nb, nrc, n, nw, loads)
+            loads = [counts[w] + cost * chunks[w] for w in range(nw)]
+            assert max(loads) <= total / nw + cost + 1, (nb, nrc, n, nw, loads)
         assert prev_end == nb
         assert np.all(seen == 1)
 
