@@ -77,13 +77,15 @@ typedef struct {
  *
  * Quantized blocks: unit u, key block j (tokens [jG, jG+G)) is one record at
  *   off_blocks + u * unit_stride + j * block_bytes, holding in order:
- *     kcode [G][W] uint32   W = head_dim * bits / 32; row t = token jG+t
- *     vcode [G][W] uint32
+ *     kcode [G][W] uint32   W = head_dim * bits / 32 words per token (token-major)
+ *     vcode [head_dim][bits] uint32   bits words per channel (channel-major)
  *     ksz   [head_dim][2] float32   (scale, zero) of each channel over the block
  *     vsz   [G][head_dim / v_group][2] float32   (scale, zero) of each token's groups
- *   at record offsets rec_kcode, rec_vcode, rec_ksz, rec_vsz. In a code row,
- *   word w holds channels [w*32/b, (w+1)*32/b); channel w*32/b + i sits at
- *   bits [b*i, b*i + b).
+ *   at record offsets rec_kcode, rec_vcode, rec_ksz, rec_vsz. A word holds
+ *   P = 32/b codes, code i at bits [b*i, b*i + b): key word w of token t holds
+ *   channels [w*P, (w+1)*P); value word k of channel c holds the block's
+ *   tokens [k*P, (k+1)*P). (Keys are read a token row at a time, values a
+ *   channel column at a time.)
  * Residual ring: unit u, slot r (token t lives in slot t mod ring_slots) is
  *   off_ring + u * ring_unit_stride + r * 4 * head_dim: the token's fp16 key
  *   row (head_dim halves) followed by its fp16 value row.

@@ -119,7 +119,8 @@ __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOM
 
 // ------------------------------------------------------------ block records
 
-// Record layout of one key block (see kivi.h): kcode [G][W], vcode [G][W],
+// Record layout of one key block (see kivi.h): kcode [G][W] (token-major),
+// vcode [D][BITS] (channel-major: a channel's 32 tokens in BITS words),
 // ksz [D][2], vsz [G][D/32][2]; known at compile time from D and BITS.
 template <int D, int BITS>
 struct Rec {
@@ -131,21 +132,25 @@ struct Rec {
     static constexpr int bytes = vsz + kG * (D / kVG) * 8;
 };
 
-// One lane's share of a block record, loaded ahead of its use.
+// One lane's share of a block record, loaded ahead of its use. Key side:
+// lane = tl * NW + w holds key-code words of tokens tl + TL*i, column w. Value
+// side: lane L holds the value codes of channels L*CPV .. L*CPV + CPV - 1,
+// all 32 tokens (BITS words per channel).
 template <int D, int BITS>
 struct BlockRegs {
     static constexpr int NW = D / 16, TL = 64 / NW, TPL = kG / TL, NWORD = BITS / 2, CPL = D / 64;
-    float ksz[2 * CPL];       // (s, z) of channels lane*CPL .. lane*CPL + CPL - 1
-    uint32_t kc[TPL][NWORD];  // key code words of this lane's tokens and column
-    uint32_t vc[TPL][NWORD];  // value code words
-    float2 vsz[TPL];          // (s, z) of each token's value group that holds this column
+    static constexpr int CPV = D / 64;  // value channels per lane
+    float ksz[2 * CPL];          // (s, z) of channels lane*CPL .. lane*CPL + CPL - 1
+    uint32_t kc[TPL][NWORD];     // key code words of this lane's tokens and column
+    uint32_t vc[CPV * BITS];     // value code words of this lane's channels
+    float2 vsz[TPL];             // (s, z) of each token's value group that holds column w
 };
 
 // A lane's byte offsets inside any record: its key-code word of token tl
-// (the value code follows at Rec::vcode, token tl + TL*i at i*TL*W*4 more),
-// its key (s, z) and its value (s, z) of token tl.
+// (token tl + TL*i at i*TL*W*4 more), its value-code words, its key (s, z)
+// and its value (s, z) of token tl.
 struct LaneOffsets {
-    int code, ksz, vsz;
+    int code, vcode, ksz, vsz;
 };
 
 template <int D, int BITS>
@@ -154,6 +159,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int w, int tl) {
     using L = Rec<D, BITS>;
     LaneOffsets o;
     o.code = (tl * L::W + w * B::NWORD) * 4;
+    o.vcode = L::vcode + lane * B::CPV * BITS * 4;
     o.ksz = L::ksz + lane * 2 * B::CPL * 4;
     o.vsz = L::vsz + (tl * (D / kVG) + (w >> 1)) * 8;
     return o;
@@ -188,17 +194,26 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, uint32_t s
         const int toff = i * B::TL * L::W * 4;
         if constexpr (B::NWORD == 1) {
             r.kc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.code + toff, so, 2);
-            r.vc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.code + L::vcode + toff, so, 2);
         } else {
             const auto kk = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.code + toff, so, 2);
-            const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.code + L::vcode + toff, so, 2);
             r.kc[i][0] = kk[0];
             r.kc[i][1] = kk[1];
-            r.vc[i][0] = vv[0];
-            r.vc[i][1] = vv[1];
         }
         const auto sz = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.vsz + i * B::TL * (D / kVG) * 8, so, 2);
         r.vsz[i] = make_float2(__uint_as_float(sz[0]), __uint_as_float(sz[1]));
+    }
+    constexpr int NV = B::CPV * BITS;  // 2, 4, 8 or 16 words, contiguous
+    if constexpr (NV == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.vcode, so, 2);
+        r.vc[0] = v[0];
+        r.vc[1] = v[1];
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV / 4; ++k) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.vcode + 16 * k, so, 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.vc[4 * k + e] = v[e];
+        }
     }
 }
 
@@ -220,15 +235,17 @@ __device__ __forceinline__ float half_lo(uint32_t x) {
 }
 __device__ __forceinline__ float half_hi(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)); }
 
-// The 16 codes of one lane's column for one token: cf[ch] = code * 2^(b * jpos(ch) - 24),
-// exact. Word k holds column channels [2 PH k, 2 PH (k + 1)), channel 2 PH k + i at
-// bits [b i, b i + b). Each cf feeds an FMA directly (v_fma_mix_f32 reads the half).
-template <int BITS>
-__device__ __forceinline__ void code_halves(const uint32_t* wd, float (&cf)[16]) {
+// The codes of NWD packed words as exact floats, in code order: word k holds
+// codes [P k, P (k + 1)) (P = 32 / b), code P k + i at bits [b i, b i + b), and
+// cf[P k + i] = code * 2^(b * jpos(i) - 24). Key side: one token's 16 channels
+// of a column (b / 2 words); value side: one channel's 32 tokens (b words).
+// Each cf feeds an FMA directly (v_fma_mix_f32 reads the half).
+template <int BITS, int NWD>
+__device__ __forceinline__ void code_halves(const uint32_t* wd, float (&cf)[NWD * 32 / BITS]) {
     using P = CodePos<BITS>;
     constexpr uint32_t M = (1u << BITS) - 1;
 #pragma unroll
-    for (int k = 0; k < P::NWORD; ++k) {
+    for (int k = 0; k < NWD; ++k) {
         const uint32_t sh = wd[k] >> 8;
 #pragma unroll
         for (int p = 0; p < P::PH; ++p) {
@@ -245,9 +262,9 @@ __device__ __forceinline__ void code_halves(const uint32_t* wd, float (&cf)[16])
 // New scores sc (base-2 log domain) of this lane's TPL tokens for each query:
 // raise the running maximum if the chunk's maximum exceeds it (rescaling the
 // accumulators), then turn the scores into weights p.
-template <int QG, int TPL, int NW>
+template <int QG, int TPL, int NW, int NO>
 __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float (&p)[QG][TPL], float (&m)[QG],
-                                               float (&l)[QG], float (&zacc)[QG], float (&o)[QG][16]) {
+                                               float (&l)[QG], float (&zacc)[QG], float (&o)[QG][NO]) {
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
         float bm = sc[gq][0];
@@ -259,7 +276,7 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
             l[gq] *= alpha;
             zacc[gq] *= alpha;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) o[gq][c] *= alpha;
+            for (int c = 0; c < NO; ++c) o[gq][c] *= alpha;
             m[gq] = bm;
         }
 #pragma unroll
@@ -277,16 +294,24 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 // waves; more buys nothing once the HBM queue is full).
 constexpr int attend_prefetch(int D, int QG) { return QG == 1 && D <= 128 ? 3 : 2; }
 
+// Two lane layouts per wave. Key side: lane = tl * NW + w scores tokens
+// tl + TL*i against channels [16w, 16w + 16). Value side: lane L accumulates
+// channels [L*CPV, L*CPV + CPV) over all 32 tokens of a chunk, with the
+// chunk's weights passed through a wave-private LDS slot (one row of 32
+// weights per value group, the group's scale and the code-half factor folded in).
 template <int D, int BITS, int QG, int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a) {
     using B = BlockRegs<D, BITS>;
     using P = CodePos<BITS>;
     using L = Rec<D, BITS>;
-    constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPL = B::CPL;
+    constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPL = B::CPL, CPV = B::CPV;
+    constexpr int NG = D / kVG;  // value groups of a token
+    constexpr int NACC = 2;      // partial sums per value channel (shorter dependency chains)
     constexpr int NT = 64 * NWAVES;
-    __shared__ __align__(16) float s_q[QG][D];           // the query heads, fp32
-    __shared__ __align__(16) float s_qt[NWAVES][QG][D];  // each wave's folded query q 2^(-b j) s
-    __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG];
+    __shared__ __align__(16) float s_q[QG][D];              // the query heads, fp32
+    __shared__ __align__(16) float s_qt[NWAVES][QG][D];     // each wave's folded query; at the end its output
+    __shared__ __align__(16) float s_p[NWAVES][QG][NG][kG]; // each wave's value weights of one chunk
+    __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
 
     const CacheGeom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -294,6 +319,8 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     // offset derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = lane % NW, tl = lane / NW;
+    const int cv0 = lane * CPV, vgrp = cv0 / kVG;  // this lane's value channels and their group
+    const bool wlead = (w & 1) == 0;               // writes its group's value weights
     const int split = blockIdx.x;
     const int64_t u = blockIdx.y;
     const int group = g.n_q_heads / g.n_kv_heads;
@@ -316,8 +343,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
     const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
 
-    // the first PF - 1 key blocks and the first residual chunk go in flight
-    // before anything waits
+    // the first PF - 1 key blocks go in flight before anything waits
     constexpr int PF = attend_prefetch(D, QG);
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
@@ -326,28 +352,6 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
     for (int k = 0; k < PF - 1; ++k)
         if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
-
-    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
-    const int ring = (int)g.ring_slots;
-    const int slot0 = (int)(a.n_quant % g.ring_slots);
-    uint4 kraw[TPL][2], vraw[TPL][2];
-    bool valid[TPL];
-    auto load_chunk = [&](int ck) {  // key and value rows of residual chunk ck, this lane's column
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int idx = ck * kG + tl + TL * i;
-            valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
-            slot -= slot >= ring ? ring : 0;
-            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
-            const uint4* vp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 2 * D + 32 * w);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
-            vraw[i][0] = vp[0];
-            vraw[i][1] = vp[1];
-        }
-    };
-    const int ck0 = NWAVES - 1 - wave;  // this wave's residual chunks: ck0, ck0 + NWAVES, ...
 
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
@@ -365,20 +369,61 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             qf[gq][k] = ldexpf(s_q[gq][c], -BITS * P::jpos(c % 16));
             qz[gq][k] = ldexpf(s_q[gq][c], -24);
         }
+    // the code-half factor of this lane's key-side tokens tl + TL*i, folded
+    // into their value weights: 2^(24 - b jpos(token))
+    float tf[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) tf[i] = ldexpf(1.0f, 24 - BITS * P::jpos(tl + TL * i));
 
-    float m[QG], l[QG], zacc[QG], o[QG][16];
+    float m[QG], l[QG], zacc[QG], o[QG][CPV * NACC];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
         m[gq] = -INFINITY;
         l[gq] = 0.f;
         zacc[gq] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) o[gq][c] = 0.f;
+        for (int c = 0; c < CPV * NACC; ++c) o[gq][c] = 0.f;
     }
 
-    // residual chunks: fp16 rows from the ring, in token order (o in true units here)
-    for (int ck = ck0; ck < rc; ck += NWAVES) {
-        load_chunk(ck);
+    // residual chunks: fp16 rows from the ring, in token order
+    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
+    const int ring = (int)g.ring_slots;
+    const int slot0 = (int)(a.n_quant % g.ring_slots);
+    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {  // chunk ck goes to wave NWAVES - 1 - ck % NWAVES
+        // key rows of this lane's tokens and column; value rows of its channels, all 32 tokens
+        uint4 kraw[TPL][2];
+        bool valid[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int idx = ck * kG + tl + TL * i;
+            valid[i] = idx < (int)nres;
+            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
+            slot -= slot >= ring ? ring : 0;
+            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            kraw[i][0] = kp[0];
+            kraw[i][1] = kp[1];
+        }
+        uint16_t vr[kG][CPV];
+#pragma unroll
+        for (int t = 0; t < kG; ++t) {
+            const int idx = ck * kG + t;
+            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            const uint16_t* vp = reinterpret_cast<const uint16_t*>(rbase + (size_t)slot * 4 * D + 2 * D) + cv0;
+            if constexpr (CPV == 1) {
+                vr[t][0] = vp[0];
+            } else if constexpr (CPV == 2) {
+                const uint32_t x = *reinterpret_cast<const uint32_t*>(vp);
+                vr[t][0] = (uint16_t)x;
+                vr[t][1] = (uint16_t)(x >> 16);
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2*>(vp);
+                vr[t][0] = (uint16_t)x.x;
+                vr[t][1] = (uint16_t)(x.x >> 16);
+                vr[t][2] = (uint16_t)x.y;
+                vr[t][3] = (uint16_t)(x.y >> 16);
+            }
+        }
         float sc[QG][TPL];
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) {
@@ -402,24 +447,33 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             }
         }
         float p[QG][TPL];
-        softmax_update<QG, TPL, NW>(sc, p, m, l, zacc, o);
+        softmax_update<QG, TPL, NW, CPV * NACC>(sc, p, m, l, zacc, o);
+        if (w == 0) {
 #pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const uint16_t* vh = reinterpret_cast<const uint16_t*>(vraw[i]);
+            for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-            for (int gq = 0; gq < QG; ++gq) {
-                const float pw = valid[i] ? p[gq][i] : 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) o[gq][c] = fmaf(pw, h2f(vh[c]), o[gq][c]);
-            }
+                for (int i = 0; i < TPL; ++i) s_p[wave][gq][0][tl + TL * i] = valid[i] ? p[gq][i] : 0.f;
         }
+        wave_lds_order();
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float pv[kG];
+#pragma unroll
+            for (int t4 = 0; t4 < kG / 4; ++t4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][0][4 * t4]);
+                pv[4 * t4] = x.x;
+                pv[4 * t4 + 1] = x.y;
+                pv[4 * t4 + 2] = x.z;
+                pv[4 * t4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int k = 0; k < CPV; ++k)
+#pragma unroll
+                for (int t = 0; t < kG; ++t)
+                    o[gq][k * NACC + t % NACC] = fmaf(pv[t], h2f(vr[t][k]), o[gq][k * NACC + t % NACC]);
+        }
+        wave_lds_order();
     }
-    // from here on channel c of o holds its value times 2^(b jpos(c) - 24), the
-    // factor the value code halves carry (exact scaling by a power of two)
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-        for (int c = 0; c < 16; ++c) o[gq][c] = ldexpf(o[gq][c], BITS * P::jpos(c) - 24);
 
     // key blocks: a ring of PF register sets, the loads of the next PF - 1
     // blocks in flight while one is computed
@@ -436,43 +490,67 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             Z[gq] = wave_sum(zp);
         }
         wave_lds_order();
-        float sc[QG][TPL];
+        // scores: token by token, every query against the same 16 code halves
+        float qt[QG][16];
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float qt[16];
+        for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4) {
                 const float4 x = *reinterpret_cast<const float4*>(&s_qt[wave][gq][16 * w + 4 * c4]);
-                qt[4 * c4] = x.x;
-                qt[4 * c4 + 1] = x.y;
-                qt[4 * c4 + 2] = x.z;
-                qt[4 * c4 + 3] = x.w;
+                qt[gq][4 * c4] = x.x;
+                qt[gq][4 * c4 + 1] = x.y;
+                qt[gq][4 * c4 + 2] = x.z;
+                qt[gq][4 * c4 + 3] = x.w;
             }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                float cf[16];
-                code_halves<BITS>(r.kc[i], cf);
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc = fmaf(qt[c], cf[c], acc);
-                sc[gq][i] = (sum_cols<NW>(acc) + Z[gq]) * scale_q;
-            }
-        }
-        wave_lds_order();
-        float p[QG][TPL];
-        softmax_update<QG, TPL, NW>(sc, p, m, l, zacc, o);
+        float sc[QG][TPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             float cf[16];
-            code_halves<BITS>(r.vc[i], cf);
+            code_halves<BITS, BITS / 2>(r.kc[i], cf);
 #pragma unroll
             for (int gq = 0; gq < QG; ++gq) {
-                const float pt = p[gq][i] * r.vsz[i].x;
-                zacc[gq] = fmaf(p[gq][i], r.vsz[i].y, zacc[gq]);
+                float acc = 0.f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) o[gq][c] = fmaf(pt, cf[c], o[gq][c]);
+                for (int c = 0; c < 16; ++c) acc = fmaf(qt[gq][c], cf[c], acc);
+                sc[gq][i] = (sum_cols<NW>(acc) + Z[gq]) * scale_q;
             }
         }
+        float p[QG][TPL];
+        softmax_update<QG, TPL, NW, CPV * NACC>(sc, p, m, l, zacc, o);
+        // value weights p s_t 2^(24 - b jpos(t)) of token t in its group's row;
+        // the value zeros accumulate per lane as sum p z_t
+        if (wlead) {
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    s_p[wave][gq][w >> 1][tl + TL * i] = p[gq][i] * (r.vsz[i].x * tf[i]);
+                    zacc[gq] = fmaf(p[gq][i], r.vsz[i].y, zacc[gq]);
+                }
+        }
+        wave_lds_order();
+        // values: one channel's 32 code halves at a time, against each query's weights
+#pragma unroll
+        for (int k = 0; k < CPV; ++k) {
+            float cf[kG];
+            code_halves<BITS, BITS>(&r.vc[k * BITS], cf);
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq) {
+                float pv[kG];
+#pragma unroll
+                for (int t4 = 0; t4 < kG / 4; ++t4) {
+                    const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][vgrp][4 * t4]);
+                    pv[4 * t4] = x.x;
+                    pv[4 * t4 + 1] = x.y;
+                    pv[4 * t4 + 2] = x.z;
+                    pv[4 * t4 + 3] = x.w;
+                }
+#pragma unroll
+                for (int t = 0; t < kG; ++t)
+                    o[gq][k * NACC + t % NACC] = fmaf(pv[t], cf[t], o[gq][k * NACC + t % NACC]);
+            }
+        }
+        wave_lds_order();
     };
     for (int j = j0; j < j1; j += PF * NWAVES) {
 #pragma unroll
@@ -485,25 +563,33 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         }
     }
 
-    // per-wave totals: channels back to true units, the value zeros join their
-    // channels, then the token lanes sum
+    // per-wave totals: the weight sum and each group's value-zero sum over the
+    // token lanes; the zero sum joins every channel of its group
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
         l[gq] = tok_sum<NW>(l[gq]);
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            o[gq][c] = tok_sum<NW>(fmaf(o[gq][c], ldexpf(1.0f, 24 - BITS * P::jpos(c)), zacc[gq]));
+        const float zt = tok_sum<NW>(zacc[gq]);
+        if (tl == 0 && wlead) s_z[wave][gq][w >> 1] = zt;
     }
+    wave_lds_order();
+    float ov[QG][CPV];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int k = 0; k < CPV; ++k) {
+            float acc = s_z[wave][gq][vgrp];
+#pragma unroll
+            for (int e = 0; e < NACC; ++e) acc += o[gq][k * NACC + e];
+            ov[gq][k] = acc;
+        }
     __syncthreads();  // every wave is done with s_qt
-    if (tl == 0) {
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
+    for (int gq = 0; gq < QG; ++gq) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) s_qt[wave][gq][16 * w + c] = o[gq][c];
-            if (w == 0) {
-                s_m[wave][gq] = m[gq];
-                s_l[wave][gq] = l[gq];
-            }
+        for (int k = 0; k < CPV; ++k) s_qt[wave][gq][cv0 + k] = ov[gq][k];
+        if (lane == 0) {
+            s_m[wave][gq] = m[gq];
+            s_l[wave][gq] = l[gq];
         }
     }
     __syncthreads();
@@ -512,24 +598,24 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         float M = -INFINITY;
 #pragma unroll
         for (int wv = 0; wv < NWAVES; ++wv) M = fmaxf(M, s_m[wv][gq]);
-        float L = 0.f, O = 0.f;
+        float Lsum = 0.f, O = 0.f;
 #pragma unroll
         for (int wv = 0; wv < NWAVES; ++wv) {
             if (s_m[wv][gq] != -INFINITY) {
                 const float f = __builtin_amdgcn_exp2f(s_m[wv][gq] - M);
-                L = fmaf(s_l[wv][gq], f, L);
+                Lsum = fmaf(s_l[wv][gq], f, Lsum);
                 O = fmaf(s_qt[wv][gq][c], f, O);
             }
         }
         if (a.n_split == 1) {
-            a.out[(row0 + gq) * D + c] = O / L;
+            a.out[(row0 + gq) * D + c] = O / Lsum;
         } else {
             float* rec = reinterpret_cast<float*>(g.base + g.off_partial +
                                                   ((row0 + gq) * g.max_splits + split) * g.partial_stride);
             rec[c] = O;
             if (c == 0) {
                 rec[D] = M;
-                rec[D + 1] = L;
+                rec[D + 1] = Lsum;
             }
         }
     }

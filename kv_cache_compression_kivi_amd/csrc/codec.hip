@@ -115,17 +115,27 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     }
     __syncthreads();
 
+    // Pack (the record layout of kivi.h), code i of a word at bits [BITS*i, BITS*i + BITS):
+    //   key words token-major, word w of token t holds channels [w*PER, (w+1)*PER);
+    //   value words channel-major, word k of channel c holds tokens [k*PER, (k+1)*PER).
     uint32_t* kw = reinterpret_cast<uint32_t*>(rec + g.rec_kcode);
     uint32_t* vw = reinterpret_cast<uint32_t*>(rec + g.rec_vcode);
     for (int idx = tid; idx < 2 * kG * W; idx += NT) {
-        const bool isv = idx >= kG * W;
-        const int r = isv ? idx - kG * W : idx;  // r = t * W + w
-        const int t = r / W, w = r % W;
-        const uint8_t* cs = (isv ? cv : ck) + t * D + w * PER;
         uint32_t word = 0;
+        if (idx < kG * W) {
+            const int t = idx / W, w = idx % W;
+            const uint8_t* cs = ck + t * D + w * PER;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i] << (BITS * i);
-        (isv ? vw : kw)[r] = word;
+            for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i] << (BITS * i);
+            kw[idx] = word;
+        } else {
+            const int x = idx - kG * W;  // x = c * BITS + k
+            const int c = x / BITS, k = x % BITS;
+            const uint8_t* cs = cv + (k * PER) * D + c;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i * D] << (BITS * i);
+            vw[x] = word;
+        }
     }
 }
 

@@ -15,13 +15,14 @@ REL_L2 = 1e-3
 
 
 def gpu_unit_blocks(cache, unit: int, n_blocks: int):
-    """(kcode [nb,G,W] u32, vcode [nb,G,W] u32, ksz [nb,d,2] f32, vsz [nb,G,d/32,2] f32)."""
+    """(kcode [nb,G,W] u32 token-major, vcode [nb,d,b] u32 channel-major, ksz [nb,d,2] f32,
+    vsz [nb,G,d/32,2] f32), read through the layout the C ABI reports."""
     L, c = cache.layout, cache.cfg
     G, d, W = c.k_block, c.head_dim, c.head_dim * c.bits // 32
     start = L.off_blocks + unit * L.unit_stride
     raw = cache.memory[start:start + n_blocks * L.block_bytes].cpu().numpy().reshape(n_blocks, L.block_bytes)
     kcode = raw[:, L.rec_kcode:L.rec_kcode + G * W * 4].copy().view(np.uint32).reshape(n_blocks, G, W)
-    vcode = raw[:, L.rec_vcode:L.rec_vcode + G * W * 4].copy().view(np.uint32).reshape(n_blocks, G, W)
+    vcode = raw[:, L.rec_vcode:L.rec_vcode + G * W * 4].copy().view(np.uint32).reshape(n_blocks, d, c.bits)
     ksz = raw[:, L.rec_ksz:L.rec_ksz + d * 8].copy().view(np.float32).reshape(n_blocks, d, 2)
     ng = d // c.v_group
     vsz = raw[:, L.rec_vsz:L.rec_vsz + G * ng * 8].copy().view(np.float32).reshape(n_blocks, G, ng, 2)
@@ -50,8 +51,10 @@ def compare_unit(cache, oc: "oracle.OracleCache", gpu_unit: int, or_unit: int):
     kc, ks, kz, vc, vs, vz = oc.unit_quantized(or_unit)
     if nb:
         gk, gv, gksz, gvsz = gpu_unit_blocks(cache, gpu_unit, nb)
+        # keys: one packed row per token; values: one packed row of the block's 32 tokens per channel
         want_k = oracle.pack_rows(kc, bits).reshape(nb, G, -1)
-        want_v = oracle.pack_rows(vc, bits).reshape(nb, G, -1)
+        vcb = np.ascontiguousarray(vc.reshape(nb, G, -1).transpose(0, 2, 1))  # [nb, d, G]
+        want_v = oracle.pack_rows(vcb.reshape(-1, G), bits).reshape(nb, c.head_dim, -1)
         bad = np.argwhere(gk != want_k)
         assert bad.size == 0, f"key codes differ at {bad[:5].tolist()}"
         bad = np.argwhere(gv != want_v)
