@@ -529,27 +529,31 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 }
         }
         wave_lds_order();
-        // values: one channel's 32 code halves at a time, against each query's weights
+        // values: one code word of one channel at a time, against each query's weights
+        // one code word (32/b tokens) of one channel at a time
+        constexpr int PW = 32 / BITS;
 #pragma unroll
-        for (int k = 0; k < CPV; ++k) {
-            float cf[kG];
-            code_halves<BITS, BITS>(&r.vc[k * BITS], cf);
+        for (int k = 0; k < CPV; ++k)
 #pragma unroll
-            for (int gq = 0; gq < QG; ++gq) {
-                float pv[kG];
+            for (int wd = 0; wd < BITS; ++wd) {
+                float cf[PW];
+                code_halves<BITS, 1>(&r.vc[k * BITS + wd], cf);
 #pragma unroll
-                for (int t4 = 0; t4 < kG / 4; ++t4) {
-                    const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][vgrp][4 * t4]);
-                    pv[4 * t4] = x.x;
-                    pv[4 * t4 + 1] = x.y;
-                    pv[4 * t4 + 2] = x.z;
-                    pv[4 * t4 + 3] = x.w;
+                for (int gq = 0; gq < QG; ++gq) {
+                    float pv[PW];
+#pragma unroll
+                    for (int t4 = 0; t4 < PW / 4; ++t4) {
+                        const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][vgrp][PW * wd + 4 * t4]);
+                        pv[4 * t4] = x.x;
+                        pv[4 * t4 + 1] = x.y;
+                        pv[4 * t4 + 2] = x.z;
+                        pv[4 * t4 + 3] = x.w;
+                    }
+#pragma unroll
+                    for (int t = 0; t < PW; ++t)
+                        o[gq][k * NACC + t % NACC] = fmaf(pv[t], cf[t], o[gq][k * NACC + t % NACC]);
                 }
-#pragma unroll
-                for (int t = 0; t < kG; ++t)
-                    o[gq][k * NACC + t % NACC] = fmaf(pv[t], cf[t], o[gq][k * NACC + t % NACC]);
             }
-        }
         wave_lds_order();
     };
     for (int j = j0; j < j1; j += PF * NWAVES) {
@@ -621,6 +625,549 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     }
 }
 
+// ------------------------------------------------------------ four query heads on the matrix cores
+
+// With four query heads per KV head both contractions of a block are small
+// matrix products, and they run exactly on the int8 matrix cores:
+//   scores  S[g][t] = sum_c q~[g][c] kcode[t][c]   (q~ = q s, per block and channel)
+//   values  O[g][c] = sum_t p~[g][t] vcode[t][c]   (p~ = p s_t, per token and value group)
+// The codes are int8 operands as they are. q~ and p~ are rounded to 23-bit
+// integers against a per-block power of two (|q| < 2^Eq per query, s < 2^Es
+// and s_t < 2^Ev per block; p <= 1) and split into three signed 8-bit
+// digits, so every product and sum is exact in int32; the only rounding is
+// that of q~ and p~ to 2^-22 of their bounds. The digits of query (or weight)
+// row g sit in columns (or rows) 4g .. 4g + 2 of a 16-wide tile; 4g + 3 is zero.
+// Scores: v_mfma_i32_16x16x64_i8, 16 tokens x 16 columns x 64 channels.
+// Values: v_mfma_i32_16x16x32_i8, 16 rows x 16 channels x the block's 32 tokens.
+// The fp16 residual runs on the vector units as in attend_kernel.
+
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Channel of byte s of a score operand, for lane group q of 64-channel chunk kc:
+// masking a token's key word by (w >> b*j) & 0x0303..03 / 0x0F0F..0F gives one
+// code per byte; these formulas follow that byte order.
+template <int BITS>
+__device__ __forceinline__ constexpr int gqa_channel(int kc, int q, int s) {
+    if constexpr (BITS == 2) {
+        return 64 * kc + 16 * q + 4 * (s % 4) + s / 4;  // word 4kc + q, s = 4j + k -> channel 4k + j
+    } else {
+        return 64 * kc + 16 * q + 8 * (s / 8) + 2 * (s % 4) + (s / 4) % 2;  // words 8kc + 2q + e, s = 8e + 4j + k
+    }
+}
+
+// Token of byte s of a value operand, for lane group q: masking a channel's
+// value word in the same way. b = 2: word q/2, bytes (w >> 2(2(q%2) + e)) ->
+// tokens 16(q/2) + 4k + 2(q%2) + e (s = 4e + k); b = 4: word q, (w >> 4e) ->
+// tokens 8q + 2k + e.
+// Score rows are assigned to tokens so that lane group rho, rows 4rho + r of a
+// 16-token tile hold exactly the tokens of bytes 4e .. 4e + 3 of one value
+// operand (q = 2 tt + rho/2, e = rho % 2): its weights then pack into one word.
+template <int BITS>
+__device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score row m
+    if constexpr (BITS == 2) {
+        return m / 4 + 4 * (m % 4);
+    } else {
+        return 8 * ((m / 4) / 2) + (m / 4) % 2 + 2 * (m % 4);
+    }
+}
+
+// Shares of a block record for one wave (loaded ahead of use).
+template <int D, int BITS>
+struct GqaRegs {
+    static constexpr int KC = D / 64;  // 64-channel chunks
+    static constexpr int KW = BITS / 2;
+    static constexpr int VT = D / 16;  // 16-channel value tiles
+    uint32_t kc[2][KC][KW];            // key words of score row l%16 of tile tt, lane group l/16 of each chunk
+    float ksz[KC][4][2];               // (s, z) of the digit producer's channels
+    float2 vsz[2][4];                  // (s, z) of the tokens of rows 4(l/16) + r, value group (l%16)%4
+    uint32_t vc[VT];                   // value word of channel 16 vt + l%16 used by lane group l/16
+};
+
+// Bytes d of four words, as one word (byte k from word k).
+__device__ __forceinline__ uint32_t bytes_d(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int d) {
+    const uint32_t lo = __builtin_amdgcn_perm(v1, v0, (uint32_t)(d | (4 + d) << 8 | 0x0c << 16 | 0x0c << 24));
+    const uint32_t hi = __builtin_amdgcn_perm(v3, v2, (uint32_t)(0x0c | 0x0c << 8 | d << 16 | (4 + d) << 24));
+    return lo | hi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kQuadBcast0 = 0x00;
+
+// The maximum over a wave (every lane holds it).
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dppf<kSwap1>(x));
+    x = fmaxf(x, dppf<kSwap2>(x));
+    x = fmaxf(x, dppf<kHalfMirror>(x));
+    x = fmaxf(x, dppf<kMirror>(x));
+    return rows_max(x);
+}
+
+// 23-bit integer of x (|x| < 2^22) as three signed bytes: (Q + 0x808080) ^ 0x808080.
+__device__ __forceinline__ uint32_t digits3(float x) {
+    const int qi = (int)__builtin_rintf(x);
+    return ((uint32_t)qi + 0x808080u) ^ 0x808080u;
+}
+
+template <int D, int BITS, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArgs a) {
+    constexpr int QG = 4;
+    using B = BlockRegs<D, BITS>;
+    using R = GqaRegs<D, BITS>;
+    using L = Rec<D, BITS>;
+    constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPV = B::CPV, KC = R::KC, VT = R::VT;
+    constexpr int NG = D / kVG;
+    static_assert(NG == 4 && CPV == 2, "the four lanes of a quad take the four value groups");
+    constexpr int NACC = 2;
+    constexpr int NT = 64 * NWAVES;
+    __shared__ __align__(16) float s_q[QG][D];
+    __shared__ __align__(16) uint32_t s_kb[NWAVES][KC][4][16][4];  // score operands: chunk, lane group, column
+    __shared__ __align__(16) uint32_t s_va[NWAVES][NG][4][16][2];  // weight operands: group, lane group, row
+    __shared__ __align__(16) float s_p[NWAVES][QG][kG];            // residual weights
+    __shared__ __align__(16) float s_o[NWAVES][QG][D];
+    __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
+
+    const CacheGeom& g = a.g;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // vector layout (residual): key rows of tokens tl + TL*i, column w; value channels cv0, cv0 + 1
+    const int w = lane % NW, tl = lane / NW;
+    const int cv0 = lane * CPV;
+    // matrix layout: n = column (scores) / row (values) / channel in a tile, rho = lane group
+    const int n = lane & 15, rho = lane >> 4;
+    const int gl = n >> 2, dq = n & 3;  // the query of score columns 4gl .. 4gl+3, and a value group
+    const int split = blockIdx.x;
+    const int64_t u = blockIdx.y;
+    const int group = g.n_q_heads / g.n_kv_heads;
+    const int64_t b = u / g.n_kv_heads;
+    const int h = (int)(u % g.n_kv_heads);
+    const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)blockIdx.z * QG;
+    const float scale = a.scale_log2;
+
+    const int64_t nres = a.n_tokens - a.n_quant;
+    const int64_t nrc = (nres + kG - 1) / kG;
+    const int64_t cost = residual_chunk_cost(BITS);
+    int64_t b0, b1;
+    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
+    const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
+    const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
+    const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
+
+    const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
+    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
+    // per-lane byte offsets of the block shares: a base per share plus
+    // compile-time steps (which become the loads' immediate offsets)
+    const int rt = gqa_row_token<BITS>(n);       // token of score row n in its tile
+    const int ob_kw = (rt * L::W + (BITS == 2 ? rho : 2 * rho)) * 4;
+    const int ob_ks = L::ksz + gqa_channel<BITS>(0, n >> 2, 4 * (n & 3)) * 8;
+    const int ob_vc = L::vcode + (n * BITS + (BITS == 2 ? rho / 2 : rho)) * 4;
+    auto kw_off = [&](int tt, int kc) { return ob_kw + (16 * tt * L::W + (BITS == 2 ? 4 : 8) * kc) * 4; };
+    auto ks_off = [&](int kc, int k) { return ob_ks + gqa_channel<BITS>(kc, 0, k) * 8; };
+    auto vs_off = [&](int tt, int r) {
+        return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * rho + r)) * NG + dq) * 8;
+    };
+    auto load = [&](int j, R& r) {
+        const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)j * L::bytes));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                if constexpr (BITS == 2) {
+                    r.kc[tt][kc][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, kw_off(tt, kc), so, 2);
+                } else {
+                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, kw_off(tt, kc), so, 2);
+                    r.kc[tt][kc][0] = x[0];
+                    r.kc[tt][kc][1] = x[1];
+                }
+            }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, ks_off(kc, k), so, 2);
+                r.ksz[kc][k][0] = __uint_as_float(x[0]);
+                r.ksz[kc][k][1] = __uint_as_float(x[1]);
+            }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, vs_off(tt, rr), so, 2);
+                r.vsz[tt][rr] = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+            }
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+            r.vc[vt] = __builtin_amdgcn_raw_buffer_load_b32(rs, ob_vc + 16 * vt * BITS * 4, so, 2);
+    };
+    R cur;
+    if (j0 < j1) load(j0, cur);
+
+    for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
+        const uint16_t v = a.q[row0 * D + idx];
+        s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
+    }
+    // digit columns / rows 4g + 3 stay zero
+    for (int idx = lane; idx < KC * 4 * 4 * 4; idx += 64) {
+        const int kc = idx / 64, q = (idx / 16) % 4, gg = (idx / 4) % 4, dw = idx % 4;
+        s_kb[wave][kc][q][4 * gg + 3][dw] = 0u;
+    }
+    for (int idx = lane; idx < NG * 4 * 4 * 2; idx += 64) {
+        const int gr = idx / 32, q = (idx / 8) % 4, gg = (idx / 2) % 4, dw = idx % 2;
+        s_va[wave][gr][q][4 * gg + 3][dw] = 0u;
+    }
+    __syncthreads();
+    // per-query bounds |q| < 2^Eq; the producer's query (rho) at its channels,
+    // scaled to 2^22 of the bound (digits) and as it is (key zeros)
+    int Eq[QG];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+        float mx = 0.f;
+#pragma unroll
+        for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(s_q[gq][c]));
+        Eq[gq] = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(mx)));
+    }
+    const int eq_mine = rho == 0 ? Eq[0] : (rho == 1 ? Eq[1] : (rho == 2 ? Eq[2] : Eq[3]));
+    const int eq_gl = gl == 0 ? Eq[0] : (gl == 1 ? Eq[1] : (gl == 2 ? Eq[2] : Eq[3]));
+    float qn[KC][4], qv[KC][4];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float x = s_q[rho][gqa_channel<BITS>(kc, n >> 2, 4 * (n & 3) + k)];
+            qn[kc][k] = ldexpf(x, 22 - eq_mine);
+            qv[kc][k] = x;
+        }
+
+    // running state. m: per query, uniform. Residual part (vector layout): l_res
+    // and o_res per query. Blocks (matrix layout): l_blk for query gl, z_blk for
+    // (gl, dq), o_blk[vt] for query rho and channel 16vt + n.
+    float m[QG], l_res[QG], o_res[QG][CPV * NACC], o_blk[VT];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+        m[gq] = -INFINITY;
+        l_res[gq] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] = 0.f;
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) o_blk[vt] = 0.f;
+    float l_blk = 0.f, z_blk = 0.f;
+    // multiply every accumulator of query gq by alpha (a new running maximum)
+    auto rescale = [&](int gq, float alpha) {
+        l_res[gq] *= alpha;
+#pragma unroll
+        for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] *= alpha;
+        if (gl == gq) {
+            l_blk *= alpha;
+            z_blk *= alpha;
+        }
+        if (rho == gq) {
+#pragma unroll
+            for (int vt = 0; vt < VT; ++vt) o_blk[vt] *= alpha;
+        }
+    };
+
+    // residual chunks (vector units, as in attend_kernel)
+    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
+    const int ring = (int)g.ring_slots;
+    const int slot0 = (int)(a.n_quant % g.ring_slots);
+    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
+        uint4 kraw[TPL][2];
+        bool valid[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int idx = ck * kG + tl + TL * i;
+            valid[i] = idx < (int)nres;
+            int slot = slot0 + (valid[i] ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            kraw[i][0] = kp[0];
+            kraw[i][1] = kp[1];
+        }
+        uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
+#pragma unroll
+        for (int t = 0; t < kG; ++t) {
+            const int idx = ck * kG + t;
+            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            vr[t] = *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
+        }
+        float sc[QG][TPL];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float qq[16];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][16 * w + 4 * c4]);
+                qq[4 * c4] = x.x;
+                qq[4 * c4 + 1] = x.y;
+                qq[4 * c4 + 2] = x.z;
+                qq[4 * c4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const uint16_t* kh = reinterpret_cast<const uint16_t*>(kraw[i]);
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc = fmaf(qq[c], h2f(kh[c]), acc);
+                acc = sum_cols<NW>(acc) * scale;
+                sc[gq][i] = valid[i] ? acc : -INFINITY;
+            }
+        }
+        float p[QG][TPL];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float bm = sc[gq][0];
+#pragma unroll
+            for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sc[gq][i]);
+            bm = tok_max<NW>(bm);
+            if (bm > m[gq]) {
+                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bm));
+                m[gq] = bm;
+            }
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                p[gq][i] = valid[i] ? __builtin_amdgcn_exp2f(sc[gq][i] - m[gq]) : 0.f;
+                l_res[gq] += p[gq][i];
+            }
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) s_p[wave][gq][tl + TL * i] = p[gq][i];
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float pv[kG];
+#pragma unroll
+            for (int t4 = 0; t4 < kG / 4; ++t4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][4 * t4]);
+                pv[4 * t4] = x.x;
+                pv[4 * t4 + 1] = x.y;
+                pv[4 * t4 + 2] = x.z;
+                pv[4 * t4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int t = 0; t < kG; ++t) {
+                o_res[gq][t % NACC] = fmaf(pv[t], half_lo(vr[t]), o_res[gq][t % NACC]);
+                o_res[gq][NACC + t % NACC] = fmaf(pv[t], half_hi(vr[t]), o_res[gq][NACC + t % NACC]);
+            }
+        }
+        wave_lds_order();
+    }
+
+    // scores, softmax, weight digits of one block
+    auto key_math = [&](const R& r, int& ev) {
+        // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
+        float smax = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) smax = fmaxf(smax, r.ksz[kc][k][0]);
+        smax = fmaxf(smax, dppf<kSwap1>(smax));
+        smax = fmaxf(smax, dppf<kSwap2>(smax));
+        smax = fmaxf(smax, dppf<kHalfMirror>(smax));
+        smax = fmaxf(smax, dppf<kMirror>(smax));  // each row of 16 lanes covers every channel
+        const int es = __builtin_amdgcn_frexp_expf(smax);
+        float zp = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint32_t vq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vq[k] = digits3(qn[kc][k] * ldexpf(r.ksz[kc][k][0], -es));
+                zp = fmaf(qv[kc][k], r.ksz[kc][k][1], zp);
+            }
+#pragma unroll
+            for (int d = 0; d < 3; ++d) s_kb[wave][kc][n >> 2][4 * rho + d][n & 3] = bytes_d(vq[0], vq[1], vq[2], vq[3], d);
+        }
+        // key zeros: Z[g] = sum_c q[g][c] z[c], query g = row rho
+        zp = sum_cols<16>(zp);
+        const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 0));
+        const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 16));
+        const float z2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 32));
+        const float z3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 48));
+        const float zs = (gl == 0 ? z0 : (gl == 1 ? z1 : (gl == 2 ? z2 : z3))) * scale;
+        // bound of the block's value scales, for the weight digits
+        float vmax = fmaxf(fmaxf(r.vsz[0][0].x, r.vsz[0][1].x), fmaxf(r.vsz[0][2].x, r.vsz[0][3].x));
+        vmax = fmaxf(vmax, fmaxf(fmaxf(r.vsz[1][0].x, r.vsz[1][1].x), fmaxf(r.vsz[1][2].x, r.vsz[1][3].x)));
+        ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(vmax)));
+        wave_lds_order();
+        // 2. scores of the tiles' tokens, columns (g, digit): exact integer products
+        const float ks = ldexpf(scale, eq_gl + es - 22);  // sum Q code = 2^(22 - Eq - Es) sum q s code
+        float sc[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            v4i32 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                v4i32 av, bv;
+                if constexpr (BITS == 2) {
+                    const uint32_t x = r.kc[tt][kc][0];
+                    av[0] = (int)(x & 0x03030303u);
+                    av[1] = (int)((x >> 2) & 0x03030303u);
+                    av[2] = (int)((x >> 4) & 0x03030303u);
+                    av[3] = (int)((x >> 6) & 0x03030303u);
+                } else {
+                    const uint32_t x0 = r.kc[tt][kc][0], x1 = r.kc[tt][kc][1];
+                    av[0] = (int)(x0 & 0x0F0F0F0Fu);
+                    av[1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
+                    av[2] = (int)(x1 & 0x0F0F0F0Fu);
+                    av[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
+                }
+                const uint4 bb = *reinterpret_cast<const uint4*>(&s_kb[wave][kc][rho][n][0]);
+                bv[0] = (int)bb.x;
+                bv[1] = (int)bb.y;
+                bv[2] = (int)bb.z;
+                bv[3] = (int)bb.w;
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+            }
+            // the digits of column 4g + d sit in lanes n .. n + 2 of each row
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+                const float f = (float)acc[r2];
+                const float comb = fmaf(dppf<kRowShl2>(f), 65536.0f, fmaf(dppf<kRowShl1>(f), 256.0f, f));
+                sc[tt][r2] = fmaf(comb, ks, zs);
+            }
+        }
+        // 3. online softmax (valid in lanes with dq == 0: query gl)
+        float bm = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+        bm = fmaxf(bm, fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        bm = rows_max(bm);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 4 * gq));
+            if (bq > m[gq]) {
+                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bq));
+                m[gq] = bq;
+            }
+        }
+        const float mg = gl == 0 ? m[0] : (gl == 1 ? m[1] : (gl == 2 ? m[2] : m[3]));
+        // 4. weights p s_t of (query gl, value group dq) as digits, rows 4gl + d
+        //    of the value operand: one word per tile (lane group 2tt + rho/2, word rho%2)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            uint32_t vp[4];
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+                const float pr = __builtin_amdgcn_exp2f(sc[tt][r2] - mg);  // valid in lanes dq == 0
+                const float p = dppf<kQuadBcast0>(pr);
+                if (dq == 0) l_blk += p;
+                z_blk = fmaf(p, r.vsz[tt][r2].y, z_blk);
+                vp[r2] = digits3(p * ldexpf(r.vsz[tt][r2].x, 22 - ev));
+            }
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                s_va[wave][dq][2 * tt + rho / 2][4 * gl + d][rho % 2] = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
+        }
+        wave_lds_order();
+    };
+    // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
+    auto value_math = [&](const R& r, int ev) {
+        const float vs = ldexpf(1.0f, ev - 22);
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            const uint2 pa = *reinterpret_cast<const uint2*>(&s_va[wave][vt / 2][rho][n][0]);
+            const uint32_t x = r.vc[vt];
+            uint32_t b0, b1;
+            if constexpr (BITS == 2) {
+                const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
+                b0 = (x >> sh) & 0x03030303u;
+                b1 = (x >> (sh + 2)) & 0x03030303u;
+            } else {
+                b0 = x & 0x0F0F0F0Fu;
+                b1 = (x >> 4) & 0x0F0F0F0Fu;
+            }
+            const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
+            const long bv = (long)(((uint64_t)b1 << 32) | b0);
+            const v4i32 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, v4i32{0, 0, 0, 0}, 0, 0, 0);
+            // rows 4rho + d: the three digits of query rho, channel 16vt + n
+            float comb;
+            if constexpr (BITS == 2) {
+                comb = (float)(c[0] + (c[1] << 8) + (c[2] << 16));  // |digit sums| < 2^14: no overflow
+            } else {
+                comb = fmaf((float)c[2], 65536.0f, fmaf((float)c[1], 256.0f, (float)c[0]));
+            }
+            o_blk[vt] = fmaf(comb, vs, o_blk[vt]);
+        }
+        wave_lds_order();
+    };
+    // the next block's loads go out once the current block's key shares are
+    // consumed, and fly during its value phase
+    R nx;
+    for (int j = j0; j < j1; j += 2 * NWAVES) {
+        int ev;
+        key_math(cur, ev);
+        if (j + NWAVES < j1) load(j + NWAVES, nx);
+        value_math(cur, ev);
+        if (j + NWAVES >= j1) break;
+        key_math(nx, ev);
+        if (j + 2 * NWAVES < j1) load(j + 2 * NWAVES, cur);
+        value_math(nx, ev);
+    }
+
+    // per-wave totals
+    const float lb = rows_sum(l_blk);  // query gl over the four rows (lanes with dq == 0 hold it)
+    const float zb = rows_sum(z_blk);  // (query gl, group dq)
+    float lq[QG];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+        lq[gq] = tok_sum<NW>(l_res[gq]) + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), 4 * gq));
+    if (rho == 0) s_z[wave][gl][dq] = zb;
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int k = 0; k < CPV; ++k) {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < NACC; ++e) acc += o_res[gq][k * NACC + e];
+            s_o[wave][gq][cv0 + k] = acc;
+        }
+    wave_lds_order();
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+        const int c = 16 * vt + n;
+        s_o[wave][rho][c] += o_blk[vt] + s_z[wave][rho][c / kVG];
+    }
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+        if (lane == 0) {
+            s_m[wave][gq] = m[gq];
+            s_l[wave][gq] = lq[gq];
+        }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
+        const int gq = idx / D, c = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < NWAVES; ++wv) M = fmaxf(M, s_m[wv][gq]);
+        float Lsum = 0.f, O = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NWAVES; ++wv) {
+            if (s_m[wv][gq] != -INFINITY) {
+                const float f = __builtin_amdgcn_exp2f(s_m[wv][gq] - M);
+                Lsum = fmaf(s_l[wv][gq], f, Lsum);
+                O = fmaf(s_o[wv][gq][c], f, O);
+            }
+        }
+        if (a.n_split == 1) {
+            a.out[(row0 + gq) * D + c] = O / Lsum;
+        } else {
+            float* rec = reinterpret_cast<float*>(g.base + g.off_partial +
+                                                  ((row0 + gq) * g.max_splits + split) * g.partial_stride);
+            rec[c] = O;
+            if (c == 0) {
+                rec[D] = M;
+                rec[D + 1] = Lsum;
+            }
+        }
+    }
+}
+
 // Log-sum-exp merge of the splits of one (batch row, query head), in split order.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
@@ -654,11 +1201,24 @@ hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int BITS, int NWAVES>
+hipError_t attend_gqa_launch(const AttendArgs& a, hipStream_t s) {
+    const int group = a.g.n_q_heads / a.g.n_kv_heads;
+    const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / 4));
+    attend_gqa_kernel<D, BITS, NWAVES><<<grid, 64 * NWAVES, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    combine_kernel<D><<<(unsigned)((int64_t)a.g.batch * a.g.n_q_heads), D, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int D, int BITS>
 hipError_t attend_db(const AttendArgs& a, hipStream_t s) {
     // the host plans (qg, nwaves) with the same attend_waves()
     switch (a.qg) {
-        case 4: return attend_launch<D, BITS, 4, attend_waves(4, D)>(a, s);
+        case 4:
+            if constexpr (D == 128) return attend_gqa_launch<D, BITS, attend_waves(4, D)>(a, s);
+            else return attend_launch<D, BITS, 4, attend_waves(4, D)>(a, s);
         case 2: return attend_launch<D, BITS, 2, attend_waves(2, D)>(a, s);
         default: return attend_launch<D, BITS, 1, attend_waves(1, D)>(a, s);
     }

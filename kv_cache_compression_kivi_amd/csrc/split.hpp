@@ -41,9 +41,12 @@ KIVI_HD inline void split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n
 KIVI_HD inline int64_t residual_wave(int64_t c, int64_t nw) { return nw - 1 - c % nw; }
 
 // Waves per work-group of the attention kernel for qg query heads per
-// work-group: 8 with one or two query heads (registers for a 3-deep ring of
-// block records with one), 4 with four (their accumulators fill the registers).
-KIVI_HD constexpr int attend_waves(int qg, int head_dim) { return qg == 4 ? 4 : (qg == 2 && head_dim > 128 ? 4 : 8); }
+// work-group: 8, except where the registers of a lane allow only 4 (four
+// query heads on the vector path, d = 64 or 256; two query heads at d = 256).
+// Four query heads at d = 128 score on the matrix cores.
+KIVI_HD constexpr int attend_waves(int qg, int head_dim) {
+    return qg == 4 ? (head_dim == 128 ? 8 : 4) : (qg == 2 && head_dim > 128 ? 4 : 8);
+}
 
 // Key blocks wave w of nw holds out of nbw.
 KIVI_HD inline int64_t wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return nbw / nw + (w < nbw % nw ? 1 : 0); }

@@ -234,7 +234,7 @@ def test_attend_plan(planner):
     p = out.ctypes.data_as(ctypes.c_void_p)
     # (units, group, head_dim, key blocks) -> the automatic split count of the five workloads
     for args, want in [((1, 1, 128, 28), 1), ((256, 1, 128, 124), 1), ((32, 1, 128, 4092), 8),
-                       ((512, 4, 128, 255), 2), ((1024, 4, 128, 124), 1)]:
+                       ((512, 4, 128, 255), 1), ((1024, 4, 128, 124), 1)]:
         planner.shim_plan_attend(*args, 256, 0, p)
         assert int(out[0]) == want, (args, out)
     for units, group, d in [(1, 1, 128), (7, 2, 64), (3, 4, 256), (2, 3, 128)]:
