@@ -353,6 +353,47 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     for (int k = 0; k < PF - 1; ++k)
         if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
 
+    // residual chunks (fp16 rows from the ring) are computed after the blocks;
+    // a wave's first chunk is loaded now, so its latency hides behind them
+    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
+    const int ring = (int)g.ring_slots;
+    const int slot0 = (int)(a.n_quant % g.ring_slots);
+    const int ck0 = NWAVES - 1 - wave;  // chunk ck goes to wave NWAVES - 1 - ck % NWAVES
+    constexpr int VRW = (CPV + 1) / 2;  // words of fp16 value pairs per token
+    uint4 kraw[TPL][2];                 // key rows of this lane's tokens, column w
+    uint32_t vr[kG][VRW];               // value rows of this lane's channels, all 32 tokens
+    bool valid[TPL];
+    auto load_chunk = [&](int ck) {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int idx = ck * kG + tl + TL * i;
+            valid[i] = idx < (int)nres;
+            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
+            slot -= slot >= ring ? ring : 0;
+            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            kraw[i][0] = kp[0];
+            kraw[i][1] = kp[1];
+        }
+#pragma unroll
+        for (int t = 0; t < kG; ++t) {
+            const int idx = ck * kG + t;
+            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            const uint8_t* vp = rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
+            if constexpr (CPV == 1) {
+                vr[t][0] = *reinterpret_cast<const uint16_t*>(vp);
+            } else if constexpr (CPV == 2) {
+                vr[t][0] = *reinterpret_cast<const uint32_t*>(vp);
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2*>(vp);
+                vr[t][0] = x.x;
+                vr[t][1] = x.y;
+            }
+        }
+    };
+    constexpr bool kEarly = D <= 128;  // d = 256: too many registers to hold a chunk across the blocks
+    if (kEarly && ck0 < rc) load_chunk(ck0);
+
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
         s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
@@ -385,45 +426,8 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         for (int c = 0; c < CPV * NACC; ++c) o[gq][c] = 0.f;
     }
 
-    // residual chunks: fp16 rows from the ring, in token order
-    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
-    const int ring = (int)g.ring_slots;
-    const int slot0 = (int)(a.n_quant % g.ring_slots);
-    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {  // chunk ck goes to wave NWAVES - 1 - ck % NWAVES
-        // key rows of this lane's tokens and column; value rows of its channels, all 32 tokens
-        uint4 kraw[TPL][2];
-        bool valid[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int idx = ck * kG + tl + TL * i;
-            valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
-            slot -= slot >= ring ? ring : 0;
-            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
-        }
-        uint16_t vr[kG][CPV];
-#pragma unroll
-        for (int t = 0; t < kG; ++t) {
-            const int idx = ck * kG + t;
-            int slot = slot0 + (idx < (int)nres ? idx : 0);
-            slot -= slot >= ring ? ring : 0;
-            const uint16_t* vp = reinterpret_cast<const uint16_t*>(rbase + (size_t)slot * 4 * D + 2 * D) + cv0;
-            if constexpr (CPV == 1) {
-                vr[t][0] = vp[0];
-            } else if constexpr (CPV == 2) {
-                const uint32_t x = *reinterpret_cast<const uint32_t*>(vp);
-                vr[t][0] = (uint16_t)x;
-                vr[t][1] = (uint16_t)(x >> 16);
-            } else {
-                const uint2 x = *reinterpret_cast<const uint2*>(vp);
-                vr[t][0] = (uint16_t)x.x;
-                vr[t][1] = (uint16_t)(x.x >> 16);
-                vr[t][2] = (uint16_t)x.y;
-                vr[t][3] = (uint16_t)(x.y >> 16);
-            }
-        }
+    // one residual chunk (rows loaded by load_chunk)
+    auto chunk_math = [&]() {
         float sc[QG][TPL];
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) {
@@ -469,11 +473,13 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
             for (int k = 0; k < CPV; ++k)
 #pragma unroll
-                for (int t = 0; t < kG; ++t)
-                    o[gq][k * NACC + t % NACC] = fmaf(pv[t], h2f(vr[t][k]), o[gq][k * NACC + t % NACC]);
+                for (int t = 0; t < kG; ++t) {
+                    const float v = (k & 1) ? half_hi(vr[t][k / 2]) : half_lo(vr[t][k / 2]);
+                    o[gq][k * NACC + t % NACC] = fmaf(pv[t], v, o[gq][k * NACC + t % NACC]);
+                }
         }
         wave_lds_order();
-    }
+    };
 
     // key blocks: a ring of PF register sets, the loads of the next PF - 1
     // blocks in flight while one is computed
@@ -561,10 +567,24 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         for (int k = 0; k < PF; ++k) {
             const int jj = j + k * NWAVES;
             if (jj >= j1) break;
+            // issue priority by work left: the SIMD favours older waves, so
+            // without it the younger waves of a work-group finish last
+            {
+                const int left = (j1 - jj + NWAVES - 1) / NWAVES + (ck0 < rc ? 1 : 0);
+                if (left >= 6) __builtin_amdgcn_s_setprio(3);
+                else if (left >= 4) __builtin_amdgcn_s_setprio(2);
+                else if (left >= 2) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
             const int jn = jj + (PF - 1) * NWAVES;
             if (jn < j1) load_block<D, BITS>(rs, (uint32_t)(jn * L::bytes), lo, rr[(k + PF - 1) % PF]);
             block_math(rr[k]);
         }
+    }
+
+    for (int ck = ck0; ck < rc; ck += NWAVES) {
+        if (!kEarly || ck != ck0) load_chunk(ck);
+        chunk_math();
     }
 
     // per-wave totals: the weight sum and each group's value-zero sum over the

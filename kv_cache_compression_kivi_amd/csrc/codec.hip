@@ -33,6 +33,15 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 // ------------------------------------------------------------------ codec
 
 // One group of N values -> (s, z) and codes written to out[i * stride].
+//
+// The bytes are those of the IEEE steps (s = (max - min) / (2^b - 1) by true
+// division, code = rint((x - z) / s)), computed faster:
+//   - min and max with v_min / v_max: which zero (+0 or -0) they return never
+//     shows, since z = min + 0 drops the sign and a zero range clamps s;
+//   - q' = (x - z) * rcp(s), where rcp is within 1 ulp of 1/s, differs from the
+//     IEEE quotient q by at most (2^-23 + 2^-24) * 15.5 + 2^-20 < 2^-18 (codes
+//     <= 15), so rint(q') = rint(q) unless q' lies within 2^-18 of a half
+//     integer; within 2^-15 of one (ties included) the true division decides.
 template <int N, int BITS>
 __device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float& z, uint8_t* out,
                                             int stride) {
@@ -40,15 +49,18 @@ __device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) {
-        mn = x[i] < mn ? x[i] : mn;
-        mx = x[i] > mx ? x[i] : mx;
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
     }
     s = (mx - mn) / kQmax;
     if (!(s >= 1e-8f)) s = 1e-8f;
     z = mn + 0.0f;  // -0 -> +0
+    const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        float r = __builtin_rintf((x[i] - z) / s);
+        const float t = x[i] - z;
+        float r = __builtin_rintf(t * rs);
+        if (fabsf(fabsf(t * rs - r) - 0.5f) < 0x1p-15f) r = __builtin_rintf(t / s);
         r = r < 0.0f ? 0.0f : r;
         r = r > kQmax ? kQmax : r;
         out[i * stride] = (uint8_t)r;
