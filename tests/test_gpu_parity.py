@@ -131,6 +131,41 @@ def test_split_invariance_and_determinism():
     assert_attention_close(ref, oc.attend(q.cpu()))
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_ties_and_near_ties(bits):
+    """Groups whose range is 2^b - 1 (so s = 1, z = 0) with values on half
+    integers: (x - z) / s is exactly k + 0.5 and must round to even. Mixed in,
+    values one fp16 step off a half integer (just on either side of a tie), and
+    groups of range 1 (s = 1/(2^b - 1), not a power of two). Bit-exact against
+    the oracle."""
+    _announce("ties", bits)
+    qmax = (1 << bits) - 1
+    G, d, T = 32, 128, 32 * 6 + 128
+    rng = np.random.default_rng(bits)
+    halves = np.arange(qmax) + 0.5                      # every tie k + 0.5
+    eps = np.float16(2.0 ** -10)                          # an fp16 step near 1..2
+    pool = np.concatenate([halves, halves + eps, halves - eps, np.arange(qmax + 1)])
+    x = rng.choice(pool, size=(T, d)).astype(np.float32)
+    # every key channel block and every value group holds 0 and qmax: s = 1
+    for j in range(T // G):
+        x[j * G, :] = 0.0
+        x[j * G + 1, :] = qmax
+    x[:, 0::32] = 0.0
+    x[:, 1::32] = qmax
+    # a few channels / groups of range 1 instead
+    x[:, 5] = rng.choice(np.linspace(0, 1, 17), size=T)
+    k = torch.from_numpy(x.astype(np.float16)).reshape(1, 1, T, d)
+    v = torch.from_numpy(np.ascontiguousarray(x[::-1]).astype(np.float16)).reshape(1, 1, T, d)
+    cache = kv.KiviCache(1, 1, 1, d, bits, max_tokens=T, device=DEV)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache(1, 1, 1, d, bits, max_tokens=T)
+    oc.append(k, v)
+    oc.flush()
+    compare_unit(cache, oc, 0, 0)
+
+
 def test_errors_on_device():
     _announce("errors")
     cache = kv.KiviCache(1, 1, 1, 128, 2, max_tokens=64)
