@@ -259,7 +259,8 @@ class KiviCache:
         return out
 
     def decode_step(self, k, v, q, out=None, stream=None) -> int:
-        """append(1) + flush when a full group is past the residual + attend; returns tokens flushed."""
+        """append(1) + flush when a full group is past the residual + attend, in one
+        call; returns the output (the tokens flushed are in self.last_flushed)."""
         import torch
         self._check_kv(k, v)
         c = self.cfg

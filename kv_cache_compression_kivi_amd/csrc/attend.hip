@@ -294,6 +294,20 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 // waves; more buys nothing once the HBM queue is full).
 constexpr int attend_prefetch(int D, int QG) { return QG == 1 && D <= 128 ? 3 : 2; }
 
+// Copies the token appended by this call (a.t_new) of unit u into its ring
+// slot: 16 bytes per lane, key row then value row (one wave).
+template <int D>
+__device__ __forceinline__ void write_new_token(const AttendArgs& a, int64_t u, const uint8_t* rbase) {
+    constexpr int CH = D / 8;  // 16-byte chunks per fp16 row
+    const int lane = threadIdx.x & 63;
+    const int slot = (int)(a.t_new % a.g.ring_slots);
+    for (int i = lane; i < 2 * CH; i += 64) {
+        const int kv = i / CH, c = i % CH;
+        const uint4 x = reinterpret_cast<const uint4*>((kv ? a.v_new : a.k_new) + u * D)[c];
+        reinterpret_cast<uint4*>(const_cast<uint8_t*>(rbase) + (size_t)slot * 4 * D + (size_t)kv * 2 * D)[c] = x;
+    }
+}
+
 // Two lane layouts per wave. Key side: lane = tl * NW + w scores tokens
 // tl + TL*i against channels [16w, 16w + 16). Value side: lane L accumulates
 // channels [L*CPV, L*CPV + CPV) over all 32 tokens of a chunk, with the
@@ -370,7 +384,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             valid[i] = idx < (int)nres;
             int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
             slot -= slot >= ring ? ring : 0;
-            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            // the token appended by this call comes from its input row
+            const uint4* kp = a.n_quant + idx == a.t_new
+                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
+                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
             kraw[i][0] = kp[0];
             kraw[i][1] = kp[1];
         }
@@ -379,7 +396,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             const int idx = ck * kG + t;
             int slot = slot0 + (idx < (int)nres ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            const uint8_t* vp = rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
+            const uint8_t* vp = a.n_quant + idx == a.t_new
+                                    ? reinterpret_cast<const uint8_t*>(a.v_new + u * D + cv0)
+                                    : rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
             if constexpr (CPV == 1) {
                 vr[t][0] = *reinterpret_cast<const uint16_t*>(vp);
             } else if constexpr (CPV == 2) {
@@ -393,6 +412,8 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     };
     constexpr bool kEarly = D <= 128;  // d = 256: too many registers to hold a chunk across the blocks
     if (kEarly && ck0 < rc) load_chunk(ck0);
+    if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0)
+        write_new_token<D>(a, u, rbase);
 
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
@@ -893,6 +914,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
     const int slot0 = (int)(a.n_quant % g.ring_slots);
+    if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0) write_new_token<D>(a, u, rbase);
     for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
         uint4 kraw[TPL][2];
         bool valid[TPL];
@@ -902,7 +924,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             valid[i] = idx < (int)nres;
             int slot = slot0 + (valid[i] ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            const uint4* kp = reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            const uint4* kp = a.n_quant + idx == a.t_new
+                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
+                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
             kraw[i][0] = kp[0];
             kraw[i][1] = kp[1];
         }
@@ -912,7 +936,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             const int idx = ck * kG + t;
             int slot = slot0 + (idx < (int)nres ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            vr[t] = *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
+            vr[t] = a.n_quant + idx == a.t_new
+                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
+                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
         }
         float sc[QG][TPL];
 #pragma unroll

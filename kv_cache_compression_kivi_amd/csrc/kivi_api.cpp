@@ -250,13 +250,11 @@ int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split) {
     return KIVI_OK;
 }
 
-int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
-    int rc = check_handle(cache);
-    if (rc != KIVI_OK) return rc;
-    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
-    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
-    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
-    if (cache->n_tokens == 0) return fail(KIVI_E_EMPTY, "attention on an empty cache");
+namespace {
+// The attention launch; (k_new, v_new, t_new) carry a token appended in the
+// same step that is not in the ring yet (t_new < 0: none).
+int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
+                const void* v_new, int64_t t_new) {
     kivi::AttendPlan p = attend_plan(cache);
     kivi::AttendArgs a;
     a.g = geom(cache);
@@ -270,10 +268,24 @@ int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float*
     a.qg = p.qg;
     a.nwaves = p.nwaves;
     a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.t_new = t_new;
     (void)hipGetLastError();
     hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(cache, "attend launch", e);
     return KIVI_OK;
+}
+}  // namespace
+
+int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
+    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
+    if (cache->n_tokens == 0) return fail(KIVI_E_EMPTY, "attention on an empty cache");
+    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, -1);
 }
 
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
@@ -283,16 +295,30 @@ int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void
     if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
     if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
     if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
-    rc = kivi_append(cache, k, v, 1, stream);  // validates k, v and the capacity before launching
-    if (rc != KIVI_OK) return rc;
-    int32_t flushed = 0;
-    const int64_t n_res = cache->n_tokens - cache->n_quant;
-    if (n_res >= (int64_t)cache->cfg.residual + cache->cfg.k_block) {
-        rc = kivi_flush(cache, stream, &flushed);
+    if (!k || !v) return fail(KIVI_E_INVAL, "k and v must be device pointers");
+    if (!aligned16(k) || !aligned16(v)) return fail(KIVI_E_INVAL, "k and v must be 16-byte aligned");
+    if (cache->n_tokens + 1 > cache->cfg.max_tokens)
+        return fail(KIVI_E_CAPACITY, "append of 1 token would exceed max_tokens (" +
+                                         std::to_string(cache->cfg.max_tokens) + ")");
+    // The same result as kivi_append(1) + kivi_flush (when a whole group lies
+    // beyond the newest R) + kivi_attend_decode, in at most two launches: the
+    // quantization of every group that leaves the residual (the new token,
+    // should it be one of them, read from k and v), then the attention, which
+    // also writes the new token into its ring slot.
+    const int64_t G = cache->cfg.k_block, R = cache->cfg.residual;
+    const int64_t nt0 = cache->n_tokens;
+    kivi::AppendPlan p = kivi::plan_append(nt0, cache->n_quant, 1, R, G);
+    const int64_t n_res = p.nt1 - p.nq1;
+    const int64_t nq = n_res >= R + G ? p.nq1 + kivi::plan_flush(p.nt1, p.nq1, R, G) : p.nq1;
+    (void)hipGetLastError();
+    if (nq > p.nq0) {
+        rc = quantize_blocks(cache, p.nq0 / G, nq / G, nt0, k, v, 1, static_cast<hipStream_t>(stream));
         if (rc != KIVI_OK) return rc;
     }
-    if (n_flushed) *n_flushed = flushed;
-    return kivi_attend_decode(cache, q, q_dtype, out, stream);
+    cache->n_tokens = p.nt1;
+    cache->n_quant = nq;
+    if (n_flushed) *n_flushed = (int32_t)(nq - p.nq1);
+    return attend_call(cache, q, q_dtype, out, stream, k, v, nt0 >= nq ? nt0 : -1);
 }
 
 }  // extern "C"

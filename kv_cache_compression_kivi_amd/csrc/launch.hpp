@@ -55,6 +55,12 @@ struct AttendArgs {
     int32_t n_split;
     int32_t qg, nwaves;
     float scale_log2;  // log2(e) / sqrt(d)
+    // A token appended by this call (t_new >= 0), not yet in the ring: its rows
+    // are k_new / v_new + unit * d. The work-group that owns a unit's residual
+    // writes them to the ring slot, and the attention reads them from there.
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t t_new;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);

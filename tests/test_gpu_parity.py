@@ -166,6 +166,42 @@ def test_quantizer_ties_and_near_ties(bits):
     compare_unit(cache, oc, 0, 0)
 
 
+@pytest.mark.parametrize("B,Hkv,Hq,d,bits,R,T0,steps", [
+    (2, 2, 2, 128, 2, 128, 200, 70),   # MHA, flushes at the steps that complete a group past R
+    (1, 2, 8, 128, 4, 32, 40, 40),     # GQA (matrix-core kernel), small residual
+    (2, 1, 1, 64, 2, 0, 5, 40),        # no residual: a flush takes the new token itself
+    (1, 1, 4, 256, 2, 64, 100, 35),    # d = 256, GQA on the vector path
+])
+def test_decode_step_parity(B, Hkv, Hq, d, bits, R, T0, steps):
+    """kivi_decode_step (quantize when due, then one attention launch that also
+    writes the new token into the ring) against the oracle run token by token:
+    attention at every few steps, the whole cache bit-exact at the end."""
+    _announce("decode_step", B, Hkv, Hq, d, bits, R, T0, steps)
+    wl = KVWorkload(B, Hkv, d, seed=11 + R, device="cpu")
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T0 + steps, residual=R, device=DEV)
+    oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T0 + steps, residual=R)
+    k, v = wl.kv(0, T0)
+    cache.append(k.to(DEV), v.to(DEV))
+    oc.append(k, v)
+    for i in range(steps):
+        kt, vt = wl.kv(T0 + i, 1)
+        q = wl.q(Hq, step=i)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), q.to(DEV))
+        oc.append(kt, vt)
+        nt, nq = oc.state()
+        if nt - nq >= R + 32:
+            assert oc.flush() == cache.last_flushed
+        else:
+            assert cache.last_flushed == 0
+        assert cache.state()[:2] == oc.state()
+        if i % 7 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            assert_attention_close(out.cpu().numpy(), oc.attend(q))
+    torch.cuda.synchronize()
+    for u in range(B * Hkv):
+        compare_unit(cache, oc, u, u)
+
+
 def test_errors_on_device():
     _announce("errors")
     cache = kv.KiviCache(1, 1, 1, 128, 2, max_tokens=64)
