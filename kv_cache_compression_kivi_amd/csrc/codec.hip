@@ -32,7 +32,7 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 
 // ------------------------------------------------------------------ codec
 
-// One group of N values -> (s, z) and codes written to out[i * stride].
+// One group of N values -> (s, z) and its codes.
 //
 // The bytes are those of the IEEE steps (s = (max - min) / (2^b - 1) by true
 // division, code = rint((x - z) / s)), computed faster:
@@ -43,8 +43,7 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 //     <= 15), so rint(q') = rint(q) unless q' lies within 2^-18 of a half
 //     integer; within 2^-15 of one (ties included) the true division decides.
 template <int N, int BITS>
-__device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float& z, uint8_t* out,
-                                            int stride) {
+__device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float& z, uint8_t (&out)[N]) {
     constexpr float kQmax = float((1 << BITS) - 1);
     float mn = x[0], mx = x[0];
 #pragma unroll
@@ -63,7 +62,7 @@ __device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float
         if (fabsf(fabsf(t * rs - r) - 0.5f) < 0x1p-15f) r = __builtin_rintf(t / s);
         r = r < 0.0f ? 0.0f : r;
         r = r > kQmax ? kQmax : r;
-        out[i * stride] = (uint8_t)r;
+        out[i] = (uint8_t)r;
     }
 }
 
@@ -77,10 +76,11 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     constexpr int PER = 32 / BITS;
     constexpr int NT = 2 * D;
     constexpr int CPR = D / 8;  // 16-byte chunks per fp16 row
+    // fp16 rows of the block; once read, the same memory holds the codes (bytes)
     __shared__ __align__(16) uint16_t sk[kG * D];
     __shared__ __align__(16) uint16_t sv[kG * D];
-    __shared__ __align__(16) uint8_t ck[kG * D];
-    __shared__ __align__(16) uint8_t cv[kG * D];
+    uint8_t* const ck = reinterpret_cast<uint8_t*>(sk);
+    uint8_t* const cv = reinterpret_cast<uint8_t*>(sv);
 
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
@@ -107,13 +107,14 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     __syncthreads();
 
     uint8_t* rec = g.base + g.off_blocks + (size_t)u * g.unit_stride + (size_t)j * g.block_bytes;
+    uint8_t codes[kG];  // kG == kVG
     if (tid < D) {
         const int c = tid;
         float x[kG];
 #pragma unroll
         for (int t = 0; t < kG; ++t) x[t] = half_bits_to_float(sk[t * D + c]);
         float s, z;
-        quant_group<kG, BITS>(x, s, z, &ck[c], D);
+        quant_group<kG, BITS>(x, s, z, codes);
         reinterpret_cast<float2*>(rec + g.rec_ksz)[c] = make_float2(s, z);
     } else {
         const int idx = tid - D;
@@ -122,8 +123,21 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
 #pragma unroll
         for (int i = 0; i < kVG; ++i) x[i] = half_bits_to_float(sv[t * D + grp * kVG + i]);
         float s, z;
-        quant_group<kVG, BITS>(x, s, z, &cv[t * D + grp * kVG], 1);
+        quant_group<kVG, BITS>(x, s, z, codes);
         reinterpret_cast<float2*>(rec + g.rec_vsz)[t * NG + grp] = make_float2(s, z);
+    }
+    __syncthreads();  // every thread is done reading the fp16 rows
+    if (tid < D) {
+#pragma unroll
+        for (int t = 0; t < kG; ++t) ck[t * D + tid] = codes[t];
+    } else {
+        const int idx = tid - D;
+        const int t = idx / NG, grp = idx % NG;
+#pragma unroll
+        for (int i = 0; i < kVG; i += 4)
+            *reinterpret_cast<uint32_t*>(&cv[t * D + grp * kVG + i]) =
+                (uint32_t)codes[i] | (uint32_t)codes[i + 1] << 8 | (uint32_t)codes[i + 2] << 16 |
+                (uint32_t)codes[i + 3] << 24;
     }
     __syncthreads();
 
