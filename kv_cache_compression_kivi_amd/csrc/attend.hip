@@ -51,9 +51,10 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint
 
 // ------------------------------------------------------------ lane reductions
 
+// Lane i reads the lane the DPP control names; a source outside the row reads 0.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kSwap1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -731,25 +732,32 @@ __device__ __forceinline__ uint32_t bytes_d(uint32_t v0, uint32_t v1, uint32_t v
     return lo | hi;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
 constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kQuadBcast0 = 0x00;
 
 // The maximum over a wave (every lane holds it).
 __device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dppf<kSwap1>(x));
-    x = fmaxf(x, dppf<kSwap2>(x));
-    x = fmaxf(x, dppf<kHalfMirror>(x));
-    x = fmaxf(x, dppf<kMirror>(x));
+    x = fmaxf(x, dpp<kSwap1>(x));
+    x = fmaxf(x, dpp<kSwap2>(x));
+    x = fmaxf(x, dpp<kHalfMirror>(x));
+    x = fmaxf(x, dpp<kMirror>(x));
     return rows_max(x);
 }
 
-// 23-bit integer of x (|x| < 2^22) as three signed bytes: (Q + 0x808080) ^ 0x808080.
-__device__ __forceinline__ uint32_t digits3(float x) {
-    const int qi = (int)__builtin_rintf(x);
-    return ((uint32_t)qi + 0x808080u) ^ 0x808080u;
+// The 23-bit integer Q = rint(a b 2^-e) (|a b| < 2^(22+e)) as three signed
+// bytes, (Q + 0x808080) ^ 0x808080 in bits 0..23. One fma with the magic
+// 1.5 2^(23+e) rounds the exact product to a multiple of 2^e (ties to even),
+// so the low 24 bits of the result's encoding hold (e & 1) << 23 (the
+// exponent's low bit, as 150 + e has the parity of e) above 2^22 + Q; the
+// bias 0x408080 - ((e & 1) << 23) turns them into Q + 0x808080.
+struct DigitScale {
+    float magic;
+    uint32_t bias;
+};
+__device__ __forceinline__ DigitScale digit_scale(int e) {
+    return {ldexpf(1.5f, 23 + e), 0x408080u - ((uint32_t)(e & 1) << 23)};
+}
+__device__ __forceinline__ uint32_t digits3(float a, float b, DigitScale ds) {
+    return (__float_as_uint(fmaf(a, b, ds.magic)) + ds.bias) ^ 0x808080u;
 }
 
 template <int D, int BITS, int NWAVES>
@@ -1014,18 +1022,19 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int k = 0; k < 4; ++k) smax = fmaxf(smax, r.ksz[kc][k][0]);
-        smax = fmaxf(smax, dppf<kSwap1>(smax));
-        smax = fmaxf(smax, dppf<kSwap2>(smax));
-        smax = fmaxf(smax, dppf<kHalfMirror>(smax));
-        smax = fmaxf(smax, dppf<kMirror>(smax));  // each row of 16 lanes covers every channel
-        const int es = __builtin_amdgcn_frexp_expf(smax);
+        smax = fmaxf(smax, dpp<kSwap1>(smax));
+        smax = fmaxf(smax, dpp<kSwap2>(smax));
+        smax = fmaxf(smax, dpp<kHalfMirror>(smax));
+        smax = fmaxf(smax, dpp<kMirror>(smax));  // each row of 16 lanes covers every channel
+        const int es = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(smax));
+        const DigitScale dk = digit_scale(es);
         float zp = 0.f;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             uint32_t vq[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                vq[k] = digits3(qn[kc][k] * ldexpf(r.ksz[kc][k][0], -es));
+                vq[k] = digits3(qn[kc][k], r.ksz[kc][k][0], dk);
                 zp = fmaf(qv[kc][k], r.ksz[kc][k][1], zp);
             }
 #pragma unroll
@@ -1076,7 +1085,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
                 const float f = (float)acc[r2];
-                const float comb = fmaf(dppf<kRowShl2>(f), 65536.0f, fmaf(dppf<kRowShl1>(f), 256.0f, f));
+                const float comb = fmaf(dpp<kRowShl2>(f), 65536.0f, fmaf(dpp<kRowShl1>(f), 256.0f, f));
                 sc[tt][r2] = fmaf(comb, ks, zs);
             }
         }
@@ -1093,6 +1102,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             }
         }
         const float mg = gl == 0 ? m[0] : (gl == 1 ? m[1] : (gl == 2 ? m[2] : m[3]));
+        const DigitScale dv = digit_scale(ev - 22);
         // 4. weights p s_t of (query gl, value group dq) as digits, rows 4gl + d
         //    of the value operand: one word per tile (lane group 2tt + rho/2, word rho%2)
 #pragma unroll
@@ -1101,10 +1111,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
                 const float pr = __builtin_amdgcn_exp2f(sc[tt][r2] - mg);  // valid in lanes dq == 0
-                const float p = dppf<kQuadBcast0>(pr);
+                const float p = dpp<kQuadBcast0>(pr);
                 if (dq == 0) l_blk += p;
                 z_blk = fmaf(p, r.vsz[tt][r2].y, z_blk);
-                vp[r2] = digits3(p * ldexpf(r.vsz[tt][r2].x, 22 - ev));
+                vp[r2] = digits3(p, r.vsz[tt][r2].x, dv);
             }
 #pragma unroll
             for (int d = 0; d < 3; ++d)
