@@ -19,6 +19,8 @@ Also measured in the same run:
   * the attention kernel alone (one launch per kivi_attend_decode), timed with
     HIP events on the stream it runs on, for the roofline entry;
   * prefill quantize-append (append(T) + flush into an empty cache): tokens/s;
+  * single-token append latency (ring write) and one 32-token flush: latency
+    and GB/s;
   * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
 """
 
@@ -318,7 +320,37 @@ def main():
     pf_tok_s = n_pf * B * Hkv * T / (pf_ms * 1e-3)
     pf_gbs = pf_bytes / (pf_ms * 1e-3) / 1e9
 
+    # single-token appends (ring writes only) and one 32-token flush, on the
+    # caches just prefilled: n_res = R there, so 32 appends fit before the ring
+    # is full and the flush then quantizes exactly one group
+    ap_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_pf)]
+    n_ap = 32
+    for i in range(n_pf):
+        h = handles[i]
+        assert caches[i].state()[2] == 128
+        ap_ev[i][0].record(stream)
+        for t in range(n_ap):
+            kp, vp = kvp[t % pool]
+            rc = lib.kivi_append(h, kp, vp, 1, sp)
+            if rc != 0:
+                raise kv.KiviError(rc, kv.kivi_last_error())
+        ap_ev[i][1].record(stream)
+        rc = lib.kivi_flush(h, sp, ctypes.byref(nfl))
+        if rc != 0:
+            raise kv.KiviError(rc, kv.kivi_last_error())
+        ap_ev[i][2].record(stream)
+        assert nfl.value == 32, nfl.value
+    torch.cuda.synchronize()
+    ap_us = sum(e[0].elapsed_time(e[1]) for e in ap_ev) * 1e3 / (n_pf * n_ap)
+    fl_us = sum(e[1].elapsed_time(e[2]) for e in ap_ev) * 1e3 / n_pf
+    fl_gbs = sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in range(n_pf)) / n_pf / (fl_us * 1e-6) / 1e9
+
     traffic = _traffic_from_profile(args.workload)
+    plan = caches[0].plan_attend()
+    gqa4 = (Hq // Hkv) % 4 == 0 and d == 128
+    attend_kernel_name = ("kivi_attend_decode = " + ("attend_gqa_kernel (four query heads, int8 matrix cores)"
+                                                     if gqa4 else "attend_kernel") +
+                          (" + combine_kernel (merge of %d splits)" % plan[0] if plan[0] > 1 else ", one split"))
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -340,9 +372,13 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "quantize_append_tokens_per_s": round(pf_tok_s, 1),
         "quantize_append_gbs": round(pf_gbs, 2),
+        "append_1_token_us": round(ap_us, 3),
+        "append_1_token_tokens_per_s": round(units / (ap_us * 1e-6), 1),
+        "flush_32_tokens_us": round(fl_us, 3),
+        "flush_32_tokens_gbs": round(fl_gbs, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "kivi_attend_decode = attend_kernel (split-K partials) + combine_kernel (merge)",
+            "kernel": attend_kernel_name,
             "achieved": round(att_gbs, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
