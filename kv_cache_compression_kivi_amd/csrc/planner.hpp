@@ -138,8 +138,8 @@ inline void attend_shape(int32_t group, int32_t head_dim, int32_t* qg, int32_t* 
     *nwaves = attend_waves(*qg, head_dim);
 }
 
-// Split-K plan. Enough work-groups for one round over the 256 CUs (one
-// 8-wave work-group per CU, or four 4-wave ones), at least 2 key blocks per
+// Split-K plan. Enough work-groups for 8 waves on each of the 256 CUs (one
+// 8-wave work-group or two 4-wave ones per CU), at least 2 key blocks per
 // wave in every split, at most max_splits partials per query head; no split
 // (and no merge launch) when the units alone fill the chip. forced > 0 fixes
 // the split count instead.
@@ -152,7 +152,7 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
     if (forced > 0) {
         n = forced;
     } else {
-        const int64_t target_waves = 256 * (p.nwaves == 8 ? 8 : 16);
+        const int64_t target_waves = 256 * 8;
         n = (target_waves + wgs_per_split * p.nwaves - 1) / (wgs_per_split * p.nwaves);
         const int64_t cap = n_blocks / (2 * p.nwaves);
         if (n > cap) n = cap;
