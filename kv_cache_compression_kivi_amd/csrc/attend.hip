@@ -678,8 +678,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 // and s_t < 2^Ev per block; p <= 1) and split into three signed 8-bit
 // digits, so every product and sum is exact in int32; the only rounding is
 // that of q~ and p~ to 2^-22 of their bounds. The digits of query (or weight)
-// row g sit in columns (or rows) 4g .. 4g + 2 of a 16-wide tile; 4g + 3 is zero.
-// Scores: v_mfma_i32_16x16x64_i8, 16 tokens x 16 columns x 64 channels.
+// row g sit in rows 4g .. 4g + 2 of a 16-row tile operand; row 4g + 3 is zero.
+// Scores: v_mfma_i32_16x16x64_i8, 16 rows (query, digit) x 16 tokens x 64
+// channels, so a lane's four results are the digit sums of one query and one
+// token (lane / 16 and lane % 16).
 // Values: v_mfma_i32_16x16x32_i8, 16 rows x 16 channels x the block's 32 tokens.
 // The fp16 residual runs on the vector units as in attend_kernel.
 
@@ -721,7 +723,7 @@ struct GqaRegs {
     static constexpr int VT = D / 16;  // 16-channel value tiles
     uint32_t kc[2][KC][KW];            // key words of score row l%16 of tile tt, lane group l/16 of each chunk
     float ksz[KC][4][2];               // (s, z) of the digit producer's channels
-    float2 vsz[2][4];                  // (s, z) of the tokens of rows 4(l/16) + r, value group (l%16)%4
+    float2 vsz[2][4];                  // (s, z) of the tokens of columns 4((l%16)/4) + r, value group l%4
     uint32_t vc[VT];                   // value word of channel 16 vt + l%16 used by lane group l/16
 };
 
@@ -758,6 +760,52 @@ __device__ __forceinline__ DigitScale digit_scale(int e) {
 }
 __device__ __forceinline__ uint32_t digits3(float a, float b, DigitScale ds) {
     return (__float_as_uint(fmaf(a, b, ds.magic)) + ds.bias) ^ 0x808080u;
+}
+
+// Staging of the four-query kernel's blocks: each wave streams its next
+// blocks from HBM straight into a ring of LDS slots (buffer loads with the LDS
+// bit, a record copied as it is, 16 bytes per lane per load), so the blocks in
+// flight hold no registers. The loads are asm, so the compiler tracks none of
+// them: each slot is read after an explicit s_waitcnt vmcnt(N), N the staging
+// loads issued after it (vector-memory loads retire in order; loads the
+// compiler issues later only make the wait stricter), and a slot is refilled
+// after an s_waitcnt lgkmcnt(0), once its reads have returned. M0 holds the
+// LDS destination of each load (one SALU write and a wait state before it);
+// nothing else in this kernel keeps a value in M0.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ uint32_t lds_address(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int NL>
+__device__ __forceinline__ void stage_record(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint32_t slot, uint32_t voff) {
+    const int so = __builtin_amdgcn_readfirstlane((int)soff);
+    const uint32_t m = __builtin_amdgcn_readfirstlane(slot);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < NL; ++c)
+        asm volatile(
+            "s_mov_b32 m0, %[m]\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %[v], %[rs], %[so] offen nt lds"
+            :
+            : [m] "s"(m + 1024u * c), [v] "v"(voff + 1024u * c), [rs] "s"(rs), [so] "s"(so)
+            : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%[n])" : : [n] "i"(N) : "memory");
+}
+
+// Waits until the staged block with `later` staged blocks after it has landed.
+template <int NL, int NS>
+__device__ __forceinline__ void wait_staged(int later) {
+    static_assert(NS <= 3, "two later stages at most");
+    if (NS > 2 && later >= 2) wait_vmem<2 * NL>();
+    else if (NS > 1 && later >= 1) wait_vmem<NL>();
+    else wait_vmem<0>();
 }
 
 template <int D, int BITS, int NWAVES>
@@ -815,43 +863,51 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     auto kw_off = [&](int tt, int kc) { return ob_kw + (16 * tt * L::W + (BITS == 2 ? 4 : 8) * kc) * 4; };
     auto ks_off = [&](int kc, int k) { return ob_ks + gqa_channel<BITS>(kc, 0, k) * 8; };
     auto vs_off = [&](int tt, int r) {
-        return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * rho + r)) * NG + dq) * 8;
+        return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
     };
-    auto load = [&](int j, R& r) {
-        const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)j * L::bytes));
+    // staged blocks: NS slots per wave (LDS for two 4-wave work-groups per CU)
+    constexpr int NS = BITS == 2 ? 3 : 2;
+    constexpr int NL = L::bytes / 1024;  // staging loads per block
+    static_assert(L::bytes % 1024 == 0, "a record is a whole number of 1 KB wave loads");
+    __shared__ __align__(16) uint8_t s_stage[NWAVES][NS][L::bytes];
+    const uint32_t stage_lds = lds_address(s_stage[wave][0]);
+    auto stage = [&](int j, int k) {
+        stage_record<NL>(rs, (uint32_t)j * L::bytes, stage_lds + k * L::bytes, 16u * lane);
+    };
+    // this lane's shares of a staged block
+    auto read_slot = [&](int k, R& r) {
+        const uint8_t* sb = s_stage[wave][k];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 if constexpr (BITS == 2) {
-                    r.kc[tt][kc][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, kw_off(tt, kc), so, 2);
+                    r.kc[tt][kc][0] = *reinterpret_cast<const uint32_t*>(sb + kw_off(tt, kc));
                 } else {
-                    const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, kw_off(tt, kc), so, 2);
-                    r.kc[tt][kc][0] = x[0];
-                    r.kc[tt][kc][1] = x[1];
+                    const uint2 x = *reinterpret_cast<const uint2*>(sb + kw_off(tt, kc));
+                    r.kc[tt][kc][0] = x.x;
+                    r.kc[tt][kc][1] = x.y;
                 }
             }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, ks_off(kc, k), so, 2);
-                r.ksz[kc][k][0] = __uint_as_float(x[0]);
-                r.ksz[kc][k][1] = __uint_as_float(x[1]);
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const float2 x = *reinterpret_cast<const float2*>(sb + ks_off(kc, k2));
+                r.ksz[kc][k2][0] = x.x;
+                r.ksz[kc][k2][1] = x.y;
             }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, vs_off(tt, rr), so, 2);
-                r.vsz[tt][rr] = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
-            }
+            for (int rr = 0; rr < 4; ++rr) r.vsz[tt][rr] = *reinterpret_cast<const float2*>(sb + vs_off(tt, rr));
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-            r.vc[vt] = __builtin_amdgcn_raw_buffer_load_b32(rs, ob_vc + 16 * vt * BITS * 4, so, 2);
+        for (int vt = 0; vt < VT; ++vt) r.vc[vt] = *reinterpret_cast<const uint32_t*>(sb + ob_vc + 16 * vt * BITS * 4);
     };
-    R cur;
-    if (j0 < j1) load(j0, cur);
+    // the first blocks go in flight before anything waits
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        if (j0 + k * NWAVES < j1) stage(j0 + k * NWAVES, k);
 
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
@@ -889,9 +945,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             qv[kc][k] = x;
         }
 
-    // running state. m: per query, uniform. Residual part (vector layout): l_res
-    // and o_res per query. Blocks (matrix layout): l_blk for query gl, z_blk for
-    // (gl, dq), o_blk[vt] for query rho and channel 16vt + n.
+    // running state, two parts merged at the end. Residual (vector layout): m,
+    // l_res and o_res per query. Blocks (matrix layout, query rho = lane / 16):
+    // running max m_b, weight sum l_b of this lane's tokens, value-zero sum z_b
+    // of group dq over the tokens of quad gl, o_blk[vt] for channel 16vt + n.
     float m[QG], l_res[QG], o_res[QG][CPV * NACC], o_blk[VT];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
@@ -902,20 +959,12 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     }
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) o_blk[vt] = 0.f;
-    float l_blk = 0.f, z_blk = 0.f;
-    // multiply every accumulator of query gq by alpha (a new running maximum)
+    float m_b = -INFINITY, l_b = 0.f, z_b = 0.f;
+    // multiply the residual accumulators of query gq by alpha (a new running maximum)
     auto rescale = [&](int gq, float alpha) {
         l_res[gq] *= alpha;
 #pragma unroll
         for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] *= alpha;
-        if (gl == gq) {
-            l_blk *= alpha;
-            z_blk *= alpha;
-        }
-        if (rho == gq) {
-#pragma unroll
-            for (int vt = 0; vt < VT; ++vt) o_blk[vt] *= alpha;
-        }
     };
 
     // residual chunks (vector units, as in attend_kernel)
@@ -1040,85 +1089,92 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
 #pragma unroll
             for (int d = 0; d < 3; ++d) s_kb[wave][kc][n >> 2][4 * rho + d][n & 3] = bytes_d(vq[0], vq[1], vq[2], vq[3], d);
         }
-        // key zeros: Z[g] = sum_c q[g][c] z[c], query g = row rho
-        zp = sum_cols<16>(zp);
-        const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 0));
-        const float z1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 16));
-        const float z2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 32));
-        const float z3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zp), 48));
-        const float zs = (gl == 0 ? z0 : (gl == 1 ? z1 : (gl == 2 ? z2 : z3))) * scale;
+        // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
+        const float zs = sum_cols<16>(zp) * scale;
         // bound of the block's value scales, for the weight digits
         float vmax = fmaxf(fmaxf(r.vsz[0][0].x, r.vsz[0][1].x), fmaxf(r.vsz[0][2].x, r.vsz[0][3].x));
         vmax = fmaxf(vmax, fmaxf(fmaxf(r.vsz[1][0].x, r.vsz[1][1].x), fmaxf(r.vsz[1][2].x, r.vsz[1][3].x)));
         ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(vmax)));
         wave_lds_order();
-        // 2. scores of the tiles' tokens, columns (g, digit): exact integer products
-        const float ks = ldexpf(scale, eq_gl + es - 22);  // sum Q code = 2^(22 - Eq - Es) sum q s code
-        float sc[2][4];
+        // 2. scores of query rho and token rt of each tile: the digit sums of
+        //    rows 4 rho .. 4 rho + 2 land in this lane's accumulators 0 .. 2
+        const float ks = ldexpf(scale, eq_mine + es - 22);  // sum Q code = 2^(22 - Eq - Es) sum q s code
+        float sc[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             v4i32 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                v4i32 av, bv;
+                v4i32 cv, qd;
                 if constexpr (BITS == 2) {
                     const uint32_t x = r.kc[tt][kc][0];
-                    av[0] = (int)(x & 0x03030303u);
-                    av[1] = (int)((x >> 2) & 0x03030303u);
-                    av[2] = (int)((x >> 4) & 0x03030303u);
-                    av[3] = (int)((x >> 6) & 0x03030303u);
+                    cv[0] = (int)(x & 0x03030303u);
+                    cv[1] = (int)((x >> 2) & 0x03030303u);
+                    cv[2] = (int)((x >> 4) & 0x03030303u);
+                    cv[3] = (int)((x >> 6) & 0x03030303u);
                 } else {
                     const uint32_t x0 = r.kc[tt][kc][0], x1 = r.kc[tt][kc][1];
-                    av[0] = (int)(x0 & 0x0F0F0F0Fu);
-                    av[1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
-                    av[2] = (int)(x1 & 0x0F0F0F0Fu);
-                    av[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
+                    cv[0] = (int)(x0 & 0x0F0F0F0Fu);
+                    cv[1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
+                    cv[2] = (int)(x1 & 0x0F0F0F0Fu);
+                    cv[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
                 }
                 const uint4 bb = *reinterpret_cast<const uint4*>(&s_kb[wave][kc][rho][n][0]);
-                bv[0] = (int)bb.x;
-                bv[1] = (int)bb.y;
-                bv[2] = (int)bb.z;
-                bv[3] = (int)bb.w;
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+                qd[0] = (int)bb.x;
+                qd[1] = (int)bb.y;
+                qd[2] = (int)bb.z;
+                qd[3] = (int)bb.w;
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qd, cv, acc, 0, 0, 0);
             }
-            // the digits of column 4g + d sit in lanes n .. n + 2 of each row
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) {
-                const float f = (float)acc[r2];
-                const float comb = fmaf(dpp<kRowShl2>(f), 65536.0f, fmaf(dpp<kRowShl1>(f), 256.0f, f));
-                sc[tt][r2] = fmaf(comb, ks, zs);
+            float comb;
+            if constexpr (BITS == 2) {
+                // |sums| <= 128 * 3 * 128 (digits 0, 1) and 128 * 3 * 64 (digit 2): exact in int32
+                comb = (float)(acc[0] + (acc[1] << 8) + (acc[2] << 16));
+            } else {
+                comb = fmaf((float)acc[2], 65536.0f, fmaf((float)acc[1], 256.0f, (float)acc[0]));
             }
+            sc[tt] = fmaf(comb, ks, zs);
         }
-        // 3. online softmax (valid in lanes with dq == 0: query gl)
-        float bm = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
-        bm = fmaxf(bm, fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        bm = rows_max(bm);
+        // 3. online softmax of query rho over the row's 32 tokens
+        float bm = fmaxf(sc[0], sc[1]);
+        bm = fmaxf(bm, dpp<kSwap1>(bm));
+        bm = fmaxf(bm, dpp<kSwap2>(bm));
+        bm = fmaxf(bm, dpp<kHalfMirror>(bm));
+        bm = fmaxf(bm, dpp<kMirror>(bm));
+        if (bm > m_b) {
+            const float alpha = __builtin_amdgcn_exp2f(m_b - bm);
+            l_b *= alpha;
+            z_b *= alpha;
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            const float bq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 4 * gq));
-            if (bq > m[gq]) {
-                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bq));
-                m[gq] = bq;
-            }
+            for (int vt = 0; vt < VT; ++vt) o_blk[vt] *= alpha;
+            m_b = bm;
         }
-        const float mg = gl == 0 ? m[0] : (gl == 1 ? m[1] : (gl == 2 ? m[2] : m[3]));
-        const DigitScale dv = digit_scale(ev - 22);
-        // 4. weights p s_t of (query gl, value group dq) as digits, rows 4gl + d
-        //    of the value operand: one word per tile (lane group 2tt + rho/2, word rho%2)
+        float pt[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
+            pt[tt] = __builtin_amdgcn_exp2f(sc[tt] - m_b);
+            l_b += pt[tt];
+        }
+        const DigitScale dv = digit_scale(ev - 22);
+        // 4. weights p s_t of value group dq for the tokens of quad gl (gathered
+        //    from its four lanes), as digits: rows 4 rho + d of the value operand,
+        //    one word per tile (lane group 2tt + gl/2, word gl%2)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float pq[4];
+            pq[0] = dpp<0x00>(pt[tt]);
+            pq[1] = dpp<0x55>(pt[tt]);
+            pq[2] = dpp<0xAA>(pt[tt]);
+            pq[3] = dpp<0xFF>(pt[tt]);
             uint32_t vp[4];
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
-                const float pr = __builtin_amdgcn_exp2f(sc[tt][r2] - mg);  // valid in lanes dq == 0
-                const float p = dpp<kQuadBcast0>(pr);
-                if (dq == 0) l_blk += p;
-                z_blk = fmaf(p, r.vsz[tt][r2].y, z_blk);
-                vp[r2] = digits3(p, r.vsz[tt][r2].x, dv);
+                z_b = fmaf(pq[r2], r.vsz[tt][r2].y, z_b);
+                vp[r2] = digits3(pq[r2], r.vsz[tt][r2].x, dv);
             }
 #pragma unroll
             for (int d = 0; d < 3; ++d)
-                s_va[wave][dq][2 * tt + rho / 2][4 * gl + d][rho % 2] = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
+                s_va[wave][dq][2 * tt + gl / 2][4 * rho + d][gl % 2] = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
         }
         wave_lds_order();
     };
@@ -1154,26 +1210,40 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     };
     // the next block's loads go out once the current block's key shares are
     // consumed, and fly during its value phase
-    R nx;
-    for (int j = j0; j < j1; j += 2 * NWAVES) {
+    // a block is read from its slot, the slot refilled with the block NS
+    // further on, then the block's math runs from registers
+    int slot = 0;
+    for (int j = j0; j < j1; j += NWAVES) {
+        wait_staged<NL, NS>((j1 - 1 - j) / NWAVES);
+        R r;
+        read_slot(slot, r);
+        if (j + NS * NWAVES < j1) stage(j + NS * NWAVES, slot);
         int ev;
-        key_math(cur, ev);
-        if (j + NWAVES < j1) load(j + NWAVES, nx);
-        value_math(cur, ev);
-        if (j + NWAVES >= j1) break;
-        key_math(nx, ev);
-        if (j + 2 * NWAVES < j1) load(j + 2 * NWAVES, cur);
-        value_math(nx, ev);
+        key_math(r, ev);
+        value_math(r, ev);
+        slot = slot + 1 == NS ? 0 : slot + 1;
     }
 
-    // per-wave totals
-    const float lb = rows_sum(l_blk);  // query gl over the four rows (lanes with dq == 0 hold it)
-    const float zb = rows_sum(z_blk);  // (query gl, group dq)
+    // per-wave totals. Block part of query rho (row rho): its max m_b, weight
+    // sum, value-zero sums of group dq; residual part per query: m, l_res, o_res
+    const float lb = sum_cols<16>(l_b);
+    float zb = z_b + dpp<kRor4>(z_b);
+    zb += dpp<kRor8>(zb);  // over the quads of the row: (query rho, group dq)
+    const float mr = rho == 0 ? m[0] : (rho == 1 ? m[1] : (rho == 2 ? m[2] : m[3]));
+    const float mt = fmaxf(mr, m_b);  // this wave's max of query rho
+    const float fb = m_b == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - mt);
+    float mq[QG], fr[QG];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+        mq[gq] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mt), 16 * gq));
+        fr[gq] = m[gq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gq] - mq[gq]);
+    }
     float lq[QG];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
-        lq[gq] = tok_sum<NW>(l_res[gq]) + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb), 4 * gq));
-    if (rho == 0) s_z[wave][gl][dq] = zb;
+        lq[gq] = tok_sum<NW>(l_res[gq]) * fr[gq] +
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb * fb), 16 * gq));
+    if (gl == 0) s_z[wave][rho][dq] = zb * fb;
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
@@ -1181,18 +1251,18 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < NACC; ++e) acc += o_res[gq][k * NACC + e];
-            s_o[wave][gq][cv0 + k] = acc;
+            s_o[wave][gq][cv0 + k] = acc * fr[gq];
         }
     wave_lds_order();
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
         const int c = 16 * vt + n;
-        s_o[wave][rho][c] += o_blk[vt] + s_z[wave][rho][c / kVG];
+        s_o[wave][rho][c] += fmaf(o_blk[vt], fb, s_z[wave][rho][c / kVG]);
     }
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
         if (lane == 0) {
-            s_m[wave][gq] = m[gq];
+            s_m[wave][gq] = mq[gq];
             s_l[wave][gq] = lq[gq];
         }
     __syncthreads();
