@@ -802,14 +802,14 @@ __device__ __forceinline__ void wait_vmem() {
 // Waits until the staged block with `later` staged blocks after it has landed.
 template <int NL, int NS>
 __device__ __forceinline__ void wait_staged(int later) {
-    static_assert(NS <= 3, "two later stages at most");
+    static_assert(NS >= 1 && NS <= 3, "two later stages at most");
     if (NS > 2 && later >= 2) wait_vmem<2 * NL>();
     else if (NS > 1 && later >= 1) wait_vmem<NL>();
     else wait_vmem<0>();
 }
 
 template <int D, int BITS, int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const AttendArgs a) {
     constexpr int QG = 4;
     using B = BlockRegs<D, BITS>;
     using R = GqaRegs<D, BITS>;
@@ -820,15 +820,24 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     constexpr int NACC = 2;
     constexpr int NT = 64 * NWAVES;
     __shared__ __align__(16) float s_q[QG][D];
-    __shared__ __align__(16) uint32_t s_kb[NWAVES][KC][4][16][4];  // score operands: chunk, lane group, column
-    __shared__ __align__(16) uint32_t s_va[NWAVES][NG][4][16][2];  // weight operands: group, lane group, row
+    // score operands [chunk][lane group][row][word] and weight operands
+    // [group][lane group][row][word], each lane group (or group) padded so
+    // that a wave's stores, lanes spread over chunk and row, hit distinct banks
+    constexpr int KB_Q = 16 * 4 + 4, VA_G = 4 * 16 * 2 + 2;
+    __shared__ __align__(16) uint32_t s_kb[NWAVES][KC * 4 * KB_Q];
+    __shared__ __align__(16) uint32_t s_va[NWAVES][NG * VA_G];
     __shared__ __align__(16) float s_p[NWAVES][QG][kG];            // residual weights
-    __shared__ __align__(16) float s_o[NWAVES][QG][D];
     __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
 
     const CacheGeom& g = a.g;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    auto kb_at = [&](int kc, int q, int row, int wd) -> uint32_t& {
+        return s_kb[wave][(kc * 4 + q) * KB_Q + row * 4 + wd];
+    };
+    auto va_at = [&](int gr, int q, int row, int wd) -> uint32_t& {
+        return s_va[wave][gr * VA_G + (q * 16 + row) * 2 + wd];
+    };
     // vector layout (residual): key rows of tokens tl + TL*i, column w; value channels cv0, cv0 + 1
     const int w = lane % NW, tl = lane / NW;
     const int cv0 = lane * CPV;
@@ -865,12 +874,16 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     auto vs_off = [&](int tt, int r) {
         return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
     };
-    // staged blocks: NS slots per wave (LDS for two 4-wave work-groups per CU)
-    constexpr int NS = BITS == 2 ? 3 : 2;
+    // staged blocks: NS slots per wave (LDS for three 4-wave work-groups per
+    // CU at b = 2, two at b = 4; measured on MI355X: no faster with 3 slots)
+    constexpr int NS = 2;
     constexpr int NL = L::bytes / 1024;  // staging loads per block
     static_assert(L::bytes % 1024 == 0, "a record is a whole number of 1 KB wave loads");
     __shared__ __align__(16) uint8_t s_stage[NWAVES][NS][L::bytes];
     const uint32_t stage_lds = lds_address(s_stage[wave][0]);
+    // a wave's output rows at the end, in its first slot (no staging load is in flight then)
+    auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
+    static_assert(QG * D * 4 <= L::bytes, "the output rows fit in one slot");
     auto stage = [&](int j, int k) {
         stage_record<NL>(rs, (uint32_t)j * L::bytes, stage_lds + k * L::bytes, 16u * lane);
     };
@@ -916,11 +929,11 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
     // digit columns / rows 4g + 3 stay zero
     for (int idx = lane; idx < KC * 4 * 4 * 4; idx += 64) {
         const int kc = idx / 64, q = (idx / 16) % 4, gg = (idx / 4) % 4, dw = idx % 4;
-        s_kb[wave][kc][q][4 * gg + 3][dw] = 0u;
+        kb_at(kc, q, 4 * gg + 3, dw) = 0u;
     }
     for (int idx = lane; idx < NG * 4 * 4 * 2; idx += 64) {
         const int gr = idx / 32, q = (idx / 8) % 4, gg = (idx / 2) % 4, dw = idx % 2;
-        s_va[wave][gr][q][4 * gg + 3][dw] = 0u;
+        va_at(gr, q, 4 * gg + 3, dw) = 0u;
     }
     __syncthreads();
     // per-query bounds |q| < 2^Eq; the producer's query (rho) at its channels,
@@ -1087,7 +1100,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
                 zp = fmaf(qv[kc][k], r.ksz[kc][k][1], zp);
             }
 #pragma unroll
-            for (int d = 0; d < 3; ++d) s_kb[wave][kc][n >> 2][4 * rho + d][n & 3] = bytes_d(vq[0], vq[1], vq[2], vq[3], d);
+            for (int d = 0; d < 3; ++d) kb_at(kc, n >> 2, 4 * rho + d, n & 3) = bytes_d(vq[0], vq[1], vq[2], vq[3], d);
         }
         // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
         const float zs = sum_cols<16>(zp) * scale;
@@ -1119,7 +1132,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
                     cv[2] = (int)(x1 & 0x0F0F0F0Fu);
                     cv[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
                 }
-                const uint4 bb = *reinterpret_cast<const uint4*>(&s_kb[wave][kc][rho][n][0]);
+                const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(kc, rho, n, 0));
                 qd[0] = (int)bb.x;
                 qd[1] = (int)bb.y;
                 qd[2] = (int)bb.z;
@@ -1174,7 +1187,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             }
 #pragma unroll
             for (int d = 0; d < 3; ++d)
-                s_va[wave][dq][2 * tt + gl / 2][4 * rho + d][gl % 2] = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
+                va_at(dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
         }
         wave_lds_order();
     };
@@ -1183,7 +1196,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
         const float vs = ldexpf(1.0f, ev - 22);
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt) {
-            const uint2 pa = *reinterpret_cast<const uint2*>(&s_va[wave][vt / 2][rho][n][0]);
+            const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(vt / 2, rho, n, 0));
             const uint32_t x = r.vc[vt];
             uint32_t b0, b1;
             if constexpr (BITS == 2) {
@@ -1251,13 +1264,13 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < NACC; ++e) acc += o_res[gq][k * NACC + e];
-            s_o[wave][gq][cv0 + k] = acc * fr[gq];
+            s_o(wave)[gq][cv0 + k] = acc * fr[gq];
         }
     wave_lds_order();
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
         const int c = 16 * vt + n;
-        s_o[wave][rho][c] += fmaf(o_blk[vt], fb, s_z[wave][rho][c / kVG]);
+        s_o(wave)[rho][c] += fmaf(o_blk[vt], fb, s_z[wave][rho][c / kVG]);
     }
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
@@ -1277,7 +1290,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_gqa_kernel(const AttendArg
             if (s_m[wv][gq] != -INFINITY) {
                 const float f = __builtin_amdgcn_exp2f(s_m[wv][gq] - M);
                 Lsum = fmaf(s_l[wv][gq], f, Lsum);
-                O = fmaf(s_o[wv][gq][c], f, O);
+                O = fmaf(s_o(wv)[gq][c], f, O);
             }
         }
         if (a.n_split == 1) {
