@@ -46,6 +46,10 @@ SHAPES = [
     (3, 2, 2, 128, 2, 100),
     (1, 2, 4, 256, 2, 517),
     (2, 1, 3, 64, 4, 1000),
+    # four query heads per KV head at d = 128 (the matrix-core kernel with staged blocks):
+    (1, 2, 8, 128, 4, 700),    # b = 4, ragged tail
+    (1, 1, 4, 128, 2, 2000),   # many blocks per wave: the slot ring wraps
+    (2, 1, 4, 128, 4, 330),    # fewer blocks than a wave's slots
 ]
 
 
@@ -104,9 +108,10 @@ def test_chunked_appends_and_flushes(bits):
         compare_unit(cache, oc, u, u)
 
 
-def test_split_invariance_and_determinism():
-    B, Hkv, Hq, d, bits, T = 2, 4, 8, 128, 2, 4096
-    _announce("splits")
+@pytest.mark.parametrize("Hq,bits", [(8, 2), (16, 2), (16, 4)], ids=["group2_b2", "group4_b2", "group4_b4"])
+def test_split_invariance_and_determinism(Hq, bits):
+    B, Hkv, d, T = 2, 4, 128, 4096
+    _announce("splits", Hq, bits)
     wl = KVWorkload(B, Hkv, d, seed=5)
     k, v = wl.kv(0, T)
     q = wl.q(Hq).to(DEV)
