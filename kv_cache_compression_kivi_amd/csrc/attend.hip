@@ -368,8 +368,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     for (int k = 0; k < PF - 1; ++k)
         if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
 
-    // residual chunks (fp16 rows from the ring) are computed after the blocks;
-    // a wave's first chunk is loaded now, so its latency hides behind them
+    // residual chunks (fp16 rows from the ring) are computed first, while the
+    // first blocks are in flight (memory is idle once the last block lands, so
+    // work left after it lengthens the tail); a wave's first chunk is loaded now
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
     const int slot0 = (int)(a.n_quant % g.ring_slots);
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             }
         }
     };
-    constexpr bool kEarly = D <= 128;  // d = 256: too many registers to hold a chunk across the blocks
+    constexpr bool kEarly = D <= 128;  // d = 256: a chunk and the first blocks take too many registers
     if (kEarly && ck0 < rc) load_chunk(ck0);
     if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0)
         write_new_token<D>(a, u, rbase);
@@ -584,6 +585,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             }
         wave_lds_order();
     };
+    for (int ck = ck0; ck < rc; ck += NWAVES) {
+        if (!kEarly || ck != ck0) load_chunk(ck);
+        chunk_math();
+    }
     for (int j = j0; j < j1; j += PF * NWAVES) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
@@ -592,7 +597,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             // issue priority by work left: the SIMD favours older waves, so
             // without it the younger waves of a work-group finish last
             {
-                const int left = (j1 - jj + NWAVES - 1) / NWAVES + (ck0 < rc ? 1 : 0);
+                const int left = (j1 - jj + NWAVES - 1) / NWAVES;
                 if (left >= 6) __builtin_amdgcn_s_setprio(3);
                 else if (left >= 4) __builtin_amdgcn_s_setprio(2);
                 else if (left >= 2) __builtin_amdgcn_s_setprio(1);
@@ -604,10 +609,6 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         }
     }
 
-    for (int ck = ck0; ck < rc; ck += NWAVES) {
-        if (!kEarly || ck != ck0) load_chunk(ck);
-        chunk_math();
-    }
 
     // per-wave totals: the weight sum and each group's value-zero sum over the
     // token lanes; the zero sum joins every channel of its group
