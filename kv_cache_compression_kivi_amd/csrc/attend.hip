@@ -704,11 +704,12 @@ __device__ __forceinline__ constexpr int gqa_channel(int kc, int q, int s) {
 // value word in the same way. b = 2: word q/2, bytes (w >> 2(2(q%2) + e)) ->
 // tokens 16(q/2) + 4k + 2(q%2) + e (s = 4e + k); b = 4: word q, (w >> 4e) ->
 // tokens 8q + 2k + e.
-// Score rows are assigned to tokens so that lane group rho, rows 4rho + r of a
-// 16-token tile hold exactly the tokens of bytes 4e .. 4e + 3 of one value
-// operand (q = 2 tt + rho/2, e = rho % 2): its weights then pack into one word.
+// Score columns are assigned to tokens so that the four lanes 4c .. 4c + 3 of
+// a row (columns of one quad) hold exactly the tokens of bytes 4e .. 4e + 3 of
+// one value operand (q = 2 tt + c/2, e = c % 2): their weights then pack into
+// one word.
 template <int BITS>
-__device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score row m
+__device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score column m
     if constexpr (BITS == 2) {
         return m / 4 + 4 * (m % 4);
     } else {
@@ -716,13 +717,13 @@ __device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (withi
     }
 }
 
-// Shares of a block record for one wave (loaded ahead of use).
+// One lane's shares of a block record, read from its LDS slot before the block's math.
 template <int D, int BITS>
 struct GqaRegs {
     static constexpr int KC = D / 64;  // 64-channel chunks
     static constexpr int KW = BITS / 2;
     static constexpr int VT = D / 16;  // 16-channel value tiles
-    uint32_t kc[2][KC][KW];            // key words of score row l%16 of tile tt, lane group l/16 of each chunk
+    uint32_t kc[2][KC][KW];            // key words of score column l%16 of tile tt, lane group l/16 of each chunk
     float ksz[KC][4][2];               // (s, z) of the digit producer's channels
     float2 vsz[2][4];                  // (s, z) of the tokens of columns 4((l%16)/4) + r, value group l%4
     uint32_t vc[VT];                   // value word of channel 16 vt + l%16 used by lane group l/16
@@ -866,7 +867,7 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
     // per-lane byte offsets of the block shares: a base per share plus
     // compile-time steps (which become the loads' immediate offsets)
-    const int rt = gqa_row_token<BITS>(n);       // token of score row n in its tile
+    const int rt = gqa_row_token<BITS>(n);       // token of score column n in its tile
     const int ob_kw = (rt * L::W + (BITS == 2 ? rho : 2 * rho)) * 4;
     const int ob_ks = L::ksz + gqa_channel<BITS>(0, n >> 2, 4 * (n & 3)) * 8;
     const int ob_vc = L::vcode + (n * BITS + (BITS == 2 ? rho / 2 : rho)) * 4;
