@@ -1115,12 +1115,20 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
         //    rows 4 rho .. 4 rho + 2 land in this lane's accumulators 0 .. 2
         const float ks = ldexpf(scale, eq_mine + es - 22);  // sum Q code = 2^(22 - Eq - Es) sum q s code
         float sc[2];
+        // both tiles' products interleave on the matrix core; the digit
+        // operand of a chunk serves both
+        v4i32 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            v4i32 acc = {0, 0, 0, 0};
+        for (int kc = 0; kc < KC; ++kc) {
+            const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(kc, rho, n, 0));
+            v4i32 qd;
+            qd[0] = (int)bb.x;
+            qd[1] = (int)bb.y;
+            qd[2] = (int)bb.z;
+            qd[3] = (int)bb.w;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                v4i32 cv, qd;
+            for (int tt = 0; tt < 2; ++tt) {
+                v4i32 cv;
                 if constexpr (BITS == 2) {
                     const uint32_t x = r.kc[tt][kc][0];
                     cv[0] = (int)(x & 0x03030303u);
@@ -1134,19 +1142,17 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
                     cv[2] = (int)(x1 & 0x0F0F0F0Fu);
                     cv[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
                 }
-                const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(kc, rho, n, 0));
-                qd[0] = (int)bb.x;
-                qd[1] = (int)bb.y;
-                qd[2] = (int)bb.z;
-                qd[3] = (int)bb.w;
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qd, cv, acc, 0, 0, 0);
+                acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qd, cv, acc[tt], 0, 0, 0);
             }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
             float comb;
             if constexpr (BITS == 2) {
                 // |sums| <= 128 * 3 * 128 (digits 0, 1) and 128 * 3 * 64 (digit 2): exact in int32
-                comb = (float)(acc[0] + (acc[1] << 8) + (acc[2] << 16));
+                comb = (float)(acc[tt][0] + (acc[tt][1] << 8) + (acc[tt][2] << 16));
             } else {
-                comb = fmaf((float)acc[2], 65536.0f, fmaf((float)acc[1], 256.0f, (float)acc[0]));
+                comb = fmaf((float)acc[tt][2], 65536.0f, fmaf((float)acc[tt][1], 256.0f, (float)acc[tt][0]));
             }
             sc[tt] = fmaf(comb, ks, zs);
         }
@@ -1196,30 +1202,39 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
     auto value_math = [&](const R& r, int ev) {
         const float vs = ldexpf(1.0f, ev - 22);
+        constexpr int VB = 4;  // tiles on the matrix core before their results are combined
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-            const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(vt / 2, rho, n, 0));
-            const uint32_t x = r.vc[vt];
-            uint32_t b0, b1;
-            if constexpr (BITS == 2) {
-                const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
-                b0 = (x >> sh) & 0x03030303u;
-                b1 = (x >> (sh + 2)) & 0x03030303u;
-            } else {
-                b0 = x & 0x0F0F0F0Fu;
-                b1 = (x >> 4) & 0x0F0F0F0Fu;
+        for (int v0 = 0; v0 < VT; v0 += VB) {
+            v4i32 c[VB];
+#pragma unroll
+            for (int i = 0; i < VB; ++i) {
+                const int vt = v0 + i;
+                const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(vt / 2, rho, n, 0));
+                const uint32_t x = r.vc[vt];
+                uint32_t b0, b1;
+                if constexpr (BITS == 2) {
+                    const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
+                    b0 = (x >> sh) & 0x03030303u;
+                    b1 = (x >> (sh + 2)) & 0x03030303u;
+                } else {
+                    b0 = x & 0x0F0F0F0Fu;
+                    b1 = (x >> 4) & 0x0F0F0F0Fu;
+                }
+                const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
+                const long bv = (long)(((uint64_t)b1 << 32) | b0);
+                c[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, v4i32{0, 0, 0, 0}, 0, 0, 0);
             }
-            const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
-            const long bv = (long)(((uint64_t)b1 << 32) | b0);
-            const v4i32 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, v4i32{0, 0, 0, 0}, 0, 0, 0);
             // rows 4rho + d: the three digits of query rho, channel 16vt + n
-            float comb;
-            if constexpr (BITS == 2) {
-                comb = (float)(c[0] + (c[1] << 8) + (c[2] << 16));  // |digit sums| < 2^14: no overflow
-            } else {
-                comb = fmaf((float)c[2], 65536.0f, fmaf((float)c[1], 256.0f, (float)c[0]));
+#pragma unroll
+            for (int i = 0; i < VB; ++i) {
+                float comb;
+                if constexpr (BITS == 2) {
+                    comb = (float)(c[i][0] + (c[i][1] << 8) + (c[i][2] << 16));  // |digit sums| < 2^14: no overflow
+                } else {
+                    comb = fmaf((float)c[i][2], 65536.0f, fmaf((float)c[i][1], 256.0f, (float)c[i][0]));
+                }
+                o_blk[v0 + i] = fmaf(comb, vs, o_blk[v0 + i]);
             }
-            o_blk[vt] = fmaf(comb, vs, o_blk[vt]);
         }
         wave_lds_order();
     };
