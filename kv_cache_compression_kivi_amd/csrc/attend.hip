@@ -738,13 +738,26 @@ __device__ __forceinline__ uint32_t bytes_d(uint32_t v0, uint32_t v1, uint32_t v
 
 constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kQuadBcast0 = 0x00;
 
-// The maximum over a wave (every lane holds it).
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<kSwap1>(x));
-    x = fmaxf(x, dpp<kSwap2>(x));
-    x = fmaxf(x, dpp<kHalfMirror>(x));
-    x = fmaxf(x, dpp<kMirror>(x));
-    return rows_max(x);
+// Maxima of non-negative floats taken on their bit patterns, which order
+// like unsigned integers (no NaN quieting, unlike fmaxf): over each row of 16
+// lanes, and over the wave (every lane holds the result).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t row_max_bits(uint32_t x) {
+    x = umax(x, dpp_u<kSwap1>(x));
+    x = umax(x, dpp_u<kSwap2>(x));
+    x = umax(x, dpp_u<kHalfMirror>(x));
+    return umax(x, dpp_u<kMirror>(x));
+}
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+    x = row_max_bits(x);
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = umax(r[0], r[1]);
+    auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return umax(t[0], t[1]);
 }
 
 // The 23-bit integer Q = rint(a b 2^-e) (|a b| < 2^(22+e)) as three signed
@@ -757,8 +770,13 @@ struct DigitScale {
     float magic;
     uint32_t bias;
 };
+// e must be the same in every lane. Both values stay whole scalars: folded
+// into the adds of digits3, the bias would cost a second add per value.
 __device__ __forceinline__ DigitScale digit_scale(int e) {
-    return {ldexpf(1.5f, 23 + e), 0x408080u - ((uint32_t)(e & 1) << 23)};
+    const float magic = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(ldexpf(1.5f, 23 + e))));
+    uint32_t bias = __builtin_amdgcn_readfirstlane(0x408080u - ((uint32_t)(e & 1) << 23));
+    asm("" : "+s"(bias));  // opaque: not reassociated into the adds
+    return {magic, bias};
 }
 __device__ __forceinline__ uint32_t digits3(float a, float b, DigitScale ds) {
     return (__float_as_uint(fmaf(a, b, ds.magic)) + ds.bias) ^ 0x808080u;
@@ -943,10 +961,10 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     int Eq[QG];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
-        float mx = 0.f;
+        uint32_t mx = 0;  // |q| as bit patterns
 #pragma unroll
-        for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(s_q[gq][c]));
-        Eq[gq] = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(mx)));
+        for (int c = lane; c < D; c += 64) mx = umax(mx, __float_as_uint(s_q[gq][c]) & 0x7fffffffu);
+        Eq[gq] = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(mx))));
     }
     const int eq_mine = rho == 0 ? Eq[0] : (rho == 1 ? Eq[1] : (rho == 2 ? Eq[2] : Eq[3]));
     const int eq_gl = gl == 0 ? Eq[0] : (gl == 1 ? Eq[1] : (gl == 2 ? Eq[2] : Eq[3]));
@@ -1081,16 +1099,13 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     // scores, softmax, weight digits of one block
     auto key_math = [&](const R& r, int& ev) {
         // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
-        float smax = 0.f;
+        uint32_t smax = 0;  // scales are positive: their bit patterns order like the values
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) smax = fmaxf(smax, r.ksz[kc][k][0]);
-        smax = fmaxf(smax, dpp<kSwap1>(smax));
-        smax = fmaxf(smax, dpp<kSwap2>(smax));
-        smax = fmaxf(smax, dpp<kHalfMirror>(smax));
-        smax = fmaxf(smax, dpp<kMirror>(smax));  // each row of 16 lanes covers every channel
-        const int es = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(smax));
+            for (int k = 0; k < 4; ++k) smax = umax(smax, __float_as_uint(r.ksz[kc][k][0]));
+        smax = row_max_bits(smax);  // each row of 16 lanes covers every channel
+        const int es = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(smax)));
         const DigitScale dk = digit_scale(es);
         float zp = 0.f;
 #pragma unroll
@@ -1107,9 +1122,12 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
         // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
         const float zs = sum_cols<16>(zp) * scale;
         // bound of the block's value scales, for the weight digits
-        float vmax = fmaxf(fmaxf(r.vsz[0][0].x, r.vsz[0][1].x), fmaxf(r.vsz[0][2].x, r.vsz[0][3].x));
-        vmax = fmaxf(vmax, fmaxf(fmaxf(r.vsz[1][0].x, r.vsz[1][1].x), fmaxf(r.vsz[1][2].x, r.vsz[1][3].x)));
-        ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(vmax)));
+        uint32_t vmax = 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) vmax = umax(vmax, __float_as_uint(r.vsz[tt][r2].x));
+        ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
         wave_lds_order();
         // 2. scores of query rho and token rt of each tile: the digit sums of
         //    rows 4 rho .. 4 rho + 2 land in this lane's accumulators 0 .. 2
@@ -1242,16 +1260,19 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     // consumed, and fly during its value phase
     // a block is read from its slot, the slot refilled with the block NS
     // further on, then the block's math runs from registers
-    int slot = 0;
-    for (int j = j0; j < j1; j += NWAVES) {
-        wait_staged<NL, NS>((j1 - 1 - j) / NWAVES);
-        R r;
-        read_slot(slot, r);
-        if (j + NS * NWAVES < j1) stage(j + NS * NWAVES, slot);
-        int ev;
-        key_math(r, ev);
-        value_math(r, ev);
-        slot = slot + 1 == NS ? 0 : slot + 1;
+    for (int j = j0; j < j1; j += NS * NWAVES) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {  // slot k: its address offsets are constants
+            const int jj = j + k * NWAVES;
+            if (jj >= j1) break;
+            wait_staged<NL, NS>((j1 - 1 - jj) / NWAVES);
+            R r;
+            read_slot(k, r);
+            if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
+            int ev;
+            key_math(r, ev);
+            value_math(r, ev);
+        }
     }
 
     // per-wave totals. Block part of query rho (row rho): its max m_b, weight
