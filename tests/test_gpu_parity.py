@@ -50,6 +50,7 @@ SHAPES = [
     (1, 2, 8, 128, 4, 700),    # b = 4, ragged tail
     (1, 1, 4, 128, 2, 2000),   # many blocks per wave: the slot ring wraps
     (2, 1, 4, 128, 4, 330),    # fewer blocks than a wave's slots
+    (1, 2, 16, 128, 2, 900),   # group of 8: two work-groups of four query heads per KV head
 ]
 
 
