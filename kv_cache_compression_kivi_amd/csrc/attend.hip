@@ -736,6 +736,21 @@ __device__ __forceinline__ uint32_t bytes_d(uint32_t v0, uint32_t v1, uint32_t v
     return lo | hi;
 }
 
+// The three digit words of four values: word d holds byte d of v0 .. v3
+// (byte k from v_k). Bytes 0 and 1 go through two pair words, byte 2 directly.
+__device__ __forceinline__ void digit_words(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, uint32_t (&w)[3]) {
+    constexpr uint32_t kPair = 0 | 4 << 8 | 1 << 16 | 5 << 24;  // [a.b0, b.b0, a.b1, b.b1]
+    const uint32_t p01 = __builtin_amdgcn_perm(v1, v0, kPair);
+    const uint32_t p23 = __builtin_amdgcn_perm(v3, v2, kPair);
+    w[0] = __builtin_amdgcn_perm(p23, p01, 0 | 1 << 8 | 4 << 16 | 5 << 24);
+    w[1] = __builtin_amdgcn_perm(p23, p01, 2 | 3 << 8 | 6 << 16 | 7 << 24);
+    w[2] = bytes_d(v0, v1, v2, v3, 2);
+}
+
+// d0 + 2^8 d1 + 2^16 d2 of three int32 digit sums (the matrix cores' results:
+// read them only from compiled code, which waits out the result hazard).
+__device__ __forceinline__ int digit_sum3(int d0, int d1, int d2) { return (d2 << 16) + ((d1 << 8) + d0); }
+
 constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kQuadBcast0 = 0x00;
 
 // Maxima of non-negative floats taken on their bit patterns, which order
@@ -1116,8 +1131,10 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
                 vq[k] = digits3(qn[kc][k], r.ksz[kc][k][0], dk);
                 zp = fmaf(qv[kc][k], r.ksz[kc][k][1], zp);
             }
+            uint32_t wq[3];
+            digit_words(vq[0], vq[1], vq[2], vq[3], wq);
 #pragma unroll
-            for (int d = 0; d < 3; ++d) kb_at(kc, n >> 2, 4 * rho + d, n & 3) = bytes_d(vq[0], vq[1], vq[2], vq[3], d);
+            for (int d = 0; d < 3; ++d) kb_at(kc, n >> 2, 4 * rho + d, n & 3) = wq[d];
         }
         // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
         const float zs = sum_cols<16>(zp) * scale;
@@ -1168,7 +1185,7 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
             float comb;
             if constexpr (BITS == 2) {
                 // |sums| <= 128 * 3 * 128 (digits 0, 1) and 128 * 3 * 64 (digit 2): exact in int32
-                comb = (float)(acc[tt][0] + (acc[tt][1] << 8) + (acc[tt][2] << 16));
+                comb = (float)digit_sum3(acc[tt][0], acc[tt][1], acc[tt][2]);
             } else {
                 comb = fmaf((float)acc[tt][2], 65536.0f, fmaf((float)acc[tt][1], 256.0f, (float)acc[tt][0]));
             }
@@ -1211,9 +1228,11 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
                 z_b = fmaf(pq[r2], r.vsz[tt][r2].y, z_b);
                 vp[r2] = digits3(pq[r2], r.vsz[tt][r2].x, dv);
             }
+            uint32_t wp[3];
+            digit_words(vp[0], vp[1], vp[2], vp[3], wp);
 #pragma unroll
             for (int d = 0; d < 3; ++d)
-                va_at(dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = bytes_d(vp[0], vp[1], vp[2], vp[3], d);
+                va_at(dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = wp[d];
         }
         wave_lds_order();
     };
@@ -1247,7 +1266,7 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
             for (int i = 0; i < VB; ++i) {
                 float comb;
                 if constexpr (BITS == 2) {
-                    comb = (float)(c[i][0] + (c[i][1] << 8) + (c[i][2] << 16));  // |digit sums| < 2^14: no overflow
+                    comb = (float)digit_sum3(c[i][0], c[i][1], c[i][2]);  // |digit sums| < 2^14: no overflow
                 } else {
                     comb = fmaf((float)c[i][2], 65536.0f, fmaf((float)c[i][1], 256.0f, (float)c[i][0]));
                 }
