@@ -1364,24 +1364,47 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
     }
 }
 
-// Log-sum-exp merge of the splits of one (batch row, query head), in split order.
+// Log-sum-exp merge of the splits of one (batch row, query head), in split
+// order. The splits' (m, l, o) are read 16 at a time in one round of loads
+// (a second round waiting on the first would double the kernel's latency);
+// a group's maximum rescales the sums of the groups before it.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
+    constexpr int CH = 16;
     const CacheGeom& g = a.g;
     const size_t row = blockIdx.x;
     const int c = threadIdx.x;
     const size_t stride = g.partial_stride / 4;
     const float* rb = reinterpret_cast<const float*>(g.base + g.off_partial) + row * g.max_splits * stride;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, rb[s * stride + D]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-        const float ms = rb[s * stride + D];
-        if (ms != -INFINITY) {
-            const float f = __builtin_amdgcn_exp2f(ms - M);
-            L = fmaf(rb[s * stride + D + 1], f, L);
-            O = fmaf(rb[s * stride + c], f, O);
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < a.n_split; s0 += CH) {
+        float ms[CH], ls[CH], os[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const bool in = s0 + i < a.n_split;
+            const float* r = rb + (size_t)(in ? s0 + i : s0) * stride;  // split s0 stands in past the end
+            ms[i] = r[D];
+            ls[i] = r[D + 1];
+            os[i] = r[c];
+            if (!in) ms[i] = -INFINITY;
         }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, ms[i]);
+        if (M != -INFINITY && Mc != M) {
+            const float f = __builtin_amdgcn_exp2f(M - Mc);
+            L *= f;
+            O *= f;
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            if (ms[i] != -INFINITY) {
+                const float f = __builtin_amdgcn_exp2f(ms[i] - Mc);
+                L = fmaf(ls[i], f, L);
+                O = fmaf(os[i], f, O);
+            }
+        }
+        M = Mc;
     }
     a.out[row * D + c] = O / L;
 }
