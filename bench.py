@@ -77,12 +77,16 @@ ATTEND_SOURCES = ("attend.hip", "split.hpp", "launch.hpp", "planner.hpp")
 
 
 def _kernel_source_hash():
-    """Hash of the sources the attention kernels are built from: a counter
-    summary taken before any of them changed no longer describes the kernel."""
+    """Hash of the sources the attention kernels are built from, without their
+    // comments and blank lines: a counter summary taken before any code in
+    them changed no longer describes the kernel."""
     h = hashlib.sha256()
     for name in ATTEND_SOURCES:
-        with open(os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode("utf-8") + b"\n")
     return h.hexdigest()[:16]
 
 
