@@ -56,8 +56,9 @@ struct AttendArgs {
     int32_t qg, nwaves;
     float scale_log2;  // log2(e) / sqrt(d)
     // A token appended by this call (t_new >= 0), not yet in the ring: its rows
-    // are k_new / v_new + unit * d. The work-group that owns a unit's residual
-    // writes them to the ring slot, and the attention reads them from there.
+    // are k_new / v_new + unit * d. One wave of the work-group that owns a
+    // unit's residual writes them to their ring slot for later calls; this
+    // call reads the token from those input rows, not from the ring.
     const uint16_t* k_new;
     const uint16_t* v_new;
     int64_t t_new;
