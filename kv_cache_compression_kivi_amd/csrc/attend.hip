@@ -751,7 +751,8 @@ __device__ __forceinline__ void digit_words(uint32_t v0, uint32_t v1, uint32_t v
 // read them only from compiled code, which waits out the result hazard).
 __device__ __forceinline__ int digit_sum3(int d0, int d1, int d2) { return (d2 << 16) + ((d1 << 8) + d0); }
 
-constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kQuadBcast0 = 0x00;
+// quad_perm broadcasts of lane k of each quad
+constexpr int kQuadBcast[4] = {0x00, 0x55, 0xAA, 0xFF};
 
 // Maxima of non-negative floats taken on their bit patterns, which order
 // like unsigned integers (no NaN quieting, unlike fmaxf): over each row of 16
@@ -1218,10 +1219,10 @@ __global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const Attend
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             float pq[4];
-            pq[0] = dpp<0x00>(pt[tt]);
-            pq[1] = dpp<0x55>(pt[tt]);
-            pq[2] = dpp<0xAA>(pt[tt]);
-            pq[3] = dpp<0xFF>(pt[tt]);
+            pq[0] = dpp<kQuadBcast[0]>(pt[tt]);
+            pq[1] = dpp<kQuadBcast[1]>(pt[tt]);
+            pq[2] = dpp<kQuadBcast[2]>(pt[tt]);
+            pq[3] = dpp<kQuadBcast[3]>(pt[tt]);
             uint32_t vp[4];
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) {
