@@ -73,7 +73,7 @@ def prefill_bytes(units, d, bits, T, n_quant):
 
 # ---------------------------------------------------------------- helpers
 
-ATTEND_SOURCES = ("attend.hip", "split.hpp", "launch.hpp", "planner.hpp")
+ATTEND_SOURCES = ("attend.hip", "attend_gqa.hip", "attend_common.hpp", "split.hpp", "launch.hpp", "planner.hpp")
 
 
 def _kernel_source_hash():

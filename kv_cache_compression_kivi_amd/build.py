@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkivi.so")
-SOURCES = [os.path.join(CSRC, "kivi_api.cpp"), os.path.join(CSRC, "codec.hip"), os.path.join(CSRC, "attend.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kivi_api.cpp", "codec.hip", "attend.hip", "attend_gqa.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

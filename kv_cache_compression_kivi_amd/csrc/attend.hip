@@ -1,4 +1,7 @@
-// attend.hip -- decode attention over the packed KIVI cache on gfx950.
+// attend.hip -- decode attention over the packed KIVI cache on gfx950: the
+// vector-unit kernel (one, two or four query heads per work-group), the merge
+// of the splits, and the dispatch (four query heads at d = 128 go to the
+// matrix-core kernel of attend_gqa.hip).
 //
 // The KIVI explainer page ("ICML 2024論文解説: KIVI — チューニング不要のKVキャッシュ
 // 2bit非対称量子化"), section 残差バッファ（Residual Buffer）: attention is one
@@ -37,115 +40,13 @@
 
 #include <cstdint>
 
-#include "launch.hpp"
+#include "attend_common.hpp"
 #include "split.hpp"
 
 namespace kivi {
 namespace {
 
-constexpr int kG = 32;   // tokens per key block
-constexpr int kVG = 32;  // channels per value group
-
-__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// ------------------------------------------------------------ lane reductions
-
-// Lane i reads the lane the DPP control names; a source outside the row reads 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-constexpr int kSwap1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kSwap2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kMirror = 0x140;      // row_mirror
-constexpr int kHalfMirror = 0x141;  // row_half_mirror
-constexpr int kRor4 = 0x124;        // row_ror:4
-constexpr int kRor8 = 0x128;        // row_ror:8
-
-// Sum over each aligned group of N (4, 8, 16) contiguous lanes, in every lane of the group.
-template <int N>
-__device__ __forceinline__ float sum_cols(float x) {
-    x += dpp<kSwap1>(x);
-    x += dpp<kSwap2>(x);
-    if constexpr (N >= 8) x += dpp<kHalfMirror>(x);
-    if constexpr (N >= 16) x += dpp<kMirror>(x);
-    return x;
-}
-
-// Sum / max of lane i and lanes i +- 16, i +- 32 (the same lane of the four rows).
-__device__ __forceinline__ float rows_sum(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-
-__device__ __forceinline__ float rows_max(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-
-// Sum / max over the lanes that share (lane mod NW): the token lanes of one column.
-template <int NW>
-__device__ __forceinline__ float tok_sum(float x) {
-    if constexpr (NW == 4) {
-        x += dpp<kRor4>(x);
-        x += dpp<kRor8>(x);
-    } else if constexpr (NW == 8) {
-        x += dpp<kRor8>(x);
-    }
-    return rows_sum(x);
-}
-
-template <int NW>
-__device__ __forceinline__ float tok_max(float x) {
-    if constexpr (NW == 4) {
-        x = fmaxf(x, dpp<kRor4>(x));
-        x = fmaxf(x, dpp<kRor8>(x));
-    } else if constexpr (NW == 8) {
-        x = fmaxf(x, dpp<kRor8>(x));
-    }
-    return rows_max(x);
-}
-
-__device__ __forceinline__ float wave_sum(float x) { return rows_sum(sum_cols<16>(x)); }
-
-// Orders this wave's LDS stores before its later LDS loads by other lanes
-// (and the loads before later stores); LDS executes a wave's accesses in order.
-__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
-
-// ------------------------------------------------------------ block records
-
-// Record layout of one key block (see kivi.h): kcode [G][W] (token-major),
-// vcode [D][BITS] (channel-major: a channel's 32 tokens in BITS words),
-// ksz [D][2], vsz [G][D/32][2]; known at compile time from D and BITS.
-template <int D, int BITS>
-struct Rec {
-    static constexpr int W = D * BITS / 32;
-    static constexpr int kcode = 0;
-    static constexpr int vcode = kG * W * 4;
-    static constexpr int ksz = 2 * kG * W * 4;
-    static constexpr int vsz = ksz + D * 8;
-    static constexpr int bytes = vsz + kG * (D / kVG) * 8;
-};
-
-// One lane's share of a block record, loaded ahead of its use. Key side:
-// lane = tl * NW + w holds key-code words of tokens tl + TL*i, column w. Value
-// side: lane L holds the value codes of channels L*CPV .. L*CPV + CPV - 1,
-// all 32 tokens (BITS words per channel).
-template <int D, int BITS>
-struct BlockRegs {
-    static constexpr int NW = D / 16, TL = 64 / NW, TPL = kG / TL, NWORD = BITS / 2, CPL = D / 64;
-    static constexpr int CPV = D / 64;  // value channels per lane
-    float ksz[2 * CPL];          // (s, z) of channels lane*CPL .. lane*CPL + CPL - 1
-    uint32_t kc[TPL][NWORD];     // key code words of this lane's tokens and column
-    uint32_t vc[CPV * BITS];     // value code words of this lane's channels
-    float2 vsz[TPL];             // (s, z) of each token's value group that holds column w
-};
+// ------------------------------------------------------------ block loads
 
 // A lane's byte offsets inside any record: its key-code word of token tl
 // (token tl + TL*i at i*TL*W*4 more), its value-code words, its key (s, z)
@@ -164,12 +65,6 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int w, int tl) {
     o.ksz = L::ksz + lane * 2 * B::CPL * 4;
     o.vsz = L::vsz + (tl * (D / kVG) + (w >> 1)) * 8;
     return o;
-}
-
-// The unit's records as one buffer (offsets past `bytes` read as zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t records(const uint8_t* base, uint64_t bytes) {
-    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n, 0x00020000);
 }
 
 template <int D, int BITS>
@@ -231,11 +126,6 @@ struct CodePos {
     __device__ static constexpr int jpos(int ch) { return (ch % PH) % ND; }
 };
 
-__device__ __forceinline__ float half_lo(uint32_t x) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
-}
-__device__ __forceinline__ float half_hi(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)); }
-
 // The codes of NWD packed words as exact floats, in code order: word k holds
 // codes [P k, P (k + 1)) (P = 32 / b), code P k + i at bits [b i, b i + b), and
 // cf[P k + i] = code * 2^(b * jpos(i) - 24). Key side: one token's 16 channels
@@ -295,20 +185,6 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 // waves; more buys nothing once the HBM queue is full).
 constexpr int attend_prefetch(int D, int QG) { return QG == 1 && D <= 128 ? 3 : 2; }
 
-// Copies the token appended by this call (a.t_new) of unit u into its ring
-// slot: 16 bytes per lane, key row then value row (one wave).
-template <int D>
-__device__ __forceinline__ void write_new_token(const AttendArgs& a, int64_t u, const uint8_t* rbase) {
-    constexpr int CH = D / 8;  // 16-byte chunks per fp16 row
-    const int lane = threadIdx.x & 63;
-    const int slot = (int)(a.t_new % a.g.ring_slots);
-    for (int i = lane; i < 2 * CH; i += 64) {
-        const int kv = i / CH, c = i % CH;
-        const uint4 x = reinterpret_cast<const uint4*>((kv ? a.v_new : a.k_new) + u * D)[c];
-        reinterpret_cast<uint4*>(const_cast<uint8_t*>(rbase) + (size_t)slot * 4 * D + (size_t)kv * 2 * D)[c] = x;
-    }
-}
-
 // Two lane layouts per wave. Key side: lane = tl * NW + w scores tokens
 // tl + TL*i against channels [16w, 16w + 16). Value side: lane L accumulates
 // channels [L*CPV, L*CPV + CPV) over all 32 tokens of a chunk, with the
@@ -348,7 +224,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     // this work-group's and this wave's share of the tokens (kernel arguments only)
     const int64_t nres = a.n_tokens - a.n_quant;
     const int64_t nrc = (nres + kG - 1) / kG;
-    const int64_t cost = residual_chunk_cost(BITS);
+    const int64_t cost = kResidualChunkCost;
     int64_t b0, b1;
     split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
     const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
@@ -668,703 +544,6 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     }
 }
 
-// ------------------------------------------------------------ four query heads on the matrix cores
-
-// With four query heads per KV head both contractions of a block are small
-// matrix products, and they run exactly on the int8 matrix cores:
-//   scores  S[g][t] = sum_c q~[g][c] kcode[t][c]   (q~ = q s, per block and channel)
-//   values  O[g][c] = sum_t p~[g][t] vcode[t][c]   (p~ = p s_t, per token and value group)
-// The codes are int8 operands as they are. q~ and p~ are rounded to 23-bit
-// integers against a per-block power of two (|q| < 2^Eq per query, s < 2^Es
-// and s_t < 2^Ev per block; p <= 1) and split into three signed 8-bit
-// digits, so every product and sum is exact in int32; the only rounding is
-// that of q~ and p~ to 2^-22 of their bounds. The digits of query (or weight)
-// row g sit in rows 4g .. 4g + 2 of a 16-row tile operand; row 4g + 3 is zero.
-// Scores: v_mfma_i32_16x16x64_i8, 16 rows (query, digit) x 16 tokens x 64
-// channels, so a lane's four results are the digit sums of one query and one
-// token (lane / 16 and lane % 16).
-// Values: v_mfma_i32_16x16x32_i8, 16 rows x 16 channels x the block's 32 tokens.
-// The fp16 residual runs on the vector units as in attend_kernel.
-
-typedef int v4i32 __attribute__((ext_vector_type(4)));
-
-// Channel of byte s of a score operand, for lane group q of 64-channel chunk kc:
-// masking a token's key word by (w >> b*j) & 0x0303..03 / 0x0F0F..0F gives one
-// code per byte; these formulas follow that byte order.
-template <int BITS>
-__device__ __forceinline__ constexpr int gqa_channel(int kc, int q, int s) {
-    if constexpr (BITS == 2) {
-        return 64 * kc + 16 * q + 4 * (s % 4) + s / 4;  // word 4kc + q, s = 4j + k -> channel 4k + j
-    } else {
-        return 64 * kc + 16 * q + 8 * (s / 8) + 2 * (s % 4) + (s / 4) % 2;  // words 8kc + 2q + e, s = 8e + 4j + k
-    }
-}
-
-// Token of byte s of a value operand, for lane group q: masking a channel's
-// value word in the same way. b = 2: word q/2, bytes (w >> 2(2(q%2) + e)) ->
-// tokens 16(q/2) + 4k + 2(q%2) + e (s = 4e + k); b = 4: word q, (w >> 4e) ->
-// tokens 8q + 2k + e.
-// Score columns are assigned to tokens so that the four lanes 4c .. 4c + 3 of
-// a row (columns of one quad) hold exactly the tokens of bytes 4e .. 4e + 3 of
-// one value operand (q = 2 tt + c/2, e = c % 2): their weights then pack into
-// one word.
-template <int BITS>
-__device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score column m
-    if constexpr (BITS == 2) {
-        return m / 4 + 4 * (m % 4);
-    } else {
-        return 8 * ((m / 4) / 2) + (m / 4) % 2 + 2 * (m % 4);
-    }
-}
-
-// One lane's shares of a block record, read from its LDS slot before the block's math.
-template <int D, int BITS>
-struct GqaRegs {
-    static constexpr int KC = D / 64;  // 64-channel chunks
-    static constexpr int KW = BITS / 2;
-    static constexpr int VT = D / 16;  // 16-channel value tiles
-    uint32_t kc[2][KC][KW];            // key words of score column l%16 of tile tt, lane group l/16 of each chunk
-    float ksz[KC][4][2];               // (s, z) of the digit producer's channels
-    float2 vsz[2][4];                  // (s, z) of the tokens of columns 4((l%16)/4) + r, value group l%4
-    uint32_t vc[VT];                   // value word of channel 16 vt + l%16 used by lane group l/16
-};
-
-// Bytes d of four words, as one word (byte k from word k).
-__device__ __forceinline__ uint32_t bytes_d(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int d) {
-    const uint32_t lo = __builtin_amdgcn_perm(v1, v0, (uint32_t)(d | (4 + d) << 8 | 0x0c << 16 | 0x0c << 24));
-    const uint32_t hi = __builtin_amdgcn_perm(v3, v2, (uint32_t)(0x0c | 0x0c << 8 | d << 16 | (4 + d) << 24));
-    return lo | hi;
-}
-
-// The three digit words of four values: word d holds byte d of v0 .. v3
-// (byte k from v_k). Bytes 0 and 1 go through two pair words, byte 2 directly.
-__device__ __forceinline__ void digit_words(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, uint32_t (&w)[3]) {
-    constexpr uint32_t kPair = 0 | 4 << 8 | 1 << 16 | 5 << 24;  // [a.b0, b.b0, a.b1, b.b1]
-    const uint32_t p01 = __builtin_amdgcn_perm(v1, v0, kPair);
-    const uint32_t p23 = __builtin_amdgcn_perm(v3, v2, kPair);
-    w[0] = __builtin_amdgcn_perm(p23, p01, 0 | 1 << 8 | 4 << 16 | 5 << 24);
-    w[1] = __builtin_amdgcn_perm(p23, p01, 2 | 3 << 8 | 6 << 16 | 7 << 24);
-    w[2] = bytes_d(v0, v1, v2, v3, 2);
-}
-
-// d0 + 2^8 d1 + 2^16 d2 of three int32 digit sums (the matrix cores' results:
-// read them only from compiled code, which waits out the result hazard).
-__device__ __forceinline__ int digit_sum3(int d0, int d1, int d2) { return (d2 << 16) + ((d1 << 8) + d0); }
-
-// quad_perm broadcasts of lane k of each quad
-constexpr int kQuadBcast[4] = {0x00, 0x55, 0xAA, 0xFF};
-
-// Maxima of non-negative floats taken on their bit patterns, which order
-// like unsigned integers (no NaN quieting, unlike fmaxf): over each row of 16
-// lanes, and over the wave (every lane holds the result).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
-}
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint32_t row_max_bits(uint32_t x) {
-    x = umax(x, dpp_u<kSwap1>(x));
-    x = umax(x, dpp_u<kSwap2>(x));
-    x = umax(x, dpp_u<kHalfMirror>(x));
-    return umax(x, dpp_u<kMirror>(x));
-}
-__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
-    x = row_max_bits(x);
-    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = umax(r[0], r[1]);
-    auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return umax(t[0], t[1]);
-}
-
-// The 23-bit integer Q = rint(a b 2^-e) (|a b| < 2^(22+e)) as three signed
-// bytes, (Q + 0x808080) ^ 0x808080 in bits 0..23. One fma with the magic
-// 1.5 2^(23+e) rounds the exact product to a multiple of 2^e (ties to even),
-// so the low 24 bits of the result's encoding hold (e & 1) << 23 (the
-// exponent's low bit, as 150 + e has the parity of e) above 2^22 + Q; the
-// bias 0x408080 - ((e & 1) << 23) turns them into Q + 0x808080.
-struct DigitScale {
-    float magic;
-    uint32_t bias;
-};
-// e must be the same in every lane. Both values stay whole scalars: folded
-// into the adds of digits3, the bias would cost a second add per value.
-__device__ __forceinline__ DigitScale digit_scale(int e) {
-    const float magic = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(ldexpf(1.5f, 23 + e))));
-    uint32_t bias = __builtin_amdgcn_readfirstlane(0x408080u - ((uint32_t)(e & 1) << 23));
-    asm("" : "+s"(bias));  // opaque: not reassociated into the adds
-    return {magic, bias};
-}
-__device__ __forceinline__ uint32_t digits3(float a, float b, DigitScale ds) {
-    return (__float_as_uint(fmaf(a, b, ds.magic)) + ds.bias) ^ 0x808080u;
-}
-
-// Staging of the four-query kernel's blocks: each wave streams its next
-// blocks from HBM straight into a ring of LDS slots (buffer loads with the LDS
-// bit, a record copied as it is, 16 bytes per lane per load), so the blocks in
-// flight hold no registers. The loads are asm, so the compiler tracks none of
-// them: each slot is read after an explicit s_waitcnt vmcnt(N), N the staging
-// loads issued after it (vector-memory loads retire in order; loads the
-// compiler issues later only make the wait stricter), and a slot is refilled
-// after an s_waitcnt lgkmcnt(0), once its reads have returned. M0 holds the
-// LDS destination of each load (one SALU write and a wait state before it);
-// nothing else in this kernel keeps a value in M0.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-__device__ __forceinline__ uint32_t lds_address(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-template <int NL>
-__device__ __forceinline__ void stage_record(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint32_t slot, uint32_t voff) {
-    const int so = __builtin_amdgcn_readfirstlane((int)soff);
-    const uint32_t m = __builtin_amdgcn_readfirstlane(slot);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int c = 0; c < NL; ++c)
-        asm volatile(
-            "s_mov_b32 m0, %[m]\n\t"
-            "s_nop 0\n\t"
-            "buffer_load_dwordx4 %[v], %[rs], %[so] offen nt lds"
-            :
-            : [m] "s"(m + 1024u * c), [v] "v"(voff + 1024u * c), [rs] "s"(rs), [so] "s"(so)
-            : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    asm volatile("s_waitcnt vmcnt(%[n])" : : [n] "i"(N) : "memory");
-}
-
-// Waits until the staged block with `later` staged blocks after it has landed.
-template <int NL, int NS>
-__device__ __forceinline__ void wait_staged(int later) {
-    static_assert(NS >= 1 && NS <= 3, "two later stages at most");
-    if (NS > 2 && later >= 2) wait_vmem<2 * NL>();
-    else if (NS > 1 && later >= 1) wait_vmem<NL>();
-    else wait_vmem<0>();
-}
-
-template <int D, int BITS, int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES, 3) void attend_gqa_kernel(const AttendArgs a) {
-    constexpr int QG = 4;
-    using B = BlockRegs<D, BITS>;
-    using R = GqaRegs<D, BITS>;
-    using L = Rec<D, BITS>;
-    constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPV = B::CPV, KC = R::KC, VT = R::VT;
-    constexpr int NG = D / kVG;
-    static_assert(NG == 4 && CPV == 2, "the four lanes of a quad take the four value groups");
-    constexpr int NACC = 2;
-    constexpr int NT = 64 * NWAVES;
-    __shared__ __align__(16) float s_q[QG][D];
-    // score operands [chunk][lane group][row][word] and weight operands
-    // [group][lane group][row][word], each lane group (or group) padded so
-    // that a wave's stores, lanes spread over chunk and row, hit distinct banks
-    constexpr int KB_Q = 16 * 4 + 4, VA_G = 4 * 16 * 2 + 2;
-    __shared__ __align__(16) uint32_t s_kb[NWAVES][KC * 4 * KB_Q];
-    __shared__ __align__(16) uint32_t s_va[NWAVES][NG * VA_G];
-    __shared__ __align__(16) float s_p[NWAVES][QG][kG];            // residual weights
-    __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
-
-    const CacheGeom& g = a.g;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    auto kb_at = [&](int kc, int q, int row, int wd) -> uint32_t& {
-        return s_kb[wave][(kc * 4 + q) * KB_Q + row * 4 + wd];
-    };
-    auto va_at = [&](int gr, int q, int row, int wd) -> uint32_t& {
-        return s_va[wave][gr * VA_G + (q * 16 + row) * 2 + wd];
-    };
-    // vector layout (residual): key rows of tokens tl + TL*i, column w; value channels cv0, cv0 + 1
-    const int w = lane % NW, tl = lane / NW;
-    const int cv0 = lane * CPV;
-    // matrix layout: n = column (scores) / row (values) / channel in a tile, rho = lane group
-    const int n = lane & 15, rho = lane >> 4;
-    const int gl = n >> 2, dq = n & 3;  // the query of score columns 4gl .. 4gl+3, and a value group
-    const int split = blockIdx.x;
-    const int64_t u = blockIdx.y;
-    const int group = g.n_q_heads / g.n_kv_heads;
-    const int64_t b = u / g.n_kv_heads;
-    const int h = (int)(u % g.n_kv_heads);
-    const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)blockIdx.z * QG;
-    const float scale = a.scale_log2;
-
-    const int64_t nres = a.n_tokens - a.n_quant;
-    const int64_t nrc = (nres + kG - 1) / kG;
-    const int64_t cost = residual_chunk_cost(BITS);
-    int64_t b0, b1;
-    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
-    const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
-    const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
-    const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
-
-    const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
-    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
-    // per-lane byte offsets of the block shares: a base per share plus
-    // compile-time steps (which become the loads' immediate offsets)
-    const int rt = gqa_row_token<BITS>(n);       // token of score column n in its tile
-    const int ob_kw = (rt * L::W + (BITS == 2 ? rho : 2 * rho)) * 4;
-    const int ob_ks = L::ksz + gqa_channel<BITS>(0, n >> 2, 4 * (n & 3)) * 8;
-    const int ob_vc = L::vcode + (n * BITS + (BITS == 2 ? rho / 2 : rho)) * 4;
-    auto kw_off = [&](int tt, int kc) { return ob_kw + (16 * tt * L::W + (BITS == 2 ? 4 : 8) * kc) * 4; };
-    auto ks_off = [&](int kc, int k) { return ob_ks + gqa_channel<BITS>(kc, 0, k) * 8; };
-    auto vs_off = [&](int tt, int r) {
-        return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
-    };
-    // staged blocks: NS slots per wave (LDS for three 4-wave work-groups per
-    // CU at b = 2, two at b = 4; measured on MI355X: no faster with 3 slots)
-    constexpr int NS = 2;
-    constexpr int NL = L::bytes / 1024;  // staging loads per block
-    static_assert(L::bytes % 1024 == 0, "a record is a whole number of 1 KB wave loads");
-    __shared__ __align__(16) uint8_t s_stage[NWAVES][NS][L::bytes];
-    const uint32_t stage_lds = lds_address(s_stage[wave][0]);
-    // a wave's output rows at the end, in its first slot (no staging load is in flight then)
-    auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
-    static_assert(QG * D * 4 <= L::bytes, "the output rows fit in one slot");
-    auto stage = [&](int j, int k) {
-        stage_record<NL>(rs, (uint32_t)j * L::bytes, stage_lds + k * L::bytes, 16u * lane);
-    };
-    // this lane's shares of a staged block
-    auto read_slot = [&](int k, R& r) {
-        const uint8_t* sb = s_stage[wave][k];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                if constexpr (BITS == 2) {
-                    r.kc[tt][kc][0] = *reinterpret_cast<const uint32_t*>(sb + kw_off(tt, kc));
-                } else {
-                    const uint2 x = *reinterpret_cast<const uint2*>(sb + kw_off(tt, kc));
-                    r.kc[tt][kc][0] = x.x;
-                    r.kc[tt][kc][1] = x.y;
-                }
-            }
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                const float2 x = *reinterpret_cast<const float2*>(sb + ks_off(kc, k2));
-                r.ksz[kc][k2][0] = x.x;
-                r.ksz[kc][k2][1] = x.y;
-            }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) r.vsz[tt][rr] = *reinterpret_cast<const float2*>(sb + vs_off(tt, rr));
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) r.vc[vt] = *reinterpret_cast<const uint32_t*>(sb + ob_vc + 16 * vt * BITS * 4);
-    };
-    // the first blocks go in flight before anything waits
-#pragma unroll
-    for (int k = 0; k < NS; ++k)
-        if (j0 + k * NWAVES < j1) stage(j0 + k * NWAVES, k);
-
-    for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
-        const uint16_t v = a.q[row0 * D + idx];
-        s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
-    }
-    // digit columns / rows 4g + 3 stay zero
-    for (int idx = lane; idx < KC * 4 * 4 * 4; idx += 64) {
-        const int kc = idx / 64, q = (idx / 16) % 4, gg = (idx / 4) % 4, dw = idx % 4;
-        kb_at(kc, q, 4 * gg + 3, dw) = 0u;
-    }
-    for (int idx = lane; idx < NG * 4 * 4 * 2; idx += 64) {
-        const int gr = idx / 32, q = (idx / 8) % 4, gg = (idx / 2) % 4, dw = idx % 2;
-        va_at(gr, q, 4 * gg + 3, dw) = 0u;
-    }
-    __syncthreads();
-    // per-query bounds |q| < 2^Eq; the producer's query (rho) at its channels,
-    // scaled to 2^22 of the bound (digits) and as it is (key zeros)
-    int Eq[QG];
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-        uint32_t mx = 0;  // |q| as bit patterns
-#pragma unroll
-        for (int c = lane; c < D; c += 64) mx = umax(mx, __float_as_uint(s_q[gq][c]) & 0x7fffffffu);
-        Eq[gq] = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(mx))));
-    }
-    const int eq_mine = rho == 0 ? Eq[0] : (rho == 1 ? Eq[1] : (rho == 2 ? Eq[2] : Eq[3]));
-    const int eq_gl = gl == 0 ? Eq[0] : (gl == 1 ? Eq[1] : (gl == 2 ? Eq[2] : Eq[3]));
-    float qn[KC][4], qv[KC][4];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float x = s_q[rho][gqa_channel<BITS>(kc, n >> 2, 4 * (n & 3) + k)];
-            qn[kc][k] = ldexpf(x, 22 - eq_mine);
-            qv[kc][k] = x;
-        }
-
-    // running state, two parts merged at the end. Residual (vector layout): m,
-    // l_res and o_res per query. Blocks (matrix layout, query rho = lane / 16):
-    // running max m_b, weight sum l_b of this lane's tokens, value-zero sum z_b
-    // of group dq over the tokens of quad gl, o_blk[vt] for channel 16vt + n.
-    float m[QG], l_res[QG], o_res[QG][CPV * NACC], o_blk[VT];
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-        m[gq] = -INFINITY;
-        l_res[gq] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] = 0.f;
-    }
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) o_blk[vt] = 0.f;
-    float m_b = -INFINITY, l_b = 0.f, z_b = 0.f;
-    // multiply the residual accumulators of query gq by alpha (a new running maximum)
-    auto rescale = [&](int gq, float alpha) {
-        l_res[gq] *= alpha;
-#pragma unroll
-        for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] *= alpha;
-    };
-
-    // residual chunks (vector units, as in attend_kernel)
-    const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
-    const int ring = (int)g.ring_slots;
-    const int slot0 = (int)(a.n_quant % g.ring_slots);
-    if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0) write_new_token<D>(a, u, rbase);
-    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
-        uint4 kraw[TPL][2];
-        bool valid[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int idx = ck * kG + tl + TL * i;
-            valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);
-            slot -= slot >= ring ? ring : 0;
-            const uint4* kp = a.n_quant + idx == a.t_new
-                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
-                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
-        }
-        uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
-#pragma unroll
-        for (int t = 0; t < kG; ++t) {
-            const int idx = ck * kG + t;
-            int slot = slot0 + (idx < (int)nres ? idx : 0);
-            slot -= slot >= ring ? ring : 0;
-            vr[t] = a.n_quant + idx == a.t_new
-                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
-                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
-        }
-        float sc[QG][TPL];
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float qq[16];
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][16 * w + 4 * c4]);
-                qq[4 * c4] = x.x;
-                qq[4 * c4 + 1] = x.y;
-                qq[4 * c4 + 2] = x.z;
-                qq[4 * c4 + 3] = x.w;
-            }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const uint16_t* kh = reinterpret_cast<const uint16_t*>(kraw[i]);
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc = fmaf(qq[c], h2f(kh[c]), acc);
-                acc = sum_cols<NW>(acc) * scale;
-                sc[gq][i] = valid[i] ? acc : -INFINITY;
-            }
-        }
-        float p[QG][TPL];
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float bm = sc[gq][0];
-#pragma unroll
-            for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sc[gq][i]);
-            bm = tok_max<NW>(bm);
-            if (bm > m[gq]) {
-                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bm));
-                m[gq] = bm;
-            }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                p[gq][i] = valid[i] ? __builtin_amdgcn_exp2f(sc[gq][i] - m[gq]) : 0.f;
-                l_res[gq] += p[gq][i];
-            }
-        }
-        if (w == 0) {
-#pragma unroll
-            for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) s_p[wave][gq][tl + TL * i] = p[gq][i];
-        }
-        wave_lds_order();
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float pv[kG];
-#pragma unroll
-            for (int t4 = 0; t4 < kG / 4; ++t4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][4 * t4]);
-                pv[4 * t4] = x.x;
-                pv[4 * t4 + 1] = x.y;
-                pv[4 * t4 + 2] = x.z;
-                pv[4 * t4 + 3] = x.w;
-            }
-#pragma unroll
-            for (int t = 0; t < kG; ++t) {
-                o_res[gq][t % NACC] = fmaf(pv[t], half_lo(vr[t]), o_res[gq][t % NACC]);
-                o_res[gq][NACC + t % NACC] = fmaf(pv[t], half_hi(vr[t]), o_res[gq][NACC + t % NACC]);
-            }
-        }
-        wave_lds_order();
-    }
-
-    // scores, softmax, weight digits of one block
-    auto key_math = [&](const R& r, int& ev) {
-        // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
-        uint32_t smax = 0;  // scales are positive: their bit patterns order like the values
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) smax = umax(smax, __float_as_uint(r.ksz[kc][k][0]));
-        smax = row_max_bits(smax);  // each row of 16 lanes covers every channel
-        const int es = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(smax)));
-        const DigitScale dk = digit_scale(es);
-        float zp = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            uint32_t vq[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vq[k] = digits3(qn[kc][k], r.ksz[kc][k][0], dk);
-                zp = fmaf(qv[kc][k], r.ksz[kc][k][1], zp);
-            }
-            uint32_t wq[3];
-            digit_words(vq[0], vq[1], vq[2], vq[3], wq);
-#pragma unroll
-            for (int d = 0; d < 3; ++d) kb_at(kc, n >> 2, 4 * rho + d, n & 3) = wq[d];
-        }
-        // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
-        const float zs = sum_cols<16>(zp) * scale;
-        // bound of the block's value scales, for the weight digits
-        uint32_t vmax = 0;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) vmax = umax(vmax, __float_as_uint(r.vsz[tt][r2].x));
-        ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
-        wave_lds_order();
-        // 2. scores of query rho and token rt of each tile: the digit sums of
-        //    rows 4 rho .. 4 rho + 2 land in this lane's accumulators 0 .. 2
-        const float ks = ldexpf(scale, eq_mine + es - 22);  // sum Q code = 2^(22 - Eq - Es) sum q s code
-        float sc[2];
-        // both tiles' products interleave on the matrix core; the digit
-        // operand of a chunk serves both
-        v4i32 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(kc, rho, n, 0));
-            v4i32 qd;
-            qd[0] = (int)bb.x;
-            qd[1] = (int)bb.y;
-            qd[2] = (int)bb.z;
-            qd[3] = (int)bb.w;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                v4i32 cv;
-                if constexpr (BITS == 2) {
-                    const uint32_t x = r.kc[tt][kc][0];
-                    cv[0] = (int)(x & 0x03030303u);
-                    cv[1] = (int)((x >> 2) & 0x03030303u);
-                    cv[2] = (int)((x >> 4) & 0x03030303u);
-                    cv[3] = (int)((x >> 6) & 0x03030303u);
-                } else {
-                    const uint32_t x0 = r.kc[tt][kc][0], x1 = r.kc[tt][kc][1];
-                    cv[0] = (int)(x0 & 0x0F0F0F0Fu);
-                    cv[1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
-                    cv[2] = (int)(x1 & 0x0F0F0F0Fu);
-                    cv[3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
-                }
-                acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qd, cv, acc[tt], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            float comb;
-            if constexpr (BITS == 2) {
-                // |sums| <= 128 * 3 * 128 (digits 0, 1) and 128 * 3 * 64 (digit 2): exact in int32
-                comb = (float)digit_sum3(acc[tt][0], acc[tt][1], acc[tt][2]);
-            } else {
-                comb = fmaf((float)acc[tt][2], 65536.0f, fmaf((float)acc[tt][1], 256.0f, (float)acc[tt][0]));
-            }
-            sc[tt] = fmaf(comb, ks, zs);
-        }
-        // 3. online softmax of query rho over the row's 32 tokens
-        float bm = fmaxf(sc[0], sc[1]);
-        bm = fmaxf(bm, dpp<kSwap1>(bm));
-        bm = fmaxf(bm, dpp<kSwap2>(bm));
-        bm = fmaxf(bm, dpp<kHalfMirror>(bm));
-        bm = fmaxf(bm, dpp<kMirror>(bm));
-        if (bm > m_b) {
-            const float alpha = __builtin_amdgcn_exp2f(m_b - bm);
-            l_b *= alpha;
-            z_b *= alpha;
-#pragma unroll
-            for (int vt = 0; vt < VT; ++vt) o_blk[vt] *= alpha;
-            m_b = bm;
-        }
-        float pt[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            pt[tt] = __builtin_amdgcn_exp2f(sc[tt] - m_b);
-            l_b += pt[tt];
-        }
-        const DigitScale dv = digit_scale(ev - 22);
-        // 4. weights p s_t of value group dq for the tokens of quad gl (gathered
-        //    from its four lanes), as digits: rows 4 rho + d of the value operand,
-        //    one word per tile (lane group 2tt + gl/2, word gl%2)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            float pq[4];
-            pq[0] = dpp<kQuadBcast[0]>(pt[tt]);
-            pq[1] = dpp<kQuadBcast[1]>(pt[tt]);
-            pq[2] = dpp<kQuadBcast[2]>(pt[tt]);
-            pq[3] = dpp<kQuadBcast[3]>(pt[tt]);
-            uint32_t vp[4];
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) {
-                z_b = fmaf(pq[r2], r.vsz[tt][r2].y, z_b);
-                vp[r2] = digits3(pq[r2], r.vsz[tt][r2].x, dv);
-            }
-            uint32_t wp[3];
-            digit_words(vp[0], vp[1], vp[2], vp[3], wp);
-#pragma unroll
-            for (int d = 0; d < 3; ++d)
-                va_at(dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = wp[d];
-        }
-        wave_lds_order();
-    };
-    // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
-    auto value_math = [&](const R& r, int ev) {
-        const float vs = ldexpf(1.0f, ev - 22);
-        constexpr int VB = 4;  // tiles on the matrix core before their results are combined
-#pragma unroll
-        for (int v0 = 0; v0 < VT; v0 += VB) {
-            v4i32 c[VB];
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                const int vt = v0 + i;
-                const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(vt / 2, rho, n, 0));
-                const uint32_t x = r.vc[vt];
-                uint32_t b0, b1;
-                if constexpr (BITS == 2) {
-                    const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
-                    b0 = (x >> sh) & 0x03030303u;
-                    b1 = (x >> (sh + 2)) & 0x03030303u;
-                } else {
-                    b0 = x & 0x0F0F0F0Fu;
-                    b1 = (x >> 4) & 0x0F0F0F0Fu;
-                }
-                const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
-                const long bv = (long)(((uint64_t)b1 << 32) | b0);
-                c[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, v4i32{0, 0, 0, 0}, 0, 0, 0);
-            }
-            // rows 4rho + d: the three digits of query rho, channel 16vt + n
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                float comb;
-                if constexpr (BITS == 2) {
-                    comb = (float)digit_sum3(c[i][0], c[i][1], c[i][2]);  // |digit sums| < 2^14: no overflow
-                } else {
-                    comb = fmaf((float)c[i][2], 65536.0f, fmaf((float)c[i][1], 256.0f, (float)c[i][0]));
-                }
-                o_blk[v0 + i] = fmaf(comb, vs, o_blk[v0 + i]);
-            }
-        }
-        wave_lds_order();
-    };
-    // the next block's loads go out once the current block's key shares are
-    // consumed, and fly during its value phase
-    // a block is read from its slot, the slot refilled with the block NS
-    // further on, then the block's math runs from registers
-    for (int j = j0; j < j1; j += NS * NWAVES) {
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {  // slot k: its address offsets are constants
-            const int jj = j + k * NWAVES;
-            if (jj >= j1) break;
-            wait_staged<NL, NS>((j1 - 1 - jj) / NWAVES);
-            R r;
-            read_slot(k, r);
-            if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
-            int ev;
-            key_math(r, ev);
-            value_math(r, ev);
-        }
-    }
-
-    // per-wave totals. Block part of query rho (row rho): its max m_b, weight
-    // sum, value-zero sums of group dq; residual part per query: m, l_res, o_res
-    const float lb = sum_cols<16>(l_b);
-    float zb = z_b + dpp<kRor4>(z_b);
-    zb += dpp<kRor8>(zb);  // over the quads of the row: (query rho, group dq)
-    const float mr = rho == 0 ? m[0] : (rho == 1 ? m[1] : (rho == 2 ? m[2] : m[3]));
-    const float mt = fmaxf(mr, m_b);  // this wave's max of query rho
-    const float fb = m_b == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - mt);
-    float mq[QG], fr[QG];
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-        mq[gq] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mt), 16 * gq));
-        fr[gq] = m[gq] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gq] - mq[gq]);
-    }
-    float lq[QG];
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-        lq[gq] = tok_sum<NW>(l_res[gq]) * fr[gq] +
-                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lb * fb), 16 * gq));
-    if (gl == 0) s_z[wave][rho][dq] = zb * fb;
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-        for (int k = 0; k < CPV; ++k) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < NACC; ++e) acc += o_res[gq][k * NACC + e];
-            s_o(wave)[gq][cv0 + k] = acc * fr[gq];
-        }
-    wave_lds_order();
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-        const int c = 16 * vt + n;
-        s_o(wave)[rho][c] += fmaf(o_blk[vt], fb, s_z[wave][rho][c / kVG]);
-    }
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-        if (lane == 0) {
-            s_m[wave][gq] = mq[gq];
-            s_l[wave][gq] = lq[gq];
-        }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
-        const int gq = idx / D, c = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int wv = 0; wv < NWAVES; ++wv) M = fmaxf(M, s_m[wv][gq]);
-        float Lsum = 0.f, O = 0.f;
-#pragma unroll
-        for (int wv = 0; wv < NWAVES; ++wv) {
-            if (s_m[wv][gq] != -INFINITY) {
-                const float f = __builtin_amdgcn_exp2f(s_m[wv][gq] - M);
-                Lsum = fmaf(s_l[wv][gq], f, Lsum);
-                O = fmaf(s_o(wv)[gq][c], f, O);
-            }
-        }
-        if (a.n_split == 1) {
-            a.out[(row0 + gq) * D + c] = O / Lsum;
-        } else {
-            float* rec = reinterpret_cast<float*>(g.base + g.off_partial +
-                                                  ((row0 + gq) * g.max_splits + split) * g.partial_stride);
-            rec[c] = O;
-            if (c == 0) {
-                rec[D] = M;
-                rec[D + 1] = Lsum;
-            }
-        }
-    }
-}
-
 // Log-sum-exp merge of the splits of one (batch row, query head), in split
 // order. The splits' (m, l, o) are read 16 at a time in one round of loads
 // (a second round waiting on the first would double the kernel's latency);
@@ -1410,26 +589,20 @@ __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
     a.out[row * D + c] = O / L;
 }
 
-template <int D, int BITS, int QG, int NWAVES>
-hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
-    const int group = a.g.n_q_heads / a.g.n_kv_heads;
-    const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / QG));
-    attend_kernel<D, BITS, QG, NWAVES><<<grid, 64 * NWAVES, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
+// Merges the splits after an attention kernel wrote them (n_split > 1).
+template <int D>
+hipError_t merge_splits(hipError_t e, const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess || a.n_split == 1) return e;
     combine_kernel<D><<<(unsigned)((int64_t)a.g.batch * a.g.n_q_heads), D, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int D, int BITS, int NWAVES>
-hipError_t attend_gqa_launch(const AttendArgs& a, hipStream_t s) {
+template <int D, int BITS, int QG, int NWAVES>
+hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     const int group = a.g.n_q_heads / a.g.n_kv_heads;
-    const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / 4));
-    attend_gqa_kernel<D, BITS, NWAVES><<<grid, 64 * NWAVES, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_split == 1) return e;
-    combine_kernel<D><<<(unsigned)((int64_t)a.g.batch * a.g.n_q_heads), D, 0, s>>>(a);
-    return hipGetLastError();
+    const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / QG));
+    attend_kernel<D, BITS, QG, NWAVES><<<grid, 64 * NWAVES, 0, s>>>(a);
+    return merge_splits<D>(hipGetLastError(), a, s);
 }
 
 template <int D, int BITS>
@@ -1437,7 +610,7 @@ hipError_t attend_db(const AttendArgs& a, hipStream_t s) {
     // the host plans (qg, nwaves) with the same attend_waves()
     switch (a.qg) {
         case 4:
-            if constexpr (D == 128) return attend_gqa_launch<D, BITS, attend_waves(4, D)>(a, s);
+            if constexpr (D == 128) return merge_splits<D>(launch_attend_gqa(a, s), a, s);
             else return attend_launch<D, BITS, 4, attend_waves(4, D)>(a, s);
         case 2: return attend_launch<D, BITS, 2, attend_waves(2, D)>(a, s);
         default: return attend_launch<D, BITS, 1, attend_waves(1, D)>(a, s);

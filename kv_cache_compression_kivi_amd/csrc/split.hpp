@@ -19,8 +19,9 @@ namespace kivi {
 
 // Cost of one residual chunk, in key blocks: a chunk of 32 fp16 tokens moves
 // 16 KB (four 2-bit blocks at d = 128) but runs no decoding; measured on
-// MI355X it takes about as long as 1.5 packed blocks.
-KIVI_HD inline int64_t residual_chunk_cost(int bits) { return bits == 2 ? 2 : 2; }
+// MI355X it takes about as long as 1.5 packed blocks at b = 2 or b = 4, and
+// costs are whole blocks.
+constexpr int64_t kResidualChunkCost = 2;
 
 // Key blocks [*b0, *b1) of split s (of n) for a unit with nb key blocks and
 // nrc residual chunks; the last split (which also owns the residual) ends at nb.
