@@ -390,6 +390,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(att_bytes_avg),
             "avg_launch_us": round(att_avg_ms * 1e3, 3),
+            "timed_launches": n_att,
         },
         "cpu_baseline": None,
     }
