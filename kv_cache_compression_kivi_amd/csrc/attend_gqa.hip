@@ -17,7 +17,8 @@
 // and s_t < 2^Ev per block; p <= 1) and split into three signed 8-bit
 // digits, so every product and sum is exact in int32; the only rounding is
 // that of q~ and p~ to 2^-22 of their bounds. The digits of query (or weight)
-// row g sit in rows 4g .. 4g + 2 of a 16-row tile operand; row 4g + 3 is zero.
+// row g sit in rows 4g .. 4g + 2 of a 16-row tile operand; row 4g + 3 is never
+// written: its products land in result row 4g + 3, which is never read.
 // Scores: v_mfma_i32_16x16x64_i8, 16 rows (query, digit) x 16 tokens x 64
 // channels, so a lane's four results are the digit sums of one query and one
 // token (lane / 16 and lane % 16).
@@ -205,24 +206,12 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     constexpr int NACC = 2;
     constexpr int NT = 64 * NWAVES;
     __shared__ __align__(16) float s_q[QG][D];
-    // score operands [chunk][lane group][row][word] and weight operands
-    // [group][lane group][row][word], each lane group (or group) padded so
-    // that a wave's stores, lanes spread over chunk and row, hit distinct banks
-    constexpr int KB_Q = 16 * 4 + 4, VA_G = 4 * 16 * 2 + 2;
-    __shared__ __align__(16) uint32_t s_kb[NWAVES][KC * 4 * KB_Q];
-    __shared__ __align__(16) uint32_t s_va[NWAVES][NG * VA_G];
-    __shared__ __align__(16) float s_p[NWAVES][QG][kG];            // residual weights
+    __shared__ __align__(16) float s_p[NWAVES][QG][kG];  // residual weights
     __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
 
     const CacheGeom& g = a.g;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    auto kb_at = [&](int kc, int q, int row, int wd) -> uint32_t& {
-        return s_kb[wave][(kc * 4 + q) * KB_Q + row * 4 + wd];
-    };
-    auto va_at = [&](int gr, int q, int row, int wd) -> uint32_t& {
-        return s_va[wave][gr * VA_G + (q * 16 + row) * 2 + wd];
-    };
     // vector layout (residual): key rows of tokens tl + TL*i, column w; value channels cv0, cv0 + 1
     const int w = lane % NW, tl = lane / NW;
     const int cv0 = lane * CPV;
@@ -260,12 +249,26 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
         return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
     };
     // staged blocks: NS slots per wave (LDS for three 4-wave work-groups per
-    // CU at b = 2, two at b = 4; measured on MI355X: no faster with 3 slots)
-    constexpr int NS = 2;
+    // CU at b = 2, two at b = 4)
+    constexpr int NS = 3;
     constexpr int NL = L::bytes / 1024;  // staging loads per block
     static_assert(L::bytes % 1024 == 0, "a record is a whole number of 1 KB wave loads");
     __shared__ __align__(16) uint8_t s_stage[NWAVES][NS][L::bytes];
     const uint32_t stage_lds = lds_address(s_stage[wave][0]);
+    // The matrix operands of the block being computed live in the slot it was
+    // read from (its next load goes out after the block's math): score
+    // operands [chunk][lane group][row][word] in the first 2 KB, weight
+    // operands [group][lane group][row][word] in the next 2 KB. Rows are
+    // XOR-swizzled by lane group (scores) or group (weights), so that a wave's
+    // stores, lanes spread over lane group and row, hit distinct banks, and
+    // each lane's 16-byte (8-byte) operand read stays contiguous.
+    static_assert(KC * 4 * 64 * 4 + NG * 4 * 16 * 2 * 4 <= L::bytes, "the operands fit in one slot");
+    auto kb_at = [&](int k, int kc, int q, int row, int wd) -> uint32_t& {
+        return reinterpret_cast<uint32_t*>(s_stage[wave][k])[(kc * 4 + q) * 64 + ((row * 4 + wd) ^ (q * 4))];
+    };
+    auto va_at = [&](int k, int gr, int q, int row, int wd) -> uint32_t& {
+        return reinterpret_cast<uint32_t*>(s_stage[wave][k])[KC * 4 * 64 + gr * 128 + (((q * 16 + row) * 2 + wd) ^ (gr * 2))];
+    };
     // a wave's output rows at the end, in its first slot (no staging load is in flight then)
     auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
     static_assert(QG * D * 4 <= L::bytes, "the output rows fit in one slot");
@@ -310,15 +313,6 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
         s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
-    }
-    // digit columns / rows 4g + 3 stay zero
-    for (int idx = lane; idx < KC * 4 * 4 * 4; idx += 64) {
-        const int kc = idx / 64, q = (idx / 16) % 4, gg = (idx / 4) % 4, dw = idx % 4;
-        kb_at(kc, q, 4 * gg + 3, dw) = 0u;
-    }
-    for (int idx = lane; idx < NG * 4 * 4 * 2; idx += 64) {
-        const int gr = idx / 32, q = (idx / 8) % 4, gg = (idx / 2) % 4, dw = idx % 2;
-        va_at(gr, q, 4 * gg + 3, dw) = 0u;
     }
     __syncthreads();
     // per-query bounds |q| < 2^Eq; the producer's query (rho) at its channels,
@@ -461,7 +455,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     }
 
     // scores, softmax, weight digits of one block
-    auto key_math = [&](const R& r, int& ev) {
+    auto key_math = [&](const R& r, int& ev, int k_slot) {
         // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
         uint32_t smax = 0;  // scales are positive: their bit patterns order like the values
 #pragma unroll
@@ -483,7 +477,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             uint32_t wq[3];
             digit_words(vq[0], vq[1], vq[2], vq[3], wq);
 #pragma unroll
-            for (int d = 0; d < 3; ++d) kb_at(kc, n >> 2, 4 * rho + d, n & 3) = wq[d];
+            for (int d = 0; d < 3; ++d) kb_at(k_slot, kc, n >> 2, 4 * rho + d, n & 3) = wq[d];
         }
         // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
         const float zs = sum_cols<16>(zp) * scale;
@@ -504,7 +498,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
         v4i32 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(kc, rho, n, 0));
+            const uint4 bb = *reinterpret_cast<const uint4*>(&kb_at(k_slot, kc, rho, n, 0));
             v4i32 qd;
             qd[0] = (int)bb.x;
             qd[1] = (int)bb.y;
@@ -581,12 +575,12 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             digit_words(vp[0], vp[1], vp[2], vp[3], wp);
 #pragma unroll
             for (int d = 0; d < 3; ++d)
-                va_at(dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = wp[d];
+                va_at(k_slot, dq, 2 * tt + gl / 2, 4 * rho + d, gl % 2) = wp[d];
         }
         wave_lds_order();
     };
     // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
-    auto value_math = [&](const R& r, int ev) {
+    auto value_math = [&](const R& r, int ev, int k_slot) {
         const float vs = ldexpf(1.0f, ev - 22);
         constexpr int VB = 4;  // tiles on the matrix core before their results are combined
 #pragma unroll
@@ -595,7 +589,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
 #pragma unroll
             for (int i = 0; i < VB; ++i) {
                 const int vt = v0 + i;
-                const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(vt / 2, rho, n, 0));
+                const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(k_slot, vt / 2, rho, n, 0));
                 const uint32_t x = r.vc[vt];
                 uint32_t b0, b1;
                 if constexpr (BITS == 2) {
@@ -624,10 +618,9 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
         }
         wave_lds_order();
     };
-    // the next block's loads go out once the current block's key shares are
-    // consumed, and fly during its value phase
-    // a block is read from its slot, the slot refilled with the block NS
-    // further on, then the block's math runs from registers
+    // a block is read from its slot into registers, its math runs with the
+    // matrix operands in that slot, and then the slot is refilled with the
+    // block NS further on
     for (int j = j0; j < j1; j += NS * NWAVES) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {  // slot k: its address offsets are constants
@@ -636,10 +629,11 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             wait_staged<NL, NS>((j1 - 1 - jj) / NWAVES);
             R r;
             read_slot(k, r);
-            if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
+            wave_lds_order();  // the slot's reads stay before the operand stores into it
             int ev;
-            key_math(r, ev);
-            value_math(r, ev);
+            key_math(r, ev, k);
+            value_math(r, ev, k);
+            if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
         }
     }
 
