@@ -241,10 +241,20 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     // compile-time steps (which become the loads' immediate offsets)
     const int rt = gqa_row_token<BITS>(n);       // token of score column n in its tile
     const int ob_kw = (rt * L::W + (BITS == 2 ? rho : 2 * rho)) * 4;
-    const int ob_ks = L::ksz + gqa_channel<BITS>(0, n >> 2, 4 * (n & 3)) * 8;
     const int ob_vc = L::vcode + (n * BITS + (BITS == 2 ? rho / 2 : rho)) * 4;
     auto kw_off = [&](int tt, int kc) { return ob_kw + (16 * tt * L::W + (BITS == 2 ? 4 : 8) * kc) * 4; };
-    auto ks_off = [&](int kc, int k) { return ob_ks + gqa_channel<BITS>(kc, 0, k) * 8; };
+    // Key (s, z): the lane's k-th pair is that of byte k' = (k + kq) mod 4 of
+    // the digit word it produces (kq = n >> 2, the word's lane group), so the
+    // 16 lanes of a 64-bit LDS read hit 32 distinct banks (in byte order they
+    // would share 8); the digit words are rotated back by kq bytes before
+    // they are stored.
+    const int kq = n >> 2;
+    constexpr int KS_STEP = gqa_channel<BITS>(0, 0, 1) * 8;  // bytes from the pair of byte k to that of k + 1
+    const int ks_a = L::ksz + (gqa_channel<BITS>(0, kq, 4 * (n & 3)) + gqa_channel<BITS>(0, 0, kq)) * 8;
+    const int ks_b = ks_a - 4 * KS_STEP;  // where k + kq wraps past byte 3
+    auto ks_off = [&](int kc, int k) {
+        return (k + kq >= 4 ? ks_b : ks_a) + KS_STEP * k + gqa_channel<BITS>(kc, 0, 0) * 8;
+    };
     auto vs_off = [&](int tt, int r) {
         return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
     };
@@ -259,15 +269,17 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     // read from (its next load goes out after the block's math): score
     // operands [chunk][lane group][row][word] in the first 2 KB, weight
     // operands [group][lane group][row][word] in the next 2 KB. Rows are
-    // XOR-swizzled by lane group (scores) or group (weights), so that a wave's
-    // stores, lanes spread over lane group and row, hit distinct banks, and
-    // each lane's 16-byte (8-byte) operand read stays contiguous.
+    // XOR-swizzled by lane group (scores) or by group and lane group
+    // (weights), so that a wave's stores, lanes spread over lane group and
+    // row, hit distinct banks (32 or 64), and each lane's 16-byte (8-byte)
+    // operand read stays contiguous.
     static_assert(KC * 4 * 64 * 4 + NG * 4 * 16 * 2 * 4 <= L::bytes, "the operands fit in one slot");
     auto kb_at = [&](int k, int kc, int q, int row, int wd) -> uint32_t& {
         return reinterpret_cast<uint32_t*>(s_stage[wave][k])[(kc * 4 + q) * 64 + ((row * 4 + wd) ^ (q * 4))];
     };
     auto va_at = [&](int k, int gr, int q, int row, int wd) -> uint32_t& {
-        return reinterpret_cast<uint32_t*>(s_stage[wave][k])[KC * 4 * 64 + gr * 128 + (((q * 16 + row) * 2 + wd) ^ (gr * 2))];
+        return reinterpret_cast<uint32_t*>(
+            s_stage[wave][k])[KC * 4 * 64 + gr * 128 + (((q * 16 + row) * 2 + wd) ^ (gr * 2) ^ ((q & 1) << 4))];
     };
     // a wave's output rows at the end, in its first slot (no staging load is in flight then)
     auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float x = s_q[rho][gqa_channel<BITS>(kc, n >> 2, 4 * (n & 3) + k)];
+            const float x = s_q[rho][gqa_channel<BITS>(kc, kq, 4 * (n & 3) + ((k + kq) & 3))];
             qn[kc][k] = ldexpf(x, 22 - eq_mine);
             qv[kc][k] = x;
         }
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             uint32_t wq[3];
             digit_words(vq[0], vq[1], vq[2], vq[3], wq);
 #pragma unroll
-            for (int d = 0; d < 3; ++d) kb_at(k_slot, kc, n >> 2, 4 * rho + d, n & 3) = wq[d];
+            for (int d = 0; d < 3; ++d) kb_at(k_slot, kc, kq, 4 * rho + d, n & 3) = __builtin_rotateleft32(wq[d], 8 * kq);
         }
         // key zeros: Z = sum_c q[rho][c] z[c], summed over row rho (all its lanes hold it)
         const float zs = sum_cols<16>(zp) * scale;
