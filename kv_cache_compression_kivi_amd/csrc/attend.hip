@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "attend_common.hpp"
 #include "split.hpp"
@@ -180,10 +181,16 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 
 // ------------------------------------------------------------ kernel
 
-// Key blocks each wave keeps in registers: the one being computed and PF - 1
-// in flight (measured on MI355X: 3 with one query head per work-group of 8
-// waves; more buys nothing once the HBM queue is full).
-constexpr int attend_prefetch(int D, int QG) { return QG == 1 && D <= 128 ? 3 : 2; }
+// Key blocks computed together by one wave: two with one query head at
+// d <= 128 (their LDS round trips and cross-lane reductions are shared, and
+// the two blocks' independent work interleaves), else one.
+constexpr int attend_pair(int D, int QG) { return QG == 1 && D <= 128 ? 2 : 1; }
+
+// Key blocks each wave keeps in registers: the NP being computed and the
+// next NP in flight (two blocks in flight with one query head at d <= 128;
+// measured on MI355X, more buys nothing once the HBM queue is full), else
+// the one being computed and one in flight.
+constexpr int attend_prefetch(int D, int QG) { return 2 * attend_pair(D, QG); }
 
 // Two lane layouts per wave. Key side: lane = tl * NW + w scores tokens
 // tl + TL*i against channels [16w, 16w + 16). Value side: lane L accumulates
@@ -200,8 +207,9 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     constexpr int NACC = 2;      // partial sums per value channel (shorter dependency chains)
     constexpr int NT = 64 * NWAVES;
     __shared__ __align__(16) float s_q[QG][D];              // the query heads, fp32
-    __shared__ __align__(16) float s_qt[NWAVES][QG][D];     // each wave's folded query; at the end its output
-    __shared__ __align__(16) float s_p[NWAVES][QG][NG][kG]; // each wave's value weights of one chunk
+    constexpr int NP = attend_pair(D, QG);                        // key blocks computed together
+    __shared__ __align__(16) float s_qt[NWAVES][NP][QG][D];      // each wave's folded queries; at the end its output
+    __shared__ __align__(16) float s_p[NWAVES][NP][QG][NG][kG];  // each wave's value weights of NP chunks
     __shared__ float s_m[NWAVES][QG], s_l[NWAVES][QG], s_z[NWAVES][QG][NG];
 
     const CacheGeom& g = a.g;
@@ -234,14 +242,14 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
     const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
 
-    // the first PF - 1 key blocks go in flight before anything waits
+    // the first NP key blocks go in flight before anything waits
     constexpr int PF = attend_prefetch(D, QG);
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
     const LaneOffsets lo = lane_offsets<D, BITS>(lane, w, tl);
     B rr[PF];
 #pragma unroll
-    for (int k = 0; k < PF - 1; ++k)
+    for (int k = 0; k < NP; ++k)
         if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
 
     // residual chunks (fp16 rows from the ring) are computed first, while the
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
             for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) s_p[wave][gq][0][tl + TL * i] = valid[i] ? p[gq][i] : 0.f;
+                for (int i = 0; i < TPL; ++i) s_p[wave][0][gq][0][tl + TL * i] = valid[i] ? p[gq][i] : 0.f;
         }
         wave_lds_order();
 #pragma unroll
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             float pv[kG];
 #pragma unroll
             for (int t4 = 0; t4 < kG / 4; ++t4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][0][4 * t4]);
+                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][0][gq][0][4 * t4]);
                 pv[4 * t4] = x.x;
                 pv[4 * t4 + 1] = x.y;
                 pv[4 * t4 + 2] = x.z;
@@ -380,95 +388,107 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         wave_lds_order();
     };
 
-    // key blocks: a ring of PF register sets, the loads of the next PF - 1
-    // blocks in flight while one is computed
-    auto block_math = [&](const B& r) {
-        float Z[QG];
+    // key blocks, NB (one or two) at a time: their folds and value weights go
+    // through the LDS together, and one softmax update covers all their tokens
+    auto blocks_math = [&](auto nb_tag, const B* r) {
+        constexpr int NB = decltype(nb_tag)::value;
+        float Z[NB][QG];
 #pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float zp = 0.f;
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                s_qt[wave][gq][lane * CPL + k] = qf[gq][k] * r.ksz[2 * k];
-                zp = fmaf(qz[gq][k], r.ksz[2 * k + 1], zp);
-            }
-            Z[gq] = wave_sum(zp);
-        }
-        wave_lds_order();
-        // scores: token by token, every query against the same 16 code halves
-        float qt[QG][16];
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_qt[wave][gq][16 * w + 4 * c4]);
-                qt[gq][4 * c4] = x.x;
-                qt[gq][4 * c4 + 1] = x.y;
-                qt[gq][4 * c4 + 2] = x.z;
-                qt[gq][4 * c4 + 3] = x.w;
-            }
-        float sc[QG][TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            float cf[16];
-            code_halves<BITS, BITS / 2>(r.kc[i], cf);
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
             for (int gq = 0; gq < QG; ++gq) {
-                float acc = 0.f;
+                float zp = 0.f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) acc = fmaf(qt[gq][c], cf[c], acc);
-                sc[gq][i] = (sum_cols<NW>(acc) + Z[gq]) * scale_q;
+                for (int k = 0; k < CPL; ++k) {
+                    s_qt[wave][bb][gq][lane * CPL + k] = qf[gq][k] * r[bb].ksz[2 * k];
+                    zp = fmaf(qz[gq][k], r[bb].ksz[2 * k + 1], zp);
+                }
+                Z[bb][gq] = wave_sum(zp);
+            }
+        wave_lds_order();
+        // scores: token by token, every query against the same 16 code halves
+        float sc[QG][NB * TPL];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            float qt[QG][16];
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const float4 x = *reinterpret_cast<const float4*>(&s_qt[wave][bb][gq][16 * w + 4 * c4]);
+                    qt[gq][4 * c4] = x.x;
+                    qt[gq][4 * c4 + 1] = x.y;
+                    qt[gq][4 * c4 + 2] = x.z;
+                    qt[gq][4 * c4 + 3] = x.w;
+                }
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                float cf[16];
+                code_halves<BITS, BITS / 2>(r[bb].kc[i], cf);
+#pragma unroll
+                for (int gq = 0; gq < QG; ++gq) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) acc = fmaf(qt[gq][c], cf[c], acc);
+                    sc[gq][bb * TPL + i] = (sum_cols<NW>(acc) + Z[bb][gq]) * scale_q;
+                }
             }
         }
-        float p[QG][TPL];
-        softmax_update<QG, TPL, NW, CPV * NACC>(sc, p, m, l, zacc, o);
+        float p[QG][NB * TPL];
+        softmax_update<QG, NB * TPL, NW, CPV * NACC>(sc, p, m, l, zacc, o);
         // value weights p s_t 2^(24 - b jpos(t)) of token t in its group's row;
         // the value zeros accumulate per lane as sum p z_t
         if (wlead) {
 #pragma unroll
-            for (int gq = 0; gq < QG; ++gq)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    s_p[wave][gq][w >> 1][tl + TL * i] = p[gq][i] * (r.vsz[i].x * tf[i]);
-                    zacc[gq] = fmaf(p[gq][i], r.vsz[i].y, zacc[gq]);
-                }
+                for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+                    for (int i = 0; i < TPL; ++i) {
+                        s_p[wave][bb][gq][w >> 1][tl + TL * i] = p[gq][bb * TPL + i] * (r[bb].vsz[i].x * tf[i]);
+                        zacc[gq] = fmaf(p[gq][bb * TPL + i], r[bb].vsz[i].y, zacc[gq]);
+                    }
         }
         wave_lds_order();
-        // values: one code word of one channel at a time, against each query's weights
-        // one code word (32/b tokens) of one channel at a time
+        // values: one code word (32/b tokens) of one channel at a time, against each query's weights
         constexpr int PW = 32 / BITS;
 #pragma unroll
-        for (int k = 0; k < CPV; ++k)
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-            for (int wd = 0; wd < BITS; ++wd) {
-                float cf[PW];
-                code_halves<BITS, 1>(&r.vc[k * BITS + wd], cf);
+            for (int k = 0; k < CPV; ++k)
 #pragma unroll
-                for (int gq = 0; gq < QG; ++gq) {
-                    float pv[PW];
+                for (int wd = 0; wd < BITS; ++wd) {
+                    float cf[PW];
+                    code_halves<BITS, 1>(&r[bb].vc[k * BITS + wd], cf);
 #pragma unroll
-                    for (int t4 = 0; t4 < PW / 4; ++t4) {
-                        const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][vgrp][PW * wd + 4 * t4]);
-                        pv[4 * t4] = x.x;
-                        pv[4 * t4 + 1] = x.y;
-                        pv[4 * t4 + 2] = x.z;
-                        pv[4 * t4 + 3] = x.w;
+                    for (int gq = 0; gq < QG; ++gq) {
+                        float pv[PW];
+#pragma unroll
+                        for (int t4 = 0; t4 < PW / 4; ++t4) {
+                            const float4 x =
+                                *reinterpret_cast<const float4*>(&s_p[wave][bb][gq][vgrp][PW * wd + 4 * t4]);
+                            pv[4 * t4] = x.x;
+                            pv[4 * t4 + 1] = x.y;
+                            pv[4 * t4 + 2] = x.z;
+                            pv[4 * t4 + 3] = x.w;
+                        }
+#pragma unroll
+                        for (int t = 0; t < PW; ++t)
+                            o[gq][k * NACC + t % NACC] = fmaf(pv[t], cf[t], o[gq][k * NACC + t % NACC]);
                     }
-#pragma unroll
-                    for (int t = 0; t < PW; ++t)
-                        o[gq][k * NACC + t % NACC] = fmaf(pv[t], cf[t], o[gq][k * NACC + t % NACC]);
                 }
-            }
         wave_lds_order();
     };
     for (int ck = ck0; ck < rc; ck += NWAVES) {
         if (!kEarly || ck != ck0) load_chunk(ck);
         chunk_math();
     }
+    // a ring of PF = 2 NP register sets: the NP blocks being computed, and the
+    // next NP in flight (issued just before)
     for (int j = j0; j < j1; j += PF * NWAVES) {
 #pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int jj = j + k * NWAVES;
+        for (int h = 0; h < 2; ++h) {
+            const int jj = j + h * NP * NWAVES;
             if (jj >= j1) break;
             // issue priority by work left: the SIMD favours older waves, so
             // without it the younger waves of a work-group finish last
@@ -479,12 +499,17 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 else if (left >= 2) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
             }
-            const int jn = jj + (PF - 1) * NWAVES;
-            if (jn < j1) load_block<D, BITS>(rs, (uint32_t)(jn * L::bytes), lo, rr[(k + PF - 1) % PF]);
-            block_math(rr[k]);
+#pragma unroll
+            for (int e = 0; e < NP; ++e) {
+                const int jn = jj + (NP + e) * NWAVES;
+                if (jn < j1) load_block<D, BITS>(rs, (uint32_t)(jn * L::bytes), lo, rr[(1 - h) * NP + e]);
+            }
+            if (NP == 2 && jj + NWAVES < j1)
+                blocks_math(std::integral_constant<int, NP>(), &rr[h * NP]);
+            else
+                blocks_math(std::integral_constant<int, 1>(), &rr[h * NP]);
         }
     }
-
 
     // per-wave totals: the weight sum and each group's value-zero sum over the
     // token lanes; the zero sum joins every channel of its group
@@ -509,7 +534,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
 #pragma unroll
-        for (int k = 0; k < CPV; ++k) s_qt[wave][gq][cv0 + k] = ov[gq][k];
+        for (int k = 0; k < CPV; ++k) s_qt[wave][0][gq][cv0 + k] = ov[gq][k];
         if (lane == 0) {
             s_m[wave][gq] = m[gq];
             s_l[wave][gq] = l[gq];
@@ -527,7 +552,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             if (s_m[wv][gq] != -INFINITY) {
                 const float f = __builtin_amdgcn_exp2f(s_m[wv][gq] - M);
                 Lsum = fmaf(s_l[wv][gq], f, Lsum);
-                O = fmaf(s_qt[wv][gq][c], f, O);
+                O = fmaf(s_qt[wv][0][gq][c], f, O);
             }
         }
         if (a.n_split == 1) {
