@@ -56,22 +56,22 @@ struct LaneOffsets {
     int code, vcode, ksz, vsz;
 };
 
-template <int D, int BITS>
+template <int D, int BITS, int CW>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane, int w, int tl) {
-    using B = BlockRegs<D, BITS>;
+    using B = BlockRegs<D, BITS, CW>;
     using L = Rec<D, BITS>;
     LaneOffsets o;
     o.code = (tl * L::W + w * B::NWORD) * 4;
     o.vcode = L::vcode + lane * B::CPV * BITS * 4;
     o.ksz = L::ksz + lane * 2 * B::CPL * 4;
-    o.vsz = L::vsz + (tl * (D / kVG) + (w >> 1)) * 8;
+    o.vsz = L::vsz + (tl * (D / kVG) + w * CW / kVG) * 8;
     return o;
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int CW>
 __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, uint32_t soff, const LaneOffsets& lo,
-                                           BlockRegs<D, BITS>& r) {
-    using B = BlockRegs<D, BITS>;
+                                           BlockRegs<D, BITS, CW>& r) {
+    using B = BlockRegs<D, BITS, CW>;
     using L = Rec<D, BITS>;
     const int so = __builtin_amdgcn_readfirstlane((int)soff);  // uniform: the block's offset
     if constexpr (B::CPL == 1) {
@@ -91,10 +91,14 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rs, uint32_t s
         const int toff = i * B::TL * L::W * 4;
         if constexpr (B::NWORD == 1) {
             r.kc[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.code + toff, so, 2);
-        } else {
+        } else if constexpr (B::NWORD == 2) {
             const auto kk = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.code + toff, so, 2);
             r.kc[i][0] = kk[0];
             r.kc[i][1] = kk[1];
+        } else {
+            const auto kk = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code + toff, so, 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r.kc[i][e] = kk[e];
         }
         const auto sz = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.vsz + i * B::TL * (D / kVG) * 8, so, 2);
         r.vsz[i] = make_float2(__uint_as_float(sz[0]), __uint_as_float(sz[1]));
@@ -181,6 +185,12 @@ __device__ __forceinline__ void softmax_update(const float (&sc)[QG][TPL], float
 
 // ------------------------------------------------------------ kernel
 
+// Channels per score column of attend_kernel: 32 at d = 128 (4 columns x 16
+// token lanes, 2 tokens per lane: a token's score needs 2 cross-lane sums
+// instead of 3, and the softmax and weight steps run over 2 tokens a lane
+// instead of 4), else 16.
+constexpr int attend_cw(int D) { return D == 128 ? 32 : 16; }
+
 // Key blocks computed together by one wave: two with one query head at
 // d <= 128 (their LDS round trips and cross-lane reductions are shared, and
 // the two blocks' independent work interleaves), else one.
@@ -199,7 +209,8 @@ constexpr int attend_prefetch(int D, int QG) { return 2 * attend_pair(D, QG); }
 // weights per value group, the group's scale and the code-half factor folded in).
 template <int D, int BITS, int QG, int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a) {
-    using B = BlockRegs<D, BITS>;
+    constexpr int CW = attend_cw(D);
+    using B = BlockRegs<D, BITS, CW>;
     using P = CodePos<BITS>;
     using L = Rec<D, BITS>;
     constexpr int NW = B::NW, TL = B::TL, TPL = B::TPL, CPL = B::CPL, CPV = B::CPV;
@@ -219,7 +230,8 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = lane % NW, tl = lane / NW;
     const int cv0 = lane * CPV, vgrp = cv0 / kVG;  // this lane's value channels and their group
-    const bool wlead = (w & 1) == 0;               // writes its group's value weights
+    const int wgrp = w * CW / kVG;                 // the value group of column w
+    const bool wlead = w * CW % kVG == 0;          // writes its group's value weights
     const int split = blockIdx.x;
     const int64_t u = blockIdx.y;
     const int group = g.n_q_heads / g.n_kv_heads;
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     constexpr int PF = attend_prefetch(D, QG);
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
-    const LaneOffsets lo = lane_offsets<D, BITS>(lane, w, tl);
+    const LaneOffsets lo = lane_offsets<D, BITS, CW>(lane, w, tl);
     B rr[PF];
 #pragma unroll
     for (int k = 0; k < NP; ++k)
@@ -260,7 +272,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int slot0 = (int)(a.n_quant % g.ring_slots);
     const int ck0 = NWAVES - 1 - wave;  // chunk ck goes to wave NWAVES - 1 - ck % NWAVES
     constexpr int VRW = (CPV + 1) / 2;  // words of fp16 value pairs per token
-    uint4 kraw[TPL][2];                 // key rows of this lane's tokens, column w
+    uint4 kraw[TPL][CW / 8];            // key rows of this lane's tokens, column w
     uint32_t vr[kG][VRW];               // value rows of this lane's channels, all 32 tokens
     bool valid[TPL];
     auto load_chunk = [&](int ck) {
@@ -272,10 +284,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             slot -= slot >= ring ? ring : 0;
             // the token appended by this call comes from its input row
             const uint4* kp = a.n_quant + idx == a.t_new
-                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
-                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
+                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + CW * w)
+                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 2 * CW * w);
+#pragma unroll
+            for (int e = 0; e < CW / 8; ++e) kraw[i][e] = kp[e];
         }
 #pragma unroll
         for (int t = 0; t < kG; ++t) {
@@ -338,10 +350,10 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         float sc[QG][TPL];
 #pragma unroll
         for (int gq = 0; gq < QG; ++gq) {
-            float qv[16];
+            float qv[CW];
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][16 * w + 4 * c4]);
+            for (int c4 = 0; c4 < CW / 4; ++c4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][CW * w + 4 * c4]);
                 qv[4 * c4] = x.x;
                 qv[4 * c4 + 1] = x.y;
                 qv[4 * c4 + 2] = x.z;
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 const uint16_t* kh = reinterpret_cast<const uint16_t*>(kraw[i]);
                 float acc = 0.f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) acc = fmaf(qv[c], h2f(kh[c]), acc);
+                for (int c = 0; c < CW; ++c) acc = fmaf(qv[c], h2f(kh[c]), acc);
                 acc = sum_cols<NW>(acc) * scale;
                 sc[gq][i] = valid[i] ? acc : -INFINITY;
             }
@@ -406,16 +418,16 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 Z[bb][gq] = wave_sum(zp);
             }
         wave_lds_order();
-        // scores: token by token, every query against the same 16 code halves
+        // scores: token by token, every query against the same CW code halves
         float sc[QG][NB * TPL];
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
-            float qt[QG][16];
+            float qt[QG][CW];
 #pragma unroll
             for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const float4 x = *reinterpret_cast<const float4*>(&s_qt[wave][bb][gq][16 * w + 4 * c4]);
+                for (int c4 = 0; c4 < CW / 4; ++c4) {
+                    const float4 x = *reinterpret_cast<const float4*>(&s_qt[wave][bb][gq][CW * w + 4 * c4]);
                     qt[gq][4 * c4] = x.x;
                     qt[gq][4 * c4 + 1] = x.y;
                     qt[gq][4 * c4 + 2] = x.z;
@@ -423,13 +435,13 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 }
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                float cf[16];
-                code_halves<BITS, BITS / 2>(r[bb].kc[i], cf);
+                float cf[CW];
+                code_halves<BITS, B::NWORD>(r[bb].kc[i], cf);
 #pragma unroll
                 for (int gq = 0; gq < QG; ++gq) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) acc = fmaf(qt[gq][c], cf[c], acc);
+                    for (int c = 0; c < CW; ++c) acc = fmaf(qt[gq][c], cf[c], acc);
                     sc[gq][bb * TPL + i] = (sum_cols<NW>(acc) + Z[bb][gq]) * scale_q;
                 }
             }
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
                 for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
                     for (int i = 0; i < TPL; ++i) {
-                        s_p[wave][bb][gq][w >> 1][tl + TL * i] = p[gq][bb * TPL + i] * (r[bb].vsz[i].x * tf[i]);
+                        s_p[wave][bb][gq][wgrp][tl + TL * i] = p[gq][bb * TPL + i] * (r[bb].vsz[i].x * tf[i]);
                         zacc[gq] = fmaf(p[gq][bb * TPL + i], r[bb].vsz[i].y, zacc[gq]);
                     }
         }
@@ -517,7 +529,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     for (int gq = 0; gq < QG; ++gq) {
         l[gq] = tok_sum<NW>(l[gq]);
         const float zt = tok_sum<NW>(zacc[gq]);
-        if (tl == 0 && wlead) s_z[wave][gq][w >> 1] = zt;
+        if (tl == 0 && wlead) s_z[wave][gq][wgrp] = zt;
     }
     wave_lds_order();
     float ov[QG][CPV];

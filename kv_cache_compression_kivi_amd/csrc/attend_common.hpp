@@ -113,12 +113,13 @@ struct Rec {
 };
 
 // One lane's share of a block record, loaded ahead of its use. Key side:
-// lane = tl * NW + w holds key-code words of tokens tl + TL*i, column w. Value
-// side: lane L holds the value codes of channels L*CPV .. L*CPV + CPV - 1,
-// all 32 tokens (BITS words per channel).
-template <int D, int BITS>
+// lane = tl * NW + w holds key-code words of tokens tl + TL*i, column w
+// (channels [CW w, CW w + CW)). Value side: lane L holds the value codes of
+// channels L*CPV .. L*CPV + CPV - 1, all 32 tokens (BITS words per channel).
+template <int D, int BITS, int CW = 16>
 struct BlockRegs {
-    static constexpr int NW = D / 16, TL = 64 / NW, TPL = kG / TL, NWORD = BITS / 2, CPL = D / 64;
+    static_assert(CW == 16 || CW == 32, "a score column is 16 or 32 channels");
+    static constexpr int NW = D / CW, TL = 64 / NW, TPL = kG / TL, NWORD = CW * BITS / 32, CPL = D / 64;
     static constexpr int CPV = D / 64;  // value channels per lane
     float ksz[2 * CPL];          // (s, z) of channels lane*CPL .. lane*CPL + CPL - 1
     uint32_t kc[TPL][NWORD];     // key code words of this lane's tokens and column
