@@ -317,15 +317,15 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt) r.vc[vt] = *reinterpret_cast<const uint32_t*>(sb + ob_vc + 16 * vt * BITS * 4);
     };
-    // the first blocks go in flight before anything waits
-#pragma unroll
-    for (int k = 0; k < NS; ++k)
-        if (j0 + k * NWAVES < j1) stage(j0 + k * NWAVES, k);
-
+    // the query first, while nothing else is in flight (its wait counts every
+    // load issued before it), then the first blocks' staging loads
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
         s_q[idx / D][idx % D] = a.q_bf16 ? bf2f(v) : h2f(v);
     }
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        if (j0 + k * NWAVES < j1) stage(j0 + k * NWAVES, k);
     __syncthreads();
     // per-query bounds |q| < 2^Eq; the producer's query (rho) at its channels,
     // scaled to 2^22 of the bound (digits) and as it is (key zeros)
@@ -370,102 +370,14 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
         for (int c = 0; c < CPV * NACC; ++c) o_res[gq][c] *= alpha;
     };
 
-    // residual chunks (vector units, as in attend_kernel)
+    // residual chunks (vector units, as in attend_kernel): computed after the
+    // key blocks, once no staging load is in flight, so that their loads (whose
+    // waits count every earlier load) do not wait for the staged blocks, and
+    // the kernel's first loads are the query and the staged blocks only
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
     const int slot0 = (int)(a.n_quant % g.ring_slots);
     if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0) write_new_token<D>(a, u, rbase);
-    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
-        uint4 kraw[TPL][2];
-        bool valid[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int idx = ck * kG + tl + TL * i;
-            valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);
-            slot -= slot >= ring ? ring : 0;
-            const uint4* kp = a.n_quant + idx == a.t_new
-                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
-                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
-            kraw[i][0] = kp[0];
-            kraw[i][1] = kp[1];
-        }
-        uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
-#pragma unroll
-        for (int t = 0; t < kG; ++t) {
-            const int idx = ck * kG + t;
-            int slot = slot0 + (idx < (int)nres ? idx : 0);
-            slot -= slot >= ring ? ring : 0;
-            vr[t] = a.n_quant + idx == a.t_new
-                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
-                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
-        }
-        float sc[QG][TPL];
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float qq[16];
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][16 * w + 4 * c4]);
-                qq[4 * c4] = x.x;
-                qq[4 * c4 + 1] = x.y;
-                qq[4 * c4 + 2] = x.z;
-                qq[4 * c4 + 3] = x.w;
-            }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const uint16_t* kh = reinterpret_cast<const uint16_t*>(kraw[i]);
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc = fmaf(qq[c], h2f(kh[c]), acc);
-                acc = sum_cols<NW>(acc) * scale;
-                sc[gq][i] = valid[i] ? acc : -INFINITY;
-            }
-        }
-        float p[QG][TPL];
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float bm = sc[gq][0];
-#pragma unroll
-            for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sc[gq][i]);
-            bm = tok_max<NW>(bm);
-            if (bm > m[gq]) {
-                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bm));
-                m[gq] = bm;
-            }
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                p[gq][i] = valid[i] ? __builtin_amdgcn_exp2f(sc[gq][i] - m[gq]) : 0.f;
-                l_res[gq] += p[gq][i];
-            }
-        }
-        if (w == 0) {
-#pragma unroll
-            for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) s_p[wave][gq][tl + TL * i] = p[gq][i];
-        }
-        wave_lds_order();
-#pragma unroll
-        for (int gq = 0; gq < QG; ++gq) {
-            float pv[kG];
-#pragma unroll
-            for (int t4 = 0; t4 < kG / 4; ++t4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][4 * t4]);
-                pv[4 * t4] = x.x;
-                pv[4 * t4 + 1] = x.y;
-                pv[4 * t4 + 2] = x.z;
-                pv[4 * t4 + 3] = x.w;
-            }
-#pragma unroll
-            for (int t = 0; t < kG; ++t) {
-                o_res[gq][t % NACC] = fmaf(pv[t], half_lo(vr[t]), o_res[gq][t % NACC]);
-                o_res[gq][NACC + t % NACC] = fmaf(pv[t], half_hi(vr[t]), o_res[gq][NACC + t % NACC]);
-            }
-        }
-        wave_lds_order();
-    }
-
     // scores, softmax, weight digits of one block
     auto key_math = [&](const R& r, int& ev, int k_slot) {
         // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
@@ -647,6 +559,97 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             value_math(r, ev, k);
             if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
         }
+    }
+
+    for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
+        uint4 kraw[TPL][2];
+        bool valid[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int idx = ck * kG + tl + TL * i;
+            valid[i] = idx < (int)nres;
+            int slot = slot0 + (valid[i] ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            const uint4* kp = a.n_quant + idx == a.t_new
+                                  ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
+                                  : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
+            kraw[i][0] = kp[0];
+            kraw[i][1] = kp[1];
+        }
+        uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
+#pragma unroll
+        for (int t = 0; t < kG; ++t) {
+            const int idx = ck * kG + t;
+            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            slot -= slot >= ring ? ring : 0;
+            vr[t] = a.n_quant + idx == a.t_new
+                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
+                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
+        }
+        float sc[QG][TPL];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float qq[16];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_q[gq][16 * w + 4 * c4]);
+                qq[4 * c4] = x.x;
+                qq[4 * c4 + 1] = x.y;
+                qq[4 * c4 + 2] = x.z;
+                qq[4 * c4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const uint16_t* kh = reinterpret_cast<const uint16_t*>(kraw[i]);
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc = fmaf(qq[c], h2f(kh[c]), acc);
+                acc = sum_cols<NW>(acc) * scale;
+                sc[gq][i] = valid[i] ? acc : -INFINITY;
+            }
+        }
+        float p[QG][TPL];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float bm = sc[gq][0];
+#pragma unroll
+            for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sc[gq][i]);
+            bm = tok_max<NW>(bm);
+            if (bm > m[gq]) {
+                rescale(gq, __builtin_amdgcn_exp2f(m[gq] - bm));
+                m[gq] = bm;
+            }
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                p[gq][i] = valid[i] ? __builtin_amdgcn_exp2f(sc[gq][i] - m[gq]) : 0.f;
+                l_res[gq] += p[gq][i];
+            }
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) s_p[wave][gq][tl + TL * i] = p[gq][i];
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) {
+            float pv[kG];
+#pragma unroll
+            for (int t4 = 0; t4 < kG / 4; ++t4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_p[wave][gq][4 * t4]);
+                pv[4 * t4] = x.x;
+                pv[4 * t4 + 1] = x.y;
+                pv[4 * t4 + 2] = x.z;
+                pv[4 * t4 + 3] = x.w;
+            }
+#pragma unroll
+            for (int t = 0; t < kG; ++t) {
+                o_res[gq][t % NACC] = fmaf(pv[t], half_lo(vr[t]), o_res[gq][t % NACC]);
+                o_res[gq][NACC + t % NACC] = fmaf(pv[t], half_hi(vr[t]), o_res[gq][NACC + t % NACC]);
+            }
+        }
+        wave_lds_order();
     }
 
     // per-wave totals. Block part of query rho (row rho): its max m_b, weight
