@@ -25,12 +25,12 @@
 // Half the positions of a half-word are masked in place and half after one
 // shift right by 8 bits, so b*j < 8 and the code never reaches the exponent
 // field. The powers of two go into the query (key side: q_c 2^(-b j(c)), and
-// 2^24 into the score scale) and into the output (value side: 2^(24 - b j(c))
-// per channel once at the end).
+// 2^24 into the score scale) and into the value weights (value side:
+// 2^(24 - b j(t)) per token).
 //
 // Lane layout inside a wave: lane = tl * NW + w. Column w owns channels
-// [16w, 16w + 16) (one code word at b = 2, two at b = 4); token lane tl owns
-// tokens tl, tl + TL, ... of every 32-token chunk. Reductions use DPP inside
+// [CW w, CW w + CW) (CW = 32 at d = 128, else 16: CW b / 32 code words); token
+// lane tl owns tokens tl, tl + TL, ... of every 32-token chunk. Reductions use DPP inside
 // rows of 16 lanes and permlane swaps across rows: VALU only, no LDS traffic.
 // Block records are read with buffer loads: the unit's records are one
 // buffer, the block offset is a scalar and each lane's offsets are constants,
@@ -133,8 +133,8 @@ struct CodePos {
 
 // The codes of NWD packed words as exact floats, in code order: word k holds
 // codes [P k, P (k + 1)) (P = 32 / b), code P k + i at bits [b i, b i + b), and
-// cf[P k + i] = code * 2^(b * jpos(i) - 24). Key side: one token's 16 channels
-// of a column (b / 2 words); value side: one channel's 32 tokens (b words).
+// cf[P k + i] = code * 2^(b * jpos(i) - 24). Key side: one token's channels
+// of a column (CW b / 32 words); value side: one word of a channel's tokens.
 // Each cf feeds an FMA directly (v_fma_mix_f32 reads the half).
 template <int BITS, int NWD>
 __device__ __forceinline__ void code_halves(const uint32_t* wd, float (&cf)[NWD * 32 / BITS]) {
@@ -203,7 +203,7 @@ constexpr int attend_pair(int D, int QG) { return QG == 1 && D <= 128 ? 2 : 1; }
 constexpr int attend_prefetch(int D, int QG) { return 2 * attend_pair(D, QG); }
 
 // Two lane layouts per wave. Key side: lane = tl * NW + w scores tokens
-// tl + TL*i against channels [16w, 16w + 16). Value side: lane L accumulates
+// tl + TL*i against channels [CW w, CW w + CW). Value side: lane L accumulates
 // channels [L*CPV, L*CPV + CPV) over all 32 tokens of a chunk, with the
 // chunk's weights passed through a wave-private LDS slot (one row of 32
 // weights per value group, the group's scale and the code-half factor folded in).
