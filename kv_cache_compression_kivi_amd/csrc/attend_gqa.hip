@@ -26,6 +26,7 @@
 // The fp16 residual runs on the vector units as in attend_kernel.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "attend_common.hpp"
@@ -192,10 +193,10 @@ __device__ __forceinline__ void wait_staged(int later) {
     else wait_vmem<0>();
 }
 
-// Three 4-wave work-groups per CU at b = 2 (at most 168 VGPRs a lane); b = 4
-// holds twice the code words and runs two.
+// Two 4-wave work-groups per CU (up to 256 VGPRs a lane: the value digit
+// sums stay in matrix-core accumulators across blocks).
 template <int D, int BITS, int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const AttendArgs a) {
     constexpr int QG = 4;
     using B = BlockRegs<D, BITS>;
     using R = GqaRegs<D, BITS>;
@@ -363,6 +364,23 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) o_blk[vt] = 0.f;
     float m_b = -INFINITY, l_b = 0.f, z_b = 0.f;
+    // value digit sums of the blocks since the last fold, per tile (rows 4 rho
+    // + d), accumulated on the matrix cores; the weights' digits are taken
+    // against 2^ew (ew wave-uniform, moved only at a fold)
+    v4i32 acc_v[VT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) acc_v[vt] = v4i32{0, 0, 0, 0};
+    int ew = INT_MIN / 2;
+    // o_blk += 2^(ew - 22) sum_d 2^(8d) acc_v[d], then the sums restart
+    auto fold = [&]() {
+        const float vs = ldexpf(1.0f, ew - 22);
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            const float comb = fmaf((float)acc_v[vt][2], 65536.0f, fmaf((float)acc_v[vt][1], 256.0f, (float)acc_v[vt][0]));
+            o_blk[vt] = fmaf(comb, vs, o_blk[vt]);
+            acc_v[vt] = v4i32{0, 0, 0, 0};
+        }
+    };
     // multiply the residual accumulators of query gq by alpha (a new running maximum)
     auto rescale = [&](int gq, float alpha) {
         l_res[gq] *= alpha;
@@ -412,6 +430,13 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) vmax = umax(vmax, __float_as_uint(r.vsz[tt][r2].x));
         ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
+        // the weights' exponent follows the block's bound when it grows, or
+        // when the bound falls more than 2 below it (at most 2 of the digits'
+        // 22 bits left unused)
+        if (ev > ew || ev < ew - 2) {
+            fold();
+            ew = ev;
+        }
         wave_lds_order();
         // 2. scores of query rho and token rt of each tile: the digit sums of
         //    rows 4 rho .. 4 rho + 2 land in this lane's accumulators 0 .. 2
@@ -468,6 +493,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             const float alpha = __builtin_amdgcn_exp2f(m_b - bm);
             l_b *= alpha;
             z_b *= alpha;
+            fold();
 #pragma unroll
             for (int vt = 0; vt < VT; ++vt) o_blk[vt] *= alpha;
             m_b = bm;
@@ -478,7 +504,7 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             pt[tt] = __builtin_amdgcn_exp2f(sc[tt] - m_b);
             l_b += pt[tt];
         }
-        const DigitScale dv = digit_scale(ev - 22);
+        const DigitScale dv = digit_scale(ew - 22);
         // 4. weights p s_t of value group dq for the tokens of quad gl (gathered
         //    from its four lanes), as digits: rows 4 rho + d of the value operand,
         //    one word per tile (lane group 2tt + gl/2, word gl%2)
@@ -504,41 +530,24 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
         wave_lds_order();
     };
     // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
-    auto value_math = [&](const R& r, int ev, int k_slot) {
-        const float vs = ldexpf(1.0f, ev - 22);
-        constexpr int VB = 4;  // tiles on the matrix core before their results are combined
+    // values of one block: acc_v[vt] += sum_t P[g][t] code[t][c] (digit rows)
+    auto value_math = [&](const R& r, int k_slot) {
 #pragma unroll
-        for (int v0 = 0; v0 < VT; v0 += VB) {
-            v4i32 c[VB];
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                const int vt = v0 + i;
-                const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(k_slot, vt / 2, rho, n, 0));
-                const uint32_t x = r.vc[vt];
-                uint32_t b0, b1;
-                if constexpr (BITS == 2) {
-                    const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
-                    b0 = (x >> sh) & 0x03030303u;
-                    b1 = (x >> (sh + 2)) & 0x03030303u;
-                } else {
-                    b0 = x & 0x0F0F0F0Fu;
-                    b1 = (x >> 4) & 0x0F0F0F0Fu;
-                }
-                const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
-                const long bv = (long)(((uint64_t)b1 << 32) | b0);
-                c[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, v4i32{0, 0, 0, 0}, 0, 0, 0);
+        for (int vt = 0; vt < VT; ++vt) {
+            const uint2 pa = *reinterpret_cast<const uint2*>(&va_at(k_slot, vt / 2, rho, n, 0));
+            const uint32_t x = r.vc[vt];
+            uint32_t b0, b1;
+            if constexpr (BITS == 2) {
+                const int sh = 4 * (rho % 2);  // tokens 2(q%2) + e of each quartet
+                b0 = (x >> sh) & 0x03030303u;
+                b1 = (x >> (sh + 2)) & 0x03030303u;
+            } else {
+                b0 = x & 0x0F0F0F0Fu;
+                b1 = (x >> 4) & 0x0F0F0F0Fu;
             }
-            // rows 4rho + d: the three digits of query rho, channel 16vt + n
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                float comb;
-                if constexpr (BITS == 2) {
-                    comb = (float)digit_sum3(c[i][0], c[i][1], c[i][2]);  // |digit sums| < 2^14: no overflow
-                } else {
-                    comb = fmaf((float)c[i][2], 65536.0f, fmaf((float)c[i][1], 256.0f, (float)c[i][0]));
-                }
-                o_blk[v0 + i] = fmaf(comb, vs, o_blk[v0 + i]);
-            }
+            const long av = (long)(((uint64_t)pa.y << 32) | pa.x);
+            const long bv = (long)(((uint64_t)b1 << 32) | b0);
+            acc_v[vt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, acc_v[vt], 0, 0, 0);
         }
         wave_lds_order();
     };
@@ -556,10 +565,11 @@ __global__ __launch_bounds__(64 * NWAVES, BITS == 2 ? 3 : 2) void attend_gqa_ker
             wave_lds_order();  // the slot's reads stay before the operand stores into it
             int ev;
             key_math(r, ev, k);
-            value_math(r, ev, k);
+            value_math(r, k);
             if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
         }
     }
+    fold();
 
     for (int ck = NWAVES - 1 - wave; ck < rc; ck += NWAVES) {
         uint4 kraw[TPL][2];

@@ -128,9 +128,14 @@ def test_split_invariance_and_determinism(Hq, bits):
         assert np.array_equal(a, b), "attention is not bitwise deterministic"
         outs[(n, n_split, bps)] = a
     ref = list(outs.values())[0]
+    # The four-query kernel takes its value weights' digits against a running
+    # power-of-two bound, up to 2^2 above a block's own bound, so the split
+    # count (which blocks a wave sees) moves a weight's rounding by up to
+    # 2^-20 of its bound; the vector kernel's fp32 sums differ only in order.
+    tol = 5e-5 if Hq // Hkv == 4 else 1e-5
     for key, a in outs.items():
         rel = np.abs(a - ref).max() / np.abs(ref).max()
-        assert rel < 1e-5, (key, rel)
+        assert rel < tol, (key, rel)
     oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T)
     oc.append(k, v)
     oc.flush()
