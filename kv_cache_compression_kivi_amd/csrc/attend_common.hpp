@@ -97,6 +97,52 @@ __device__ __forceinline__ float wave_sum(float x) { return rows_sum(sum_cols<16
 // (and the loads before later stores); LDS executes a wave's accesses in order.
 __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Maxima of non-negative floats taken on their bit patterns, which order
+// like unsigned integers (no NaN quieting, unlike fmaxf): over each row of 16
+// lanes, and over the wave (every lane holds the result).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t row_max_bits(uint32_t x) {
+    x = umax(x, dpp_u<kSwap1>(x));
+    x = umax(x, dpp_u<kSwap2>(x));
+    x = umax(x, dpp_u<kHalfMirror>(x));
+    return umax(x, dpp_u<kMirror>(x));
+}
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+    x = row_max_bits(x);
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = umax(r[0], r[1]);
+    auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return umax(t[0], t[1]);
+}
+
+// The 23-bit integer Q = rint(a b 2^-e) (|a b| < 2^(22+e)) as three signed
+// bytes, (Q + 0x808080) ^ 0x808080 in bits 0..23. One fma with the magic
+// 1.5 2^(23+e) rounds the exact product to a multiple of 2^e (ties to even),
+// so the low 24 bits of the result's encoding hold (e & 1) << 23 (the
+// exponent's low bit, as 150 + e has the parity of e) above 2^22 + Q; the
+// bias 0x408080 - ((e & 1) << 23) turns them into Q + 0x808080.
+struct DigitScale {
+    float magic;
+    uint32_t bias;
+};
+// e must be the same in every lane. Both values stay whole scalars: folded
+// into the adds of digits3, the bias would cost a second add per value.
+__device__ __forceinline__ DigitScale digit_scale(int e) {
+    const float magic = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(ldexpf(1.5f, 23 + e))));
+    uint32_t bias = __builtin_amdgcn_readfirstlane(0x408080u - ((uint32_t)(e & 1) << 23));
+    asm("" : "+s"(bias));  // opaque: not reassociated into the adds
+    return {magic, bias};
+}
+__device__ __forceinline__ uint32_t digits3(float a, float b, DigitScale ds) {
+    return (__float_as_uint(fmaf(a, b, ds.magic)) + ds.bias) ^ 0x808080u;
+}
+
 // ------------------------------------------------------------ block records
 
 // Record layout of one key block (see kivi.h): kcode [G][W] (token-major),
