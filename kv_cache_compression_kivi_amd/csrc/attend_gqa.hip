@@ -13,16 +13,19 @@
 //   scores  S[g][t] = sum_c q~[g][c] kcode[t][c]   (q~ = q s, per block and channel)
 //   values  O[g][c] = sum_t p~[g][t] vcode[t][c]   (p~ = p s_t, per token and value group)
 // The codes are int8 operands as they are. q~ and p~ are rounded to 23-bit
-// integers against a per-block power of two (|q| < 2^Eq per query, s < 2^Es
-// and s_t < 2^Ev per block; p <= 1) and split into three signed 8-bit
-// digits, so every product and sum is exact in int32; the only rounding is
-// that of q~ and p~ to 2^-22 of their bounds. The digits of query (or weight)
+// integers against powers of two (|q| < 2^Eq per query and s < 2^Es per
+// block for q~; for p~, p <= 1 and a running bound 2^ew on s_t, within 2^2 of
+// the block's own) and split into three signed 8-bit digits, so every product
+// and sum is exact in int32; the only rounding is that of q~ and p~ to 2^-22
+// of their bounds. The digits of query (or weight)
 // row g sit in rows 4g .. 4g + 2 of a 16-row tile operand; row 4g + 3 is never
 // written: its products land in result row 4g + 3, which is never read.
 // Scores: v_mfma_i32_16x16x64_i8, 16 rows (query, digit) x 16 tokens x 64
 // channels, so a lane's four results are the digit sums of one query and one
 // token (lane / 16 and lane % 16).
-// Values: v_mfma_i32_16x16x32_i8, 16 rows x 16 channels x the block's 32 tokens.
+// Values: v_mfma_i32_16x16x32_i8, 16 rows x 16 channels x the block's 32 tokens,
+// accumulated in int32 from block to block and folded into fp32 only when
+// the running maximum or the weights' bound moves.
 // The fp16 residual runs on the vector units as in attend_kernel.
 #include <hip/hip_runtime.h>
 
@@ -213,8 +216,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     auto vs_off = [&](int tt, int r) {
         return L::vsz + ((16 * tt + gqa_row_token<BITS>(4 * gl + r)) * NG + dq) * 8;
     };
-    // staged blocks: NS slots per wave (LDS for three 4-wave work-groups per
-    // CU at b = 2, two at b = 4)
+    // staged blocks: NS slots per wave (two 4-wave work-groups per CU, set by
+    // registers; measured on MI355X: no faster with 4 slots)
     constexpr int NS = 3;
     constexpr int NL = L::bytes / 1024;  // staging loads per block
     static_assert(L::bytes % 1024 == 0, "a record is a whole number of 1 KB wave loads");
@@ -306,7 +309,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     // running state, two parts merged at the end. Residual (vector layout): m,
     // l_res and o_res per query. Blocks (matrix layout, query rho = lane / 16):
     // running max m_b, weight sum l_b of this lane's tokens, value-zero sum z_b
-    // of group dq over the tokens of quad gl, o_blk[vt] for channel 16vt + n.
+    // of group dq over the tokens of quad gl, o_blk[vt] (folded from acc_v) for
+    // channel 16vt + n.
     float m[QG], l_res[QG], o_res[QG][CPV * NACC], o_blk[VT];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     const int slot0 = (int)(a.n_quant % g.ring_slots);
     if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0) write_new_token<D>(a, u, rbase);
     // scores, softmax, weight digits of one block
-    auto key_math = [&](const R& r, int& ev, int k_slot) {
+    auto key_math = [&](const R& r, int k_slot) {
         // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
         uint32_t smax = 0;  // scales are positive: their bit patterns order like the values
 #pragma unroll
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) vmax = umax(vmax, __float_as_uint(r.vsz[tt][r2].x));
-        ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
+        const int ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
         // the weights' exponent follows the block's bound when it grows, or
         // when the bound falls more than 2 below it (at most 2 of the digits'
         // 22 bits left unused)
@@ -483,7 +487,6 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
         }
         wave_lds_order();
     };
-    // values of one block: O[g][c] += 2^(Ev - 22) sum_t P[g][t] code[t][c]
     // values of one block: acc_v[vt] += sum_t P[g][t] code[t][c] (digit rows)
     auto value_math = [&](const R& r, int k_slot) {
 #pragma unroll
@@ -517,8 +520,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
             R r;
             read_slot(k, r);
             wave_lds_order();  // the slot's reads stay before the operand stores into it
-            int ev;
-            key_math(r, ev, k);
+            key_math(r, k);
             value_math(r, k);
             if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
         }
