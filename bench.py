@@ -71,6 +71,19 @@ def prefill_bytes(units, d, bits, T, n_quant):
     return units * (T * 4 * d + n_quant * bytes_per_quant_token(d, bits) + (T - n_quant) * 4 * d)
 
 
+def row_groups(c):
+    """A cache's rows grouped by their counters: [(n_tokens, n_quant, n_resid, rows)]."""
+    from collections import Counter
+    cnt = Counter(c.row_state(b) for b in range(c.cfg.batch))
+    return [(nt, nq, nr, w) for (nt, nq, nr), w in sorted(cnt.items())]
+
+
+def cache_attend_bytes(c):
+    """Algorithmic bytes of one decode attention over the cache's current rows."""
+    Hkv, Hq, d, bits = c.cfg.n_kv_heads, c.cfg.n_q_heads, c.cfg.head_dim, c.cfg.bits
+    return sum(attend_bytes(Hkv * w, Hq * w, d, bits, nq, nr) for _, nq, nr, w in row_groups(c))
+
+
 # ---------------------------------------------------------------- helpers
 
 ATTEND_SOURCES = ("attend.hip", "attend_gqa.hip", "attend_common.hpp", "split.hpp", "launch.hpp", "planner.hpp")
@@ -153,10 +166,8 @@ def _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows
     n_caches = len(caches)
     if n_att is None:
         n_att = max(2 * n_caches, min(200, 20 * n_caches))
-    att_bytes = 0
-    for i in range(n_att):
-        nt, nq, nr = caches[i % n_caches].state()
-        att_bytes += attend_bytes(units, rows, d, caches[i % n_caches].cfg.bits, nq, nr)
+    per_cache = [cache_attend_bytes(c) for c in caches]
+    att_bytes = sum(per_cache[i % n_caches] for i in range(n_att))
     for i in range(min(n_caches, 8)):  # warm the launch path
         caches[i].attend(q0, out=out)
     torch.cuda.synchronize()
@@ -179,7 +190,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_7b_layer",
-                    choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack"])
+                    choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
+                             "gqa_ragged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--profile", action="store_true",
@@ -195,7 +207,7 @@ def main():
     import torch
 
     import kv_cache_compression_kivi_amd as kv
-    from kivi_inputs import CONFIGS, KVWorkload
+    from kivi_inputs import CONFIGS, KVWorkload, row_lengths
 
     kv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -207,9 +219,12 @@ def main():
     layer_bits = cfg.get("layer_bits", [cfg.get("bits", 2)] * layers)
     q_dtype = torch.bfloat16 if cfg.get("q_dtype") == "bf16" else torch.float16
     total_steps = args.warmup + args.steps
+    # a serving batch: each sequence at its own seeded length (appended with kivi_append_rows)
+    lens = row_lengths(B, cfg["ragged"][0], cfg["ragged"][1], cfg["seed"]) if cfg.get("ragged") else [T] * B
 
     # one cache per layer; rotate over copies when a step's working set would sit in the Infinity Cache
-    per_step_bytes = sum(attend_bytes(units, rows, d, b, ((T - 128) // 32) * 32, 128) for b in layer_bits)
+    per_step_bytes = sum(attend_bytes(Hkv, Hq, d, b, max(0, (t - 128) // 32 * 32), t - max(0, (t - 128) // 32 * 32))
+                         for b in layer_bits for t in lens)
     n_rot = 1 if per_step_bytes >= (1 << 30) else min(16, int(-(-(1 << 30) // per_step_bytes)))
     n_caches = n_rot * layers
     max_tokens = T + -(-total_steps // n_rot) + 64
@@ -224,7 +239,10 @@ def main():
             wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], layer=layer + 1000 * r, device=dev)
             k, v = wl.kv(0, T)
             c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev)
-            c.append(k, v)
+            if cfg.get("ragged"):
+                c.append_rows(k, v, lens)
+            else:
+                c.append(k, v)
             c.flush()
             caches.append(c)
             if r == 0 and layer in (0, layers - 1):
@@ -266,20 +284,22 @@ def main():
     # the bytes of each step follow from the host counters alone: replay the
     # counter arithmetic before timing (checked against the caches afterwards)
     bytes_total = 0
-    sim_state = [c.state() for c in caches]
+    sim_state = [row_groups(c) for c in caches]
     for i in range(args.warmup, total_steps):
         r = i % n_rot
         for layer in range(layers):
             ci = r * layers + layer
-            nt, nq, nr = sim_state[ci]
-            nt, nr = nt + 1, nr + 1
-            b = append_bytes(units, d, 1)
-            if nr >= 128 + 32:
-                b += flush_bytes(units, d, layer_bits[layer], 32)
-                nq, nr = nq + 32, nr - 32
-            b += attend_bytes(units, rows, d, layer_bits[layer], nq, nr)
-            bytes_total += b
-            sim_state[ci] = (nt, nq, nr)
+            groups = []
+            for nt, nq, nr, w in sim_state[ci]:
+                nt, nr = nt + 1, nr + 1
+                b = append_bytes(Hkv * w, d, 1)
+                if nr >= 128 + 32:
+                    b += flush_bytes(Hkv * w, d, layer_bits[layer], 32)
+                    nq, nr = nq + 32, nr - 32
+                b += attend_bytes(Hkv * w, Hq * w, d, layer_bits[layer], nq, nr)
+                bytes_total += b
+                groups.append((nt, nq, nr, w))
+            sim_state[ci] = groups
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total_steps):
@@ -287,7 +307,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for ci, c in enumerate(caches):
-        assert c.state() == sim_state[ci], (c.state(), sim_state[ci])
+        assert row_groups(c) == sorted(sim_state[ci]), (row_groups(c), sim_state[ci])
     ms_per_step = wall / args.steps * 1e3
     value = bytes_total / wall / 1e9
 
@@ -314,40 +334,44 @@ def main():
         k, v = prefill_inputs.get(layer, prefill_inputs[0])
         c.reset()
         pf_ev[i][0].record(stream)
-        c.append(k, v)
+        if cfg.get("ragged"):
+            c.append_rows(k, v, lens)
+        else:
+            c.append(k, v)
         c.flush()
         pf_ev[i][1].record(stream)
-        nt, nq, nr = c.state()
-        pf_bytes += prefill_bytes(units, d, c.cfg.bits, T, nq)
+        pf_bytes += sum(prefill_bytes(Hkv * w, d, c.cfg.bits, nt, nq) for nt, nq, _, w in row_groups(c))
     torch.cuda.synchronize()
     pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
-    pf_tok_s = n_pf * B * Hkv * T / (pf_ms * 1e-3)
+    pf_tok_s = n_pf * Hkv * sum(lens) / (pf_ms * 1e-3)
     pf_gbs = pf_bytes / (pf_ms * 1e-3) / 1e9
 
     # single-token appends (ring writes only) and one 32-token flush, on the
     # caches just prefilled: n_res = R there, so 32 appends fit before the ring
-    # is full and the flush then quantizes exactly one group
-    ap_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_pf)]
-    n_ap = 32
-    for i in range(n_pf):
-        h = handles[i]
-        assert caches[i].state()[2] == 128
-        ap_ev[i][0].record(stream)
-        for t in range(n_ap):
-            kp, vp = kvp[t % pool]
-            rc = lib.kivi_append(h, kp, vp, 1, sp)
+    # is full and the flush then quantizes exactly one group (rows at one length only)
+    ap_us = fl_us = fl_gbs = None
+    if not cfg.get("ragged"):
+        ap_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_pf)]
+        n_ap = 32
+        for i in range(n_pf):
+            h = handles[i]
+            assert caches[i].state()[2] == 128
+            ap_ev[i][0].record(stream)
+            for t in range(n_ap):
+                kp, vp = kvp[t % pool]
+                rc = lib.kivi_append(h, kp, vp, 1, sp)
+                if rc != 0:
+                    raise kv.KiviError(rc, kv.kivi_last_error())
+            ap_ev[i][1].record(stream)
+            rc = lib.kivi_flush(h, sp, ctypes.byref(nfl))
             if rc != 0:
                 raise kv.KiviError(rc, kv.kivi_last_error())
-        ap_ev[i][1].record(stream)
-        rc = lib.kivi_flush(h, sp, ctypes.byref(nfl))
-        if rc != 0:
-            raise kv.KiviError(rc, kv.kivi_last_error())
-        ap_ev[i][2].record(stream)
-        assert nfl.value == 32, nfl.value
-    torch.cuda.synchronize()
-    ap_us = sum(e[0].elapsed_time(e[1]) for e in ap_ev) * 1e3 / (n_pf * n_ap)
-    fl_us = sum(e[1].elapsed_time(e[2]) for e in ap_ev) * 1e3 / n_pf
-    fl_gbs = sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in range(n_pf)) / n_pf / (fl_us * 1e-6) / 1e9
+            ap_ev[i][2].record(stream)
+            assert nfl.value == 32, nfl.value
+        torch.cuda.synchronize()
+        ap_us = sum(e[0].elapsed_time(e[1]) for e in ap_ev) * 1e3 / (n_pf * n_ap)
+        fl_us = sum(e[1].elapsed_time(e[2]) for e in ap_ev) * 1e3 / n_pf
+        fl_gbs = sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in range(n_pf)) / n_pf / (fl_us * 1e-6) / 1e9
 
     traffic = _traffic_from_profile(args.workload)
     plan = caches[0].plan_attend()
@@ -369,17 +393,20 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_kv_heads": Hkv, "n_q_heads": Hq, "head_dim": d,
-                   "tokens": T, "bits": layer_bits if layers > 1 else layer_bits[0], "layers": layers,
+                   "tokens": T if not cfg.get("ragged") else {"per_row": "uniform over [%d, %d]" % tuple(cfg["ragged"]),
+                                                              "min": min(lens), "max": max(lens),
+                                                              "mean": round(sum(lens) / B, 1)},
+                   "bits": layer_bits if layers > 1 else layer_bits[0], "layers": layers,
                    "k_block": 32, "v_group": 32, "residual": 128, "q_dtype": str(q_dtype).replace("torch.", ""),
                    "step": "append 1 token + flush when due + decode attention, per layer",
                    "rotating_caches": n_rot},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "quantize_append_tokens_per_s": round(pf_tok_s, 1),
         "quantize_append_gbs": round(pf_gbs, 2),
-        "append_1_token_us": round(ap_us, 3),
-        "append_1_token_tokens_per_s": round(units / (ap_us * 1e-6), 1),
-        "flush_32_tokens_us": round(fl_us, 3),
-        "flush_32_tokens_gbs": round(fl_gbs, 2),
+        "append_1_token_us": round(ap_us, 3) if ap_us else None,
+        "append_1_token_tokens_per_s": round(units / (ap_us * 1e-6), 1) if ap_us else None,
+        "flush_32_tokens_us": round(fl_us, 3) if fl_us else None,
+        "flush_32_tokens_gbs": round(fl_gbs, 2) if fl_gbs else None,
         "roofline": {
             "bound": "hbm",
             "kernel": attend_kernel_name,

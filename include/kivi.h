@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KIVI_ABI_VERSION 1
+#define KIVI_ABI_VERSION 2
 
 typedef enum {
     KIVI_OK = 0,
@@ -49,8 +49,12 @@ typedef enum {
     KIVI_E_CAPACITY = -4,    /* the append would exceed max_tokens */
     KIVI_E_EMPTY = -5,       /* attention on a cache holding no token */
     KIVI_E_DEVICE = -6,      /* a HIP launch failed (message from hipGetErrorString) */
-    KIVI_E_STATE = -7        /* the handle saw an earlier device failure */
+    KIVI_E_STATE = -7,       /* the handle saw an earlier device failure */
+    KIVI_E_RAGGED = -8       /* the call needs every sequence to hold the same number of tokens */
 } kivi_status;
+
+/* Largest batch whose sequences may hold different numbers of tokens. */
+#define KIVI_MAX_RAGGED_BATCH 128
 
 enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
 
@@ -58,7 +62,11 @@ enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
  * Supported: head_dim in {64, 128, 256}; bits in {2, 4}; k_block = v_group = 32;
  * residual a multiple of k_block (0 allowed); n_q_heads a multiple of
  * n_kv_heads; max_tokens >= 1; max_splits = 0 (library default, 256) or
- * 2..4096. Every sequence of the batch holds the same number of tokens. */
+ * 2..4096. Each sequence (batch row) keeps its own counters: kivi_append and
+ * kivi_decode_step add the same number of tokens to every row, while
+ * kivi_append_rows and kivi_reset_row let rows differ in length (a batch of
+ * at most KIVI_MAX_RAGGED_BATCH rows then). Each row follows the same rules
+ * (residual ring, flushes) as a batch of one. */
 typedef struct {
     int32_t batch;       /* B */
     int32_t n_kv_heads;  /* Hkv; a "unit" is one (batch row, KV head): unit = b * Hkv + h */
@@ -137,8 +145,24 @@ int kivi_cache_reset(kivi_cache* cache);
  * would exceed max_tokens. */
 int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, void* stream);
 
-/* Quantize the oldest floor((n_resid - R) / G) * G residual tokens (none if
- * n_resid < R + G); *n_flushed (may be NULL) receives that count. */
+/* Append ntok[b] >= 0 tokens to sequence b, each row by the rules of
+ * kivi_append. k, v: device fp16 [B][Hkv][max_ntok][d], contiguous; row b's
+ * tokens are its first ntok[b] of the max_ntok slots. ntok: host array of B
+ * entries, each in [0, max_ntok]. For prefilling sequences of different
+ * lengths, or one row (the others 0) when a new sequence takes a freed row.
+ * KIVI_E_CAPACITY if a row would exceed max_tokens; KIVI_E_UNSUPPORTED if the
+ * rows would differ in length with batch > KIVI_MAX_RAGGED_BATCH. */
+int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int32_t* ntok, int32_t max_ntok,
+                     void* stream);
+
+/* Empty sequence `row` (host counters only; launches nothing), so that a new
+ * sequence can take the row. KIVI_E_UNSUPPORTED if the rows would then differ
+ * in length with batch > KIVI_MAX_RAGGED_BATCH. */
+int kivi_reset_row(kivi_cache* cache, int32_t row);
+
+/* Quantize, in every row, the oldest floor((n_resid - R) / G) * G residual
+ * tokens (none if n_resid < R + G); *n_flushed (may be NULL) receives the
+ * largest count of a row. */
 int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
 
 /* Decode attention of one query per head over every cached token:
@@ -147,23 +171,28 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
  * i / (Hq / Hkv). q: device [B][Hq][d] of q_dtype (KIVI_F16 / KIVI_BF16);
  * out: device float32 [B][Hq][d]. Split-K over key blocks, then a
  * log-sum-exp merge of the splits. Concurrent calls on one cache (several
- * streams) are not allowed: they share the split partials.
- * KIVI_E_EMPTY on an empty cache. */
+ * streams) are not allowed: they share the split partials. Each row attends
+ * over its own tokens. KIVI_E_EMPTY if a sequence holds no token. */
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
 
 /* One decode step in one call: kivi_append of one token per sequence (k, v:
  * device fp16 [B][Hkv][1][d]), then kivi_flush if a whole group of G tokens
  * lies beyond the newest R (so the residual cycles through R .. R+G-1 tokens
  * at attention time), then kivi_attend_decode. *n_flushed (may be NULL)
- * receives the tokens the flush quantized. Same contract and errors as the
- * three calls; validation of all three happens before the first launch. */
+ * receives the largest count the flush quantized in a row. Same contract and
+ * errors as the three calls; validation of all three happens before the first
+ * launch. */
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
                      void* stream, int32_t* n_flushed);
 
-/* Current counters. */
+/* Current counters (KIVI_E_RAGGED when the rows differ: see kivi_query_row). */
 int kivi_cache_query(const kivi_cache* cache, kivi_state* state);
 
-/* Counters the cache would have after kivi_append(ntok) (host only). */
+/* Current counters of sequence `row`. */
+int kivi_query_row(const kivi_cache* cache, int32_t row, kivi_state* state);
+
+/* Counters the cache would have after kivi_append(ntok) (host only;
+ * KIVI_E_RAGGED when the rows differ). */
 int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after);
 
 /* Split plan kivi_attend_decode would use now: *n_split work-groups per

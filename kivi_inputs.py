@@ -29,6 +29,10 @@ Draw order, for a workload with seed S and layer L:
      randn(B, Hq, d).
 Chunks are drawn independently, so a prefill of T tokens followed by decode
 tokens T, T+1, ... is reproducible from (S, L) and the positions alone.
+
+Batches whose sequences differ in length (a serving batch) draw one length per
+batch row, uniform over the integers [T_min, T_max], from a generator seeded
+with hash(S, 3); row b then holds tokens [0, len[b]) of its chunk draws.
 """
 
 from __future__ import annotations
@@ -95,7 +99,14 @@ class KVWorkload:
         return q.to(dtype).contiguous()
 
 
-# The five workloads the method is measured on. `T` is the number of tokens
+def row_lengths(batch: int, t_min: int, t_max: int, seed: int) -> list:
+    """Seeded per-row sequence lengths, uniform over [t_min, t_max]."""
+    g = torch.Generator()
+    g.manual_seed(_mix(seed, 3))
+    return [int(x) for x in torch.randint(t_min, t_max + 1, (batch,), generator=g)]
+
+
+# The workloads the method is measured on. `T` is the number of tokens
 # appended before the decode attention; "prefill" means append(T) then flush.
 CONFIGS = {
     "tiny": dict(batch=1, n_kv_heads=1, n_q_heads=1, head_dim=128, T=1024, bits=2, seed=1),
@@ -105,4 +116,8 @@ CONFIGS = {
                           decode_steps=256),
     "full_stack": dict(batch=128, n_kv_heads=8, n_q_heads=32, head_dim=128, T=4096, seed=5,
                        layers=32, layer_bits=[2] * 16 + [4] * 16, q_dtype="bf16"),
+    # A serving batch: the GQA shape above with each sequence at its own length,
+    # uniform over [512, 8192] tokens (T is the longest possible).
+    "gqa_ragged": dict(batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=6,
+                       ragged=(512, 8192)),
 }

@@ -18,6 +18,7 @@ from ._native import (  # noqa: F401
     KiviError,
     kivi_abi_version,
     kivi_append,
+    kivi_append_rows,
     kivi_attend_decode,
     kivi_cache_bytes,
     kivi_cache_create,
@@ -32,6 +33,8 @@ from ._native import (  # noqa: F401
     kivi_layout,
     kivi_plan_append,
     kivi_plan_attend,
+    kivi_query_row,
+    kivi_reset_row,
     kivi_set_attend_splits,
     kivi_state,
     library_path,

@@ -13,7 +13,7 @@ KIVI_BF16 = 1
 
 STATUS = {
     0: "KIVI_OK", -1: "KIVI_E_INVAL", -2: "KIVI_E_UNSUPPORTED", -3: "KIVI_E_NOMEM",
-    -4: "KIVI_E_CAPACITY", -5: "KIVI_E_EMPTY", -6: "KIVI_E_DEVICE", -7: "KIVI_E_STATE",
+    -4: "KIVI_E_CAPACITY", -5: "KIVI_E_EMPTY", -6: "KIVI_E_DEVICE", -7: "KIVI_E_STATE", -8: "KIVI_E_RAGGED",
 }
 
 
@@ -68,6 +68,9 @@ _SIGS = {
     "kivi_plan_attend": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "kivi_set_attend_splits": (ctypes.c_int, [_P, ctypes.c_int32]),
     "kivi_decode_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]),
+    "kivi_append_rows": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _P]),
+    "kivi_reset_row": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "kivi_query_row": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(kivi_state)]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -136,6 +139,22 @@ def kivi_cache_reset(h: int) -> None:
 def kivi_append(h: int, k_ptr: int, v_ptr: int, ntok: int, stream: int = 0) -> None:
     _check(load_library().kivi_append(ctypes.c_void_p(h), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
                                       ntok, ctypes.c_void_p(stream)))
+
+
+def kivi_append_rows(h: int, k_ptr: int, v_ptr: int, ntok, max_ntok: int, stream: int = 0) -> None:
+    arr = (ctypes.c_int32 * len(ntok))(*[int(x) for x in ntok])
+    _check(load_library().kivi_append_rows(ctypes.c_void_p(h), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                           arr, max_ntok, ctypes.c_void_p(stream)))
+
+
+def kivi_reset_row(h: int, row: int) -> None:
+    _check(load_library().kivi_reset_row(ctypes.c_void_p(h), row))
+
+
+def kivi_query_row(h: int, row: int) -> kivi_state:
+    st = kivi_state()
+    _check(load_library().kivi_query_row(ctypes.c_void_p(h), row, ctypes.byref(st)))
+    return st
 
 
 def kivi_flush(h: int, stream: int = 0) -> int:
@@ -239,6 +258,22 @@ class KiviCache:
     def append(self, k, v, stream=None):
         self._check_kv(k, v)
         kivi_append(self.handle, k.data_ptr(), v.data_ptr(), int(k.shape[2]), self._stream(stream))
+
+    def append_rows(self, k, v, ntok, stream=None):
+        """Append ntok[b] tokens to sequence b: k, v are [batch, n_kv_heads, max_ntok,
+        head_dim] fp16 and row b's tokens are its first ntok[b] slots."""
+        self._check_kv(k, v)
+        ntok = [int(x) for x in ntok]
+        if len(ntok) != self.cfg.batch:
+            raise ValueError(f"ntok must have {self.cfg.batch} entries, got {len(ntok)}")
+        kivi_append_rows(self.handle, k.data_ptr(), v.data_ptr(), ntok, int(k.shape[2]), self._stream(stream))
+
+    def reset_row(self, row):
+        kivi_reset_row(self.handle, row)
+
+    def row_state(self, row):
+        st = kivi_query_row(self.handle, row)
+        return st.n_tokens, st.n_quant, st.n_resid
 
     def flush(self, stream=None) -> int:
         return kivi_flush(self.handle, self._stream(stream))

@@ -207,7 +207,7 @@ constexpr int attend_prefetch(int D, int QG) { return 2 * attend_pair(D, QG); }
 // channels [L*CPV, L*CPV + CPV) over all 32 tokens of a chunk, with the
 // chunk's weights passed through a wave-private LDS slot (one row of 32
 // weights per value group, the group's scale and the code-half factor folded in).
-template <int D, int BITS, int QG, int NWAVES>
+template <int D, int BITS, int QG, int NWAVES, bool RAGGED>
 __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a) {
     constexpr int CW = attend_cw(D);
     using B = BlockRegs<D, BITS, CW>;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const int wgrp = w * CW / kVG;                 // the value group of column w
     const bool wlead = w * CW % kVG == 0;          // writes its group's value weights
     const int split = blockIdx.x;
-    const int64_t u = blockIdx.y;
+    const int64_t u = dispatch_unit<RAGGED>(a, blockIdx.y);
     const int group = g.n_q_heads / g.n_kv_heads;
     const int64_t b = u / g.n_kv_heads;
     const int h = (int)(u % g.n_kv_heads);
@@ -242,12 +242,16 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const float scale_q = ldexpf(a.scale_log2, 24);  // for scores summed in units of 2^-24
 
     // this work-group's and this wave's share of the tokens (kernel arguments only)
-    const int64_t nres = a.n_tokens - a.n_quant;
+    // this unit's counters (its batch row's, when the rows differ in length)
+    const RowCounts cnt = row_counts<RAGGED>(a, b);
+    if constexpr (RAGGED)
+        if (split >= cnt.n_split) return;  // an idle split of a shorter row (the whole work-group)
+    const int64_t nres = cnt.n_tokens - cnt.n_quant;
     const int64_t nrc = (nres + kG - 1) / kG;
     const int64_t cost = kResidualChunkCost;
     int64_t b0, b1;
-    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
-    const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
+    split_range(cnt.n_blocks, nrc, cost, cnt.n_split, split, &b0, &b1);
+    const int rc = (int)(split == cnt.n_split - 1 ? nrc : 0);
     // this wave's key blocks: j0, j0 + NWAVES, ... below j1 (round robin). Block
     // indices of a unit fit in 32 bits (its records are one buffer of < 4 GiB);
     // readfirstlane keeps them, and each block offset, in scalar registers
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     // the first NP key blocks go in flight before anything waits
     constexpr int PF = attend_prefetch(D, QG);
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
-    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
+    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)cnt.n_blocks * L::bytes);
     const LaneOffsets lo = lane_offsets<D, BITS, CW>(lane, w, tl);
     B rr[PF];
 #pragma unroll
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     // work left after it lengthens the tail); a wave's first chunk is loaded now
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
-    const int slot0 = (int)(a.n_quant % g.ring_slots);
+    const int slot0 = (int)(cnt.n_quant % g.ring_slots);
     const int ck0 = NWAVES - 1 - wave;  // chunk ck goes to wave NWAVES - 1 - ck % NWAVES
     constexpr int VRW = (CPV + 1) / 2;  // words of fp16 value pairs per token
     uint4 kraw[TPL][CW / 8];            // key rows of this lane's tokens, column w
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
             slot -= slot >= ring ? ring : 0;
             // the token appended by this call comes from its input row
-            const uint4* kp = a.n_quant + idx == a.t_new
+            const uint4* kp = cnt.n_quant + idx == cnt.t_new
                                   ? reinterpret_cast<const uint4*>(a.k_new + u * D + CW * w)
                                   : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 2 * CW * w);
 #pragma unroll
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
             const int idx = ck * kG + t;
             int slot = slot0 + (idx < (int)nres ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            const uint8_t* vp = a.n_quant + idx == a.t_new
+            const uint8_t* vp = cnt.n_quant + idx == cnt.t_new
                                     ? reinterpret_cast<const uint8_t*>(a.v_new + u * D + cv0)
                                     : rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
             if constexpr (CPV == 1) {
@@ -310,8 +314,8 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     };
     constexpr bool kEarly = D <= 128;  // d = 256: a chunk and the first blocks take too many registers
     if (kEarly && ck0 < rc) load_chunk(ck0);
-    if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0)
-        write_new_token<D>(a, u, rbase);
+    if (cnt.t_new >= 0 && split == cnt.n_split - 1 && blockIdx.z == 0 && wave == 0)
+        write_new_token<D>(a, u, cnt.t_new, rbase);
 
     for (int idx = threadIdx.x; idx < QG * D; idx += NT) {
         const uint16_t v = a.q[row0 * D + idx];
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 // order. The splits' (m, l, o) are read 16 at a time in one round of loads
 // (a second round waiting on the first would double the kernel's latency);
 // a group's maximum rescales the sums of the groups before it.
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
     constexpr int CH = 16;
     const CacheGeom& g = a.g;
@@ -593,12 +597,13 @@ __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
     const int c = threadIdx.x;
     const size_t stride = g.partial_stride / 4;
     const float* rb = reinterpret_cast<const float*>(g.base + g.off_partial) + row * g.max_splits * stride;
+    const int n_split = (int)row_counts<RAGGED>(a, (int64_t)(row / g.n_q_heads)).n_split;  // this batch row's splits
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < a.n_split; s0 += CH) {
+    for (int s0 = 0; s0 < n_split; s0 += CH) {
         float ms[CH], ls[CH], os[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const bool in = s0 + i < a.n_split;
+            const bool in = s0 + i < n_split;
             const float* r = rb + (size_t)(in ? s0 + i : s0) * stride;  // split s0 stands in past the end
             ms[i] = r[D];
             ls[i] = r[D + 1];
@@ -630,7 +635,11 @@ __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
 template <int D>
 hipError_t merge_splits(hipError_t e, const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess || a.n_split == 1) return e;
-    combine_kernel<D><<<(unsigned)((int64_t)a.g.batch * a.g.n_q_heads), D, 0, s>>>(a);
+    const dim3 grid((unsigned)((int64_t)a.g.batch * a.g.n_q_heads));
+    if (a.rows.n)
+        combine_kernel<D, true><<<grid, D, 0, s>>>(a);
+    else
+        combine_kernel<D, false><<<grid, D, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -638,7 +647,10 @@ template <int D, int BITS, int QG, int NWAVES>
 hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
     const int group = a.g.n_q_heads / a.g.n_kv_heads;
     const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / QG));
-    attend_kernel<D, BITS, QG, NWAVES><<<grid, 64 * NWAVES, 0, s>>>(a);
+    if (a.rows.n)
+        attend_kernel<D, BITS, QG, NWAVES, true><<<grid, 64 * NWAVES, 0, s>>>(a);
+    else
+        attend_kernel<D, BITS, QG, NWAVES, false><<<grid, 64 * NWAVES, 0, s>>>(a);
     return merge_splits<D>(hipGetLastError(), a, s);
 }
 

@@ -185,13 +185,13 @@ __device__ __forceinline__ float half_lo(uint32_t x) {
 }
 __device__ __forceinline__ float half_hi(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)); }
 
-// Copies the token appended by this call (a.t_new) of unit u into its ring
-// slot: 16 bytes per lane, key row then value row (one wave).
+// Copies the token t_new appended by this call of unit u into its ring slot:
+// 16 bytes per lane, key row then value row (one wave).
 template <int D>
-__device__ __forceinline__ void write_new_token(const AttendArgs& a, int64_t u, const uint8_t* rbase) {
+__device__ __forceinline__ void write_new_token(const AttendArgs& a, int64_t u, int64_t t_new, const uint8_t* rbase) {
     constexpr int CH = D / 8;  // 16-byte chunks per fp16 row
     const int lane = threadIdx.x & 63;
-    const int slot = (int)(a.t_new % a.g.ring_slots);
+    const int slot = (int)(t_new % a.g.ring_slots);
     for (int i = lane; i < 2 * CH; i += 64) {
         const int kv = i / CH, c = i % CH;
         const uint4 x = reinterpret_cast<const uint4*>((kv ? a.v_new : a.k_new) + u * D)[c];

@@ -152,7 +152,7 @@ __device__ __forceinline__ void wait_staged(int later) {
 
 // Two 4-wave work-groups per CU (up to 256 VGPRs a lane: the value digit
 // sums stay in matrix-core accumulators across blocks).
-template <int D, int BITS, int NWAVES>
+template <int D, int BITS, int NWAVES, bool RAGGED>
 __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const AttendArgs a) {
     constexpr int QG = 4;
     using B = BlockRegs<D, BITS>;
@@ -177,24 +177,28 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     const int n = lane & 15, rho = lane >> 4;
     const int gl = n >> 2, dq = n & 3;  // the query of score columns 4gl .. 4gl+3, and a value group
     const int split = blockIdx.x;
-    const int64_t u = blockIdx.y;
+    const int64_t u = dispatch_unit<RAGGED>(a, blockIdx.y);
     const int group = g.n_q_heads / g.n_kv_heads;
     const int64_t b = u / g.n_kv_heads;
     const int h = (int)(u % g.n_kv_heads);
     const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)blockIdx.z * QG;
     const float scale = a.scale_log2;
 
-    const int64_t nres = a.n_tokens - a.n_quant;
+    // this unit's counters (its batch row's, when the rows differ in length)
+    const RowCounts cnt = row_counts<RAGGED>(a, b);
+    if constexpr (RAGGED)
+        if (split >= cnt.n_split) return;  // an idle split of a shorter row (the whole work-group)
+    const int64_t nres = cnt.n_tokens - cnt.n_quant;
     const int64_t nrc = (nres + kG - 1) / kG;
     const int64_t cost = kResidualChunkCost;
     int64_t b0, b1;
-    split_range(a.n_blocks, nrc, cost, a.n_split, split, &b0, &b1);
-    const int rc = (int)(split == a.n_split - 1 ? nrc : 0);
+    split_range(cnt.n_blocks, nrc, cost, cnt.n_split, split, &b0, &b1);
+    const int rc = (int)(split == cnt.n_split - 1 ? nrc : 0);
     const int j0 = __builtin_amdgcn_readfirstlane((int)b0 + wave);
     const int j1 = __builtin_amdgcn_readfirstlane((int)b1);
 
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
-    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)a.n_blocks * L::bytes);
+    const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)cnt.n_blocks * L::bytes);
     // per-lane byte offsets of the block shares: a base per share plus
     // compile-time steps (which become the loads' immediate offsets)
     const int rt = gqa_row_token<BITS>(n);       // token of score column n in its tile
@@ -352,8 +356,9 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     // the kernel's first loads are the query and the staged blocks only
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
-    const int slot0 = (int)(a.n_quant % g.ring_slots);
-    if (a.t_new >= 0 && split == a.n_split - 1 && blockIdx.z == 0 && wave == 0) write_new_token<D>(a, u, rbase);
+    const int slot0 = (int)(cnt.n_quant % g.ring_slots);
+    if (cnt.t_new >= 0 && split == cnt.n_split - 1 && blockIdx.z == 0 && wave == 0)
+        write_new_token<D>(a, u, cnt.t_new, rbase);
     // scores, softmax, weight digits of one block
     auto key_math = [&](const R& r, int k_slot) {
         // 1. digits of the folded query: rint(q 2^(22-Eq) * s 2^-Es)
@@ -536,7 +541,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
             valid[i] = idx < (int)nres;
             int slot = slot0 + (valid[i] ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            const uint4* kp = a.n_quant + idx == a.t_new
+            const uint4* kp = cnt.n_quant + idx == cnt.t_new
                                   ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
                                   : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
             kraw[i][0] = kp[0];
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
             const int idx = ck * kG + t;
             int slot = slot0 + (idx < (int)nres ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            vr[t] = a.n_quant + idx == a.t_new
+            vr[t] = cnt.n_quant + idx == cnt.t_new
                         ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
                         : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
         }
@@ -693,7 +698,10 @@ hipError_t gqa_launch(const AttendArgs& a, hipStream_t s) {
     constexpr int NW = attend_waves(4, 128);
     const int group = a.g.n_q_heads / a.g.n_kv_heads;
     const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / 4));
-    attend_gqa_kernel<128, BITS, NW><<<grid, 64 * NW, 0, s>>>(a);
+    if (a.rows.n)
+        attend_gqa_kernel<128, BITS, NW, true><<<grid, 64 * NW, 0, s>>>(a);
+    else
+        attend_gqa_kernel<128, BITS, NW, false><<<grid, 64 * NW, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -72,7 +72,8 @@ __device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float
     }
 }
 
-// One work-group per (key block j, unit): 2*D threads. Threads [0, D) take
+// One work-group per (key block j, unit): 2*D threads (with a row table, block
+// j0[row] + blockIdx.x of the unit's batch row, if below j1[row]). Threads [0, D) take
 // one key channel each over the block's 32 tokens; threads [D, 2D) take one
 // (token, 32-channel value group) each. Then all threads pack words.
 template <int D, int BITS>
@@ -90,20 +91,24 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
 
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
-    const int64_t j = a.j0 + blockIdx.x;
     const int64_t u = blockIdx.y;
+    // this unit's blocks and ring boundary: its batch row's, when rows differ
+    const int64_t brow = u / g.n_kv_heads;
+    const int64_t j = (a.rows.n ? a.rows.j0[brow] : a.j0) + blockIdx.x;
+    if (a.rows.n && j >= a.rows.j1[brow]) return;  // the whole work-group
+    const int64_t ring_end = a.rows.n ? a.rows.ring_end[brow] : a.ring_end;
 
     for (int idx = tid; idx < kG * CPR; idx += NT) {
         const int t = idx / CPR, c16 = idx % CPR;
         const int64_t tok = j * kG + t;
         const uint4 *ks, *vs;
-        if (tok < a.ring_end) {
+        if (tok < ring_end) {
             const uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
                                   (size_t)(tok % g.ring_slots) * 4 * D;
             ks = reinterpret_cast<const uint4*>(slot) + c16;
             vs = reinterpret_cast<const uint4*>(slot + 2 * D) + c16;
         } else {
-            const int64_t row = u * a.ntok + (tok - a.ring_end);
+            const int64_t row = u * a.ntok + (tok - ring_end);
             ks = reinterpret_cast<const uint4*>(a.k + row * D) + c16;
             vs = reinterpret_cast<const uint4*>(a.v + row * D) + c16;
         }
@@ -171,20 +176,25 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     }
 }
 
-// Copy tokens [t0, t1) of every unit into their ring slots: one thread per
-// 16-byte chunk of a key or value row.
+// Copy tokens [t0, t1) of every unit into their ring slots (with a row table,
+// each batch row's own range): one thread per 16-byte chunk of a key or value
+// row.
 template <int D>
 __global__ __launch_bounds__(256) void ring_write_kernel(const RingArgs a) {
     constexpr int CPR = D / 8;
     const CacheGeom& g = a.g;
     const int64_t u = blockIdx.y;
+    const int64_t brow = u / g.n_kv_heads;
+    const int64_t t0 = a.rows.n ? a.rows.t0[brow] : a.t0;
+    const int64_t t1 = a.rows.n ? a.rows.t1[brow] : a.t1;
+    const int64_t in_t0 = a.rows.n ? a.rows.in_t0[brow] : a.in_t0;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n = (a.t1 - a.t0) * 2 * CPR;
+    const int64_t n = (t1 - t0) * 2 * CPR;
     if (idx >= n) return;
     const int c16 = (int)(idx % CPR);
     const int kv = (int)((idx / CPR) & 1);
-    const int64_t tok = a.t0 + idx / (2 * CPR);
-    const int64_t row = u * a.ntok + (tok - a.in_t0);
+    const int64_t tok = t0 + idx / (2 * CPR);
+    const int64_t row = u * a.ntok + (tok - in_t0);
     const uint4* src = reinterpret_cast<const uint4*>((kv ? a.v : a.k) + row * D) + c16;
     uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
                     (size_t)(tok % g.ring_slots) * 4 * D + (size_t)kv * 2 * D;

@@ -4,21 +4,25 @@
 
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "kivi.h"
 #include "launch.hpp"
 #include "planner.hpp"
+
+static_assert(kivi::kMaxRaggedRows == KIVI_MAX_RAGGED_BATCH, "row tables hold the largest ragged batch");
 
 struct kivi_cache {
     kivi_config cfg;
     kivi_layout L;
     uint8_t* mem;
     size_t bytes;
-    int64_t n_tokens;
-    int64_t n_quant;
+    // per batch row (sequence): tokens held, and how many of them are quantized
+    std::vector<int64_t> nt, nq;
     int32_t forced_splits;
     bool poisoned;
 };
@@ -69,21 +73,215 @@ int check_handle(const kivi_cache* c) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Quantize key blocks [j0, j1) of every unit; tokens below ring_end come from
-// the ring, the rest from input rows of k / v (ntok rows per unit).
-int quantize_blocks(kivi_cache* c, int64_t j0, int64_t j1, int64_t ring_end, const void* k, const void* v,
-                    int64_t ntok, hipStream_t s) {
-    if (j1 <= j0) return KIVI_OK;
-    kivi::QuantArgs a;
-    a.g = geom(c);
-    a.j0 = j0;
-    a.j1 = j1;
-    a.ring_end = ring_end;
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.ntok = ntok;
-    hipError_t e = kivi::launch_quantize(a, s);
-    if (e != hipSuccess) return device_fail(c, "quantize launch", e);
+// True when every entry of x equals the first.
+bool all_same(const std::vector<int64_t>& x) {
+    for (int64_t e : x)
+        if (e != x[0]) return false;
+    return true;
+}
+
+bool rows_agree(const kivi_cache* c) { return all_same(c->nt) && all_same(c->nq); }
+
+int64_t max_of(const std::vector<int64_t>& x) {
+    int64_t m = x[0];
+    for (int64_t e : x) m = e > m ? e : m;
+    return m;
+}
+
+// Batches whose sequences differ in length pass per-row counters with the
+// kernel arguments, which bounds their batch size.
+int check_ragged_batch(const kivi_cache* c) {
+    if (c->cfg.batch > kivi::kMaxRaggedRows)
+        return fail(KIVI_E_UNSUPPORTED, "sequences of different lengths need batch <= " +
+                                            std::to_string(kivi::kMaxRaggedRows) + " (batch is " +
+                                            std::to_string(c->cfg.batch) + ")");
+    return KIVI_OK;
+}
+
+// Per-row work of one append or flush: quantize key blocks [j0, j1) with
+// tokens below ring_end read from the ring (the rest from input rows t -
+// ring_end), then copy tokens [t0, t1) into the ring from input rows t - in_t0.
+struct RowWork {
+    std::vector<int64_t> j0, j1, ring_end, t0, t1, in_t0;
+    explicit RowWork(int n) : j0(n), j1(n), ring_end(n), t0(n), t1(n), in_t0(n) {}
+};
+
+// Whether the rows' ranges differ, so that the launches need row tables.
+bool work_ragged(const RowWork& w) {
+    return !(all_same(w.j0) && all_same(w.j1) && all_same(w.ring_end) && all_same(w.t0) && all_same(w.t1) &&
+             all_same(w.in_t0));
+}
+
+// The launches of one append or flush (ntok input rows per unit in k and v).
+// The quantization goes first: its ring reads must see the slots before this
+// call's writes.
+int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, int64_t ntok, hipStream_t s) {
+    const int B = c->cfg.batch;
+    const bool ragged = work_ragged(w);
+    int64_t nblk = 0, ntk = 0;
+    for (int b = 0; b < B; ++b) {
+        nblk = w.j1[b] - w.j0[b] > nblk ? w.j1[b] - w.j0[b] : nblk;
+        ntk = w.t1[b] - w.t0[b] > ntk ? w.t1[b] - w.t0[b] : ntk;
+    }
+    if (nblk > 0) {
+        kivi::QuantArgs a;
+        a.g = geom(c);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.ntok = ntok;
+        a.rows.n = 0;
+        if (ragged) {
+            a.j0 = 0;
+            a.j1 = nblk;
+            a.ring_end = 0;
+            a.rows.n = B;
+            for (int b = 0; b < B; ++b) {
+                a.rows.j0[b] = (int32_t)w.j0[b];
+                a.rows.j1[b] = (int32_t)w.j1[b];
+                a.rows.ring_end[b] = (int32_t)w.ring_end[b];
+            }
+        } else {
+            a.j0 = w.j0[0];
+            a.j1 = w.j1[0];
+            a.ring_end = w.ring_end[0];
+        }
+        hipError_t e = kivi::launch_quantize(a, s);
+        if (e != hipSuccess) return device_fail(c, "quantize launch", e);
+    }
+    if (ntk > 0) {
+        kivi::RingArgs a;
+        a.g = geom(c);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.ntok = ntok;
+        a.rows.n = 0;
+        if (ragged) {
+            a.t0 = 0;
+            a.t1 = ntk;
+            a.in_t0 = 0;
+            a.rows.n = B;
+            for (int b = 0; b < B; ++b) {
+                a.rows.t0[b] = (int32_t)w.t0[b];
+                a.rows.t1[b] = (int32_t)(w.t1[b] > w.t0[b] ? w.t1[b] : w.t0[b]);
+                a.rows.in_t0[b] = (int32_t)w.in_t0[b];
+            }
+        } else {
+            a.t0 = w.t0[0];
+            a.t1 = w.t1[0];
+            a.in_t0 = w.in_t0[0];
+        }
+        hipError_t e = kivi::launch_ring_write(a, s);
+        if (e != hipSuccess) return device_fail(c, "ring write launch", e);
+    }
+    return KIVI_OK;
+}
+
+// Appends ntok[b] tokens to row b: the per-row work and the counters after.
+RowWork plan_rows(const kivi_cache* c, const int32_t* ntok, std::vector<int64_t>& nt1, std::vector<int64_t>& nq1) {
+    const int B = c->cfg.batch;
+    const int64_t G = c->cfg.k_block, R = c->cfg.residual;
+    RowWork w(B);
+    for (int b = 0; b < B; ++b) {
+        const kivi::AppendPlan p = kivi::plan_append(c->nt[b], c->nq[b], ntok[b], R, G);
+        w.j0[b] = p.nq0 / G;
+        w.j1[b] = p.nq1 / G;
+        w.ring_end[b] = p.nt0;
+        w.t0[b] = p.ring_t0;
+        w.t1[b] = p.nt1 > p.ring_t0 ? p.nt1 : p.ring_t0;
+        w.in_t0[b] = p.nt0;
+        nt1[b] = p.nt1;
+        nq1[b] = p.nq1;
+    }
+    return w;
+}
+
+int validate_kv(const void* k, const void* v) {
+    if (!k || !v) return fail(KIVI_E_INVAL, "k and v must be device pointers");
+    if (!aligned16(k) || !aligned16(v)) return fail(KIVI_E_INVAL, "k and v must be 16-byte aligned");
+    return KIVI_OK;
+}
+
+int validate_q(const void* q, int32_t q_dtype, const float* out) {
+    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
+    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
+    return KIVI_OK;
+}
+
+// The split plan; *cost_max receives the costliest row's cost (rows that differ).
+kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
+    const int B = c->cfg.batch;
+    const int32_t group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+    const int64_t G = c->cfg.k_block;
+    if (rows_agree(c)) {
+        if (cost_max) *cost_max = kivi::unit_cost(c->nq[0] / G, c->nt[0] - c->nq[0]);
+        return kivi::plan_attend((int64_t)B * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
+                                 c->L.max_splits, c->forced_splits);
+    }
+    std::vector<int64_t> cost(B);
+    for (int b = 0; b < B; ++b) cost[b] = kivi::unit_cost(c->nq[b] / G, c->nt[b] - c->nq[b]);
+    int64_t cm = 1;
+    kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, B, cost.data(),
+                                                max_of(c->nq) / G, c->L.max_splits, c->forced_splits, &cm);
+    if (cost_max) *cost_max = cm;
+    return p;
+}
+
+// The attention launch over the counters of the handle. With k_new / v_new,
+// the newest token of each row for which appended[b] holds (its token n_t - 1)
+// was appended by this call and is not in the ring yet.
+int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
+                const void* v_new, const std::vector<char>* appended) {
+    const int B = cache->cfg.batch;
+    int64_t cost_max = 1;
+    kivi::AttendPlan p = attend_plan(cache, &cost_max);
+    kivi::AttendArgs a;
+    a.g = geom(cache);
+    a.q = static_cast<const uint16_t*>(q);
+    a.q_bf16 = q_dtype == KIVI_BF16;
+    a.out = out;
+    a.n_split = p.n_split;
+    a.qg = p.qg;
+    a.nwaves = p.nwaves;
+    a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    std::vector<int64_t> t_new(B, -1);
+    if (appended)
+        for (int b = 0; b < B; ++b) t_new[b] = (*appended)[b] ? cache->nt[b] - 1 : -1;
+    a.rows.n = 0;
+    a.cost_max = cost_max;
+    if (rows_agree(cache) && all_same(t_new)) {
+        a.n_tokens = cache->nt[0];
+        a.n_quant = cache->nq[0];
+        a.n_blocks = cache->nq[0] / cache->cfg.k_block;
+        a.t_new = t_new[0];
+    } else {
+        a.n_tokens = max_of(cache->nt);
+        a.n_quant = max_of(cache->nq);
+        a.n_blocks = a.n_quant / cache->cfg.k_block;
+        a.t_new = -1;
+        a.rows.n = B;
+        std::vector<int64_t> cost(B);
+        for (int b = 0; b < B; ++b) {
+            a.rows.n_tokens[b] = (int32_t)cache->nt[b];
+            a.rows.n_quant[b] = (int32_t)cache->nq[b];
+            a.rows.t_new[b] = (int32_t)t_new[b];
+            a.rows.order[b] = b;
+            cost[b] = kivi::unit_cost(cache->nq[b] / cache->cfg.k_block, cache->nt[b] - cache->nq[b]);
+        }
+        // costliest rows first: their work-groups start in the first round
+        std::stable_sort(a.rows.order, a.rows.order + B, [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+    }
+    (void)hipGetLastError();
+    hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(cache, "attend launch", e);
+    return KIVI_OK;
+}
+
+int check_row(const kivi_cache* c, int32_t row) {
+    if (row < 0 || row >= c->cfg.batch)
+        return fail(KIVI_E_INVAL, "row " + std::to_string(row) + " outside [0, " + std::to_string(c->cfg.batch) + ")");
     return KIVI_OK;
 }
 
@@ -133,8 +331,8 @@ int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_
     c->L = L;
     c->mem = static_cast<uint8_t*>(dev_mem);
     c->bytes = bytes;
-    c->n_tokens = 0;
-    c->n_quant = 0;
+    c->nt.assign(cfg->batch, 0);
+    c->nq.assign(cfg->batch, 0);
     c->forced_splits = 0;
     c->poisoned = false;
     *out = c;
@@ -149,18 +347,45 @@ int kivi_cache_destroy(kivi_cache* cache) {
 
 int kivi_cache_reset(kivi_cache* cache) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
-    cache->n_tokens = 0;
-    cache->n_quant = 0;
+    std::fill(cache->nt.begin(), cache->nt.end(), 0);
+    std::fill(cache->nq.begin(), cache->nq.end(), 0);
     cache->poisoned = false;
+    return KIVI_OK;
+}
+
+int kivi_reset_row(kivi_cache* cache, int32_t row) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if ((rc = check_row(cache, row)) != KIVI_OK) return rc;
+    const int64_t nt = cache->nt[row], nq = cache->nq[row];
+    cache->nt[row] = 0;
+    cache->nq[row] = 0;
+    if (!rows_agree(cache) && (rc = check_ragged_batch(cache)) != KIVI_OK) {
+        cache->nt[row] = nt;
+        cache->nq[row] = nq;
+        return rc;
+    }
     return KIVI_OK;
 }
 
 int kivi_cache_query(const kivi_cache* cache, kivi_state* st) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
     if (!st) return fail(KIVI_E_INVAL, "state is NULL");
-    st->n_tokens = cache->n_tokens;
-    st->n_quant = cache->n_quant;
-    st->n_resid = cache->n_tokens - cache->n_quant;
+    if (!rows_agree(cache)) return fail(KIVI_E_RAGGED, "the sequences differ in length; use kivi_query_row");
+    st->n_tokens = cache->nt[0];
+    st->n_quant = cache->nq[0];
+    st->n_resid = cache->nt[0] - cache->nq[0];
+    return KIVI_OK;
+}
+
+int kivi_query_row(const kivi_cache* cache, int32_t row, kivi_state* st) {
+    if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
+    if (!st) return fail(KIVI_E_INVAL, "state is NULL");
+    int rc = check_row(cache, row);
+    if (rc != KIVI_OK) return rc;
+    st->n_tokens = cache->nt[row];
+    st->n_quant = cache->nq[row];
+    st->n_resid = cache->nt[row] - cache->nq[row];
     return KIVI_OK;
 }
 
@@ -168,10 +393,9 @@ int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
     if (!after) return fail(KIVI_E_INVAL, "state is NULL");
     if (ntok < 1) return fail(KIVI_E_INVAL, "ntok must be >= 1");
-    if (cache->n_tokens + ntok > cache->cfg.max_tokens)
-        return fail(KIVI_E_CAPACITY, "append would exceed max_tokens");
-    kivi::AppendPlan p =
-        kivi::plan_append(cache->n_tokens, cache->n_quant, ntok, cache->cfg.residual, cache->cfg.k_block);
+    if (!rows_agree(cache)) return fail(KIVI_E_RAGGED, "the sequences differ in length");
+    if (cache->nt[0] + ntok > cache->cfg.max_tokens) return fail(KIVI_E_CAPACITY, "append would exceed max_tokens");
+    kivi::AppendPlan p = kivi::plan_append(cache->nt[0], cache->nq[0], ntok, cache->cfg.residual, cache->cfg.k_block);
     after->n_tokens = p.nt1;
     after->n_quant = p.nq1;
     after->n_resid = p.nt1 - p.nq1;
@@ -181,58 +405,76 @@ int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after) {
 int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, void* stream) {
     int rc = check_handle(cache);
     if (rc != KIVI_OK) return rc;
-    if (!k || !v) return fail(KIVI_E_INVAL, "k and v must be device pointers");
-    if (!aligned16(k) || !aligned16(v)) return fail(KIVI_E_INVAL, "k and v must be 16-byte aligned");
+    if ((rc = validate_kv(k, v)) != KIVI_OK) return rc;
     if (ntok < 1) return fail(KIVI_E_INVAL, "ntok must be >= 1");
-    if (cache->n_tokens + ntok > cache->cfg.max_tokens)
+    if (max_of(cache->nt) + ntok > cache->cfg.max_tokens)
         return fail(KIVI_E_CAPACITY, "append of " + std::to_string(ntok) + " tokens would exceed max_tokens (" +
                                          std::to_string(cache->cfg.max_tokens) + ")");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t G = cache->cfg.k_block;
-    kivi::AppendPlan p = kivi::plan_append(cache->n_tokens, cache->n_quant, ntok, cache->cfg.residual, G);
+    const int B = cache->cfg.batch;
+    std::vector<int32_t> n(B, ntok);
+    std::vector<int64_t> nt1(B), nq1(B);
+    const RowWork w = plan_rows(cache, n.data(), nt1, nq1);
     (void)hipGetLastError();
-    // quantize first: its ring reads must see the slots before this call's writes
-    rc = quantize_blocks(cache, p.nq0 / G, p.nq1 / G, p.nt0, k, v, ntok, s);
+    rc = launch_work(cache, w, k, v, ntok, static_cast<hipStream_t>(stream));
     if (rc != KIVI_OK) return rc;
-    if (p.nt1 > p.ring_t0) {
-        kivi::RingArgs a;
-        a.g = geom(cache);
-        a.t0 = p.ring_t0;
-        a.t1 = p.nt1;
-        a.in_t0 = p.nt0;
-        a.k = static_cast<const uint16_t*>(k);
-        a.v = static_cast<const uint16_t*>(v);
-        a.ntok = ntok;
-        hipError_t e = kivi::launch_ring_write(a, s);
-        if (e != hipSuccess) return device_fail(cache, "ring write launch", e);
+    cache->nt = nt1;
+    cache->nq = nq1;
+    return KIVI_OK;
+}
+
+int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int32_t* ntok, int32_t max_ntok,
+                     void* stream) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if ((rc = validate_kv(k, v)) != KIVI_OK) return rc;
+    if (!ntok) return fail(KIVI_E_INVAL, "ntok is NULL");
+    if (max_ntok < 1) return fail(KIVI_E_INVAL, "max_ntok must be >= 1");
+    const int B = cache->cfg.batch;
+    for (int b = 0; b < B; ++b) {
+        if (ntok[b] < 0 || ntok[b] > max_ntok)
+            return fail(KIVI_E_INVAL, "ntok[" + std::to_string(b) + "] = " + std::to_string(ntok[b]) +
+                                          " outside [0, max_ntok]");
+        if (cache->nt[b] + ntok[b] > cache->cfg.max_tokens)
+            return fail(KIVI_E_CAPACITY, "append of " + std::to_string(ntok[b]) + " tokens to row " +
+                                             std::to_string(b) + " would exceed max_tokens (" +
+                                             std::to_string(cache->cfg.max_tokens) + ")");
     }
-    cache->n_tokens = p.nt1;
-    cache->n_quant = p.nq1;
+    std::vector<int64_t> nt1(B), nq1(B);
+    const RowWork w = plan_rows(cache, ntok, nt1, nq1);
+    if ((work_ragged(w) || !(all_same(nt1) && all_same(nq1))) && (rc = check_ragged_batch(cache)) != KIVI_OK)
+        return rc;
+    (void)hipGetLastError();
+    rc = launch_work(cache, w, k, v, max_ntok, static_cast<hipStream_t>(stream));
+    if (rc != KIVI_OK) return rc;
+    cache->nt = nt1;
+    cache->nq = nq1;
     return KIVI_OK;
 }
 
 int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed) {
     int rc = check_handle(cache);
     if (rc != KIVI_OK) return rc;
+    const int B = cache->cfg.batch;
     const int64_t G = cache->cfg.k_block;
-    const int64_t k = kivi::plan_flush(cache->n_tokens, cache->n_quant, cache->cfg.residual, G);
-    (void)hipGetLastError();
-    if (k > 0) {
-        rc = quantize_blocks(cache, cache->n_quant / G, (cache->n_quant + k) / G, cache->n_tokens, nullptr, nullptr,
-                             0, static_cast<hipStream_t>(stream));
-        if (rc != KIVI_OK) return rc;
-        cache->n_quant += k;
+    RowWork w(B);
+    std::vector<int64_t> nq1(B);
+    int64_t kmax = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t k = kivi::plan_flush(cache->nt[b], cache->nq[b], cache->cfg.residual, G);
+        w.j0[b] = cache->nq[b] / G;
+        w.j1[b] = (cache->nq[b] + k) / G;
+        w.ring_end[b] = cache->nt[b];
+        w.t0[b] = w.t1[b] = w.in_t0[b] = 0;
+        nq1[b] = cache->nq[b] + k;
+        kmax = k > kmax ? k : kmax;
     }
-    if (n_flushed) *n_flushed = (int32_t)k;
+    (void)hipGetLastError();
+    rc = launch_work(cache, w, nullptr, nullptr, 0, static_cast<hipStream_t>(stream));
+    if (rc != KIVI_OK) return rc;
+    cache->nq = nq1;
+    if (n_flushed) *n_flushed = (int32_t)kmax;
     return KIVI_OK;
 }
-
-namespace {
-kivi::AttendPlan attend_plan(const kivi_cache* c) {
-    return kivi::plan_attend((int64_t)c->cfg.batch * c->cfg.n_kv_heads, c->cfg.n_q_heads / c->cfg.n_kv_heads,
-                             c->cfg.head_dim, c->n_quant / c->cfg.k_block, c->L.max_splits, c->forced_splits);
-}
-}  // namespace
 
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
@@ -250,54 +492,24 @@ int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split) {
     return KIVI_OK;
 }
 
-namespace {
-// The attention launch; (k_new, v_new, t_new) carry a token appended in the
-// same step that is not in the ring yet (t_new < 0: none).
-int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
-                const void* v_new, int64_t t_new) {
-    kivi::AttendPlan p = attend_plan(cache);
-    kivi::AttendArgs a;
-    a.g = geom(cache);
-    a.q = static_cast<const uint16_t*>(q);
-    a.q_bf16 = q_dtype == KIVI_BF16;
-    a.out = out;
-    a.n_tokens = cache->n_tokens;
-    a.n_quant = cache->n_quant;
-    a.n_blocks = cache->n_quant / cache->cfg.k_block;
-    a.n_split = p.n_split;
-    a.qg = p.qg;
-    a.nwaves = p.nwaves;
-    a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
-    a.k_new = static_cast<const uint16_t*>(k_new);
-    a.v_new = static_cast<const uint16_t*>(v_new);
-    a.t_new = t_new;
-    (void)hipGetLastError();
-    hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return device_fail(cache, "attend launch", e);
-    return KIVI_OK;
-}
-}  // namespace
-
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
     int rc = check_handle(cache);
     if (rc != KIVI_OK) return rc;
-    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
-    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
-    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
-    if (cache->n_tokens == 0) return fail(KIVI_E_EMPTY, "attention on an empty cache");
-    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, -1);
+    if ((rc = validate_q(q, q_dtype, out)) != KIVI_OK) return rc;
+    for (int b = 0; b < cache->cfg.batch; ++b)
+        if (cache->nt[b] == 0)
+            return fail(KIVI_E_EMPTY, rows_agree(cache) ? std::string("attention on an empty cache")
+                                                        : "attention with sequence " + std::to_string(b) + " empty");
+    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr);
 }
 
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
                      void* stream, int32_t* n_flushed) {
     int rc = check_handle(cache);
     if (rc != KIVI_OK) return rc;
-    if (!q || !out) return fail(KIVI_E_INVAL, "q and out must be device pointers");
-    if (!aligned16(q) || !aligned16(out)) return fail(KIVI_E_INVAL, "q and out must be 16-byte aligned");
-    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
-    if (!k || !v) return fail(KIVI_E_INVAL, "k and v must be device pointers");
-    if (!aligned16(k) || !aligned16(v)) return fail(KIVI_E_INVAL, "k and v must be 16-byte aligned");
-    if (cache->n_tokens + 1 > cache->cfg.max_tokens)
+    if ((rc = validate_q(q, q_dtype, out)) != KIVI_OK) return rc;
+    if ((rc = validate_kv(k, v)) != KIVI_OK) return rc;
+    if (max_of(cache->nt) + 1 > cache->cfg.max_tokens)
         return fail(KIVI_E_CAPACITY, "append of 1 token would exceed max_tokens (" +
                                          std::to_string(cache->cfg.max_tokens) + ")");
     // The same result as kivi_append(1) + kivi_flush (when a whole group lies
@@ -305,20 +517,33 @@ int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void
     // quantization of every group that leaves the residual (the new token,
     // should it be one of them, read from k and v), then the attention, which
     // also writes the new token into its ring slot.
+    const int B = cache->cfg.batch;
     const int64_t G = cache->cfg.k_block, R = cache->cfg.residual;
-    const int64_t nt0 = cache->n_tokens;
-    kivi::AppendPlan p = kivi::plan_append(nt0, cache->n_quant, 1, R, G);
-    const int64_t n_res = p.nt1 - p.nq1;
-    const int64_t nq = n_res >= R + G ? p.nq1 + kivi::plan_flush(p.nt1, p.nq1, R, G) : p.nq1;
-    (void)hipGetLastError();
-    if (nq > p.nq0) {
-        rc = quantize_blocks(cache, p.nq0 / G, nq / G, nt0, k, v, 1, static_cast<hipStream_t>(stream));
-        if (rc != KIVI_OK) return rc;
+    RowWork w(B);
+    std::vector<int64_t> nt1(B), nq1(B);
+    std::vector<char> appended(B);
+    int64_t fmax = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t nt0 = cache->nt[b];
+        const kivi::AppendPlan p = kivi::plan_append(nt0, cache->nq[b], 1, R, G);
+        const int64_t n_res = p.nt1 - p.nq1;
+        const int64_t nq = n_res >= R + G ? p.nq1 + kivi::plan_flush(p.nt1, p.nq1, R, G) : p.nq1;
+        w.j0[b] = p.nq0 / G;
+        w.j1[b] = nq / G;
+        w.ring_end[b] = nt0;
+        w.t0[b] = w.t1[b] = w.in_t0[b] = 0;  // the attention writes the token into the ring
+        nt1[b] = p.nt1;
+        nq1[b] = nq;
+        appended[b] = nt0 >= nq;
+        fmax = nq - p.nq1 > fmax ? nq - p.nq1 : fmax;
     }
-    cache->n_tokens = p.nt1;
-    cache->n_quant = nq;
-    if (n_flushed) *n_flushed = (int32_t)(nq - p.nq1);
-    return attend_call(cache, q, q_dtype, out, stream, k, v, nt0 >= nq ? nt0 : -1);
+    (void)hipGetLastError();
+    rc = launch_work(cache, w, k, v, 1, static_cast<hipStream_t>(stream));
+    if (rc != KIVI_OK) return rc;
+    cache->nt = nt1;
+    cache->nq = nq1;
+    if (n_flushed) *n_flushed = (int32_t)fmax;
+    return attend_call(cache, q, q_dtype, out, stream, k, v, &appended);
 }
 
 }  // extern "C"

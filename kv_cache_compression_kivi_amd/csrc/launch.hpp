@@ -6,6 +6,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "split.hpp"
+
 namespace kivi {
 
 // Geometry shared by every kernel of one cache.
@@ -20,9 +22,22 @@ struct CacheGeom {
     int32_t batch, n_kv_heads, n_q_heads, head_dim, bits;
 };
 
+// Sequences of one batch may hold different numbers of tokens. A launch over
+// such a batch carries one entry per batch row in a row table, passed with
+// the kernel arguments (no device copy per call); n = 0 marks a batch whose
+// rows all agree, and then the uniform fields of the arguments apply. Token
+// counts of one sequence fit in 32 bits (its blocks fit in 4 GiB).
+constexpr int kMaxRaggedRows = 128;
+
 // Quantize key blocks [j0, j1) of every unit. Token t of a block comes from
 // the ring when t < ring_end, else from input row t - ring_end of k / v
-// ([units][ntok][d] fp16).
+// ([units][ntok][d] fp16). With a row table, row b's units take
+// [rows.j0[b], rows.j1[b]) and rows.ring_end[b], and j1 - j0 is the largest
+// block count of a row (the grid).
+struct QuantRows {
+    int32_t n;
+    int32_t j0[kMaxRaggedRows], j1[kMaxRaggedRows], ring_end[kMaxRaggedRows];
+};
 struct QuantArgs {
     CacheGeom g;
     int64_t j0, j1;
@@ -30,15 +45,29 @@ struct QuantArgs {
     const uint16_t* k;
     const uint16_t* v;
     int64_t ntok;
+    QuantRows rows;
 };
 
 // Copy tokens [t0, t1) of every unit from input rows (t - in_t0) into the ring.
+// With a row table, row b's units copy [rows.t0[b], rows.t1[b]) from input
+// rows (t - rows.in_t0[b]), and t1 - t0 is the largest count of a row.
+struct RingRows {
+    int32_t n;
+    int32_t t0[kMaxRaggedRows], t1[kMaxRaggedRows], in_t0[kMaxRaggedRows];
+};
 struct RingArgs {
     CacheGeom g;
     int64_t t0, t1, in_t0;
     const uint16_t* k;
     const uint16_t* v;
     int64_t ntok;
+    RingRows rows;
+};
+
+struct AttendRows {
+    int32_t n;
+    int32_t n_tokens[kMaxRaggedRows], n_quant[kMaxRaggedRows], t_new[kMaxRaggedRows];
+    int32_t order[kMaxRaggedRows];  // batch rows in dispatch order: costliest first
 };
 
 // Decode attention. Work-group (split s, unit u, query chunk z) covers the
@@ -62,7 +91,50 @@ struct AttendArgs {
     const uint16_t* k_new;
     const uint16_t* v_new;
     int64_t t_new;
+    // With a row table, row b holds rows.n_tokens[b] tokens, rows.n_quant[b]
+    // of them quantized, and rows.t_new[b] (or -1) is its appended token;
+    // n_blocks is then the largest row's block count, n_split the split count
+    // of the costliest row (cost_max, in unit_cost terms), and row b takes
+    // row_split_count(its cost, cost_max, n_split) splits.
+    AttendRows rows;
+    int64_t cost_max;
 };
+
+// The counters of batch row b for one attention launch, and its split count.
+struct RowCounts {
+    int64_t n_tokens, n_quant, n_blocks, t_new, n_split;
+};
+// The kernels are built twice: RAGGED for launches with a row table, and
+// without it for batches whose rows agree, which then read only the uniform
+// fields (no row-table read on the way to their first loads).
+
+// The unit of grid row y: with a row table, the rows go out costliest first
+// (their work-groups are dispatched in grid order), else unit y.
+template <bool RAGGED>
+__host__ __device__ inline int64_t dispatch_unit(const AttendArgs& a, int64_t y) {
+    if constexpr (!RAGGED) return y;
+    const int64_t hkv = a.g.n_kv_heads;
+    return (int64_t)a.rows.order[y / hkv] * hkv + y % hkv;
+}
+
+template <bool RAGGED>
+__host__ __device__ inline RowCounts row_counts(const AttendArgs& a, int64_t b) {
+    RowCounts c;
+    if constexpr (RAGGED) {
+        c.n_tokens = a.rows.n_tokens[b];
+        c.n_quant = a.rows.n_quant[b];
+        c.t_new = a.rows.t_new[b];
+        c.n_blocks = c.n_quant / 32;  // 32 tokens per key block
+        c.n_split = row_split_count(unit_cost(c.n_blocks, c.n_tokens - c.n_quant), a.cost_max, a.n_split);
+    } else {
+        c.n_tokens = a.n_tokens;
+        c.n_quant = a.n_quant;
+        c.t_new = a.t_new;
+        c.n_blocks = a.n_blocks;
+        c.n_split = a.n_split;
+    }
+    return c;
+}
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingArgs& a, hipStream_t s);

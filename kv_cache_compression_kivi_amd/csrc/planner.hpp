@@ -164,4 +164,50 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
     return p;
 }
 
+// Split plan of a batch whose rows differ in length (cost[r]: unit_cost of
+// row r; nb_max: the longest row's key blocks). n is the split count of the
+// costliest row and each row takes its share (row_split_count), so that the
+// work-groups carry about equal work. n is the largest count whose work-groups
+// still fit one round over the CUs (as for rows that agree: 8 waves a CU), at
+// least 1: then every work-group starts at once, and the costliest rows'
+// work-groups, dispatched first, pair with short ones on their CUs (measured
+// on MI355X: more splits, with a second round of work-groups and the merge,
+// were 15-40% slower on a 64-row serving batch). At least 2 key blocks per
+// wave in the costliest row's splits, at most max_splits; forced > 0 fixes n.
+inline AttendPlan plan_attend_rows(int64_t n_kv_heads, int32_t group, int32_t head_dim, int64_t rows,
+                                   const int64_t* cost, int64_t nb_max, int32_t max_splits, int32_t forced,
+                                   int64_t* cost_max) {
+    AttendPlan p;
+    attend_shape(group, head_dim, &p.qg, &p.nwaves);
+    const int64_t wgs_per_row = n_kv_heads * (group / p.qg);  // work-groups of one split of one row
+    int64_t cmax = 1;
+    for (int64_t r = 0; r < rows; ++r) cmax = cost[r] > cmax ? cost[r] : cmax;
+    auto wgs = [&](int64_t n) {
+        int64_t w = 0;
+        for (int64_t r = 0; r < rows; ++r) w += row_split_count(cost[r], cmax, n);
+        return w * wgs_per_row;
+    };
+    int64_t n;
+    if (forced > 0) {
+        n = forced;
+    } else {
+        const int64_t target_wgs = 256 * 8 / p.nwaves;
+        int64_t hi = nb_max / (2 * p.nwaves);
+        if (hi > max_splits) hi = max_splits;
+        // the largest n in [1, hi] with wgs(n) <= target (wgs grows with n)
+        n = 1;
+        while (n < hi) {
+            const int64_t mid = (n + hi + 1) / 2;
+            if (wgs(mid) <= target_wgs) n = mid;
+            else hi = mid - 1;
+        }
+    }
+    if (n > max_splits) n = max_splits;
+    if (n < 1) n = 1;
+    p.n_split = (int32_t)n;
+    p.blocks_per_split = (int32_t)((nb_max + n - 1) / n);
+    *cost_max = cmax;
+    return p;
+}
+
 }  // namespace kivi

@@ -34,6 +34,19 @@ KIVI_HD inline void split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n
     *b1 = s == n - 1 ? nb : (hi < nb ? hi : nb);
 }
 
+// Cost of a unit's attention work, in key blocks: nb key blocks and the
+// residual's chunks of 32 tokens.
+KIVI_HD inline int64_t unit_cost(int64_t nb, int64_t n_resid) { return nb + kResidualChunkCost * ((n_resid + 31) / 32); }
+
+// Splits of one batch row when the rows differ in length: n splits for the
+// costliest row (cost_max), and for a row of cost c the share of n its cost
+// calls for, so that every split of every row holds about cost_max / n
+// (rounded up, at least 1). Splits s >= this count of a row are idle.
+KIVI_HD inline int64_t row_split_count(int64_t cost, int64_t cost_max, int64_t n) {
+    const int64_t k = (n * cost + cost_max - 1) / cost_max;
+    return k < 1 ? 1 : k;
+}
+
 // Inside a work-group of nw waves, wave w takes the split's key blocks
 // b0 + w, b0 + w + nw, b0 + w + 2 nw, ... (round robin), so the waves sweep
 // the split's records together, and residual chunk c goes to wave

@@ -43,9 +43,9 @@ def gpu_unit_residual(cache, unit: int, n_quant: int, n_tokens: int):
 def compare_unit(cache, oc: "oracle.OracleCache", gpu_unit: int, or_unit: int):
     """Bit-exact comparison of one unit's quantized blocks and residual."""
     nt, nq = oc.state()
-    st = cache.state()
-    assert (st[0], st[1]) == (nt, nq), (st, (nt, nq))
     c = cache.cfg
+    st = cache.row_state(gpu_unit // c.n_kv_heads)
+    assert (st[0], st[1]) == (nt, nq), (st, (nt, nq))
     G, bits = c.k_block, c.bits
     nb = nq // G
     kc, ks, kz, vc, vs, vz = oc.unit_quantized(or_unit)

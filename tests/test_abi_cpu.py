@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(native):
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(native.EXPORTED)
-    assert native.kivi_abi_version() == 1
+    assert native.kivi_abi_version() == 2
     nm = subprocess.run(["nm", "-D", "--defined-only", native.library_path()], capture_output=True, text=True).stdout
     for name in declared:
         assert re.search(r"\bT " + name + r"\b", nm), name
@@ -137,6 +137,56 @@ def test_create_and_host_only_calls(native):
         native.kivi_cache_destroy(h)
 
 
+def test_row_entry_points_host_only(native):
+    """The per-sequence calls validate before anything would be launched, and
+    appending nothing launches nothing."""
+    cfg = _cfg(native)  # batch 2
+    n = native.kivi_cache_bytes(cfg)
+    fake = 1 << 40
+    h = native.kivi_cache_create(cfg, fake, n)
+    try:
+        st = native.kivi_query_row(h, 1)
+        assert (st.n_tokens, st.n_quant, st.n_resid) == (0, 0, 0)
+        for row in (-1, 2):
+            for call in (lambda: native.kivi_query_row(h, row), lambda: native.kivi_reset_row(h, row)):
+                with pytest.raises(native.KiviError) as e:
+                    call()
+                assert e.value.status == "KIVI_E_INVAL"
+        native.kivi_reset_row(h, 0)
+        for ntok, max_ntok, status in [([1, 2], 1, "KIVI_E_INVAL"), ([-1, 0], 4, "KIVI_E_INVAL"),
+                                       ([1, 1], 0, "KIVI_E_INVAL"), ([1001, 0], 1001, "KIVI_E_CAPACITY")]:
+            with pytest.raises(native.KiviError) as e:
+                native.kivi_append_rows(h, fake, fake, ntok, max_ntok)
+            assert e.value.status == status, (ntok, max_ntok)
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append_rows(h, 0, fake, [1, 1], 1)
+        assert e.value.status == "KIVI_E_INVAL"
+        native.kivi_append_rows(h, fake, fake, [0, 0], 3)  # nothing to append: no launch
+        st = native.kivi_cache_query(h)
+        assert (st.n_tokens, st.n_quant, st.n_resid) == (0, 0, 0)
+    finally:
+        native.kivi_cache_destroy(h)
+
+
+def test_ragged_batch_limit(native):
+    """Rows of different lengths pass their counters with the kernel arguments,
+    so a batch above the row-table size is refused before any launch."""
+    cfg = _cfg(native, batch=129, n_kv_heads=1, n_q_heads=1)
+    n = native.kivi_cache_bytes(cfg)
+    fake = 1 << 40
+    h = native.kivi_cache_create(cfg, fake, n)
+    try:
+        ntok = [0] * 129
+        ntok[3] = 5
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append_rows(h, fake, fake, ntok, 5)
+        assert e.value.status == "KIVI_E_UNSUPPORTED"
+        assert native.kivi_query_row(h, 3).n_tokens == 0
+    finally:
+        native.kivi_cache_destroy(h)
+    assert "#define KIVI_MAX_RAGGED_BATCH 128" in open(HEADER, encoding="utf-8").read()
+
+
 # ---------------------------------------------------------------- host planner
 
 SHIM = r"""
@@ -160,6 +210,13 @@ int64_t shim_wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return kivi::wave
 int64_t shim_residual_wave(int64_t c, int64_t nw) {
     return kivi::residual_wave(c, nw);
 }
+void shim_plan_rows(int64_t hkv, int32_t group, int32_t d, int64_t rows, const int64_t* cost, int64_t nb_max,
+                    int32_t max_splits, int32_t forced, int32_t* out, int64_t* cost_max) {
+    kivi::AttendPlan p = kivi::plan_attend_rows(hkv, group, d, rows, cost, nb_max, max_splits, forced, cost_max);
+    out[0] = p.n_split; out[1] = p.blocks_per_split; out[2] = p.qg; out[3] = p.nwaves;
+}
+int64_t shim_row_split_count(int64_t c, int64_t cm, int64_t n) { return kivi::row_split_count(c, cm, n); }
+int64_t shim_unit_cost(int64_t nb, int64_t nres) { return kivi::unit_cost(nb, nres); }
 }
 """
 
@@ -186,6 +243,12 @@ def planner(tmp_path_factory):
     lib.shim_wave_blocks.restype = i64
     lib.shim_residual_wave.argtypes = [i64] * 2
     lib.shim_residual_wave.restype = i64
+    lib.shim_plan_rows.argtypes = [i64, i32, i32, i64, ctypes.c_void_p, i64, i32, i32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.shim_row_split_count.argtypes = [i64] * 3
+    lib.shim_row_split_count.restype = i64
+    lib.shim_unit_cost.argtypes = [i64] * 2
+    lib.shim_unit_cost.restype = i64
     return lib
 
 
@@ -285,6 +348,56 @@ def test_split_and_wave_ranges_cover_every_block_once(planner, cost):
             assert max(loads) <= total / nw + cost + 1, (nb, nrc, n, nw, loads)
         assert prev_end == nb
         assert np.all(seen == 1)
+
+
+def test_ragged_split_plan(planner):
+    """Rows of different lengths: the costliest row takes all n splits, every
+    row's splits cover its key blocks exactly once with the residual in its
+    last split, no row's splits average more than cost_max / n, and n is the
+    largest count whose work-groups fit one round over the CUs."""
+    rng = np.random.default_rng(3)
+    out = np.zeros(4, np.int32)
+    cmax_buf = np.zeros(1, np.int64)
+    rng_buf = np.zeros(2, np.int64)
+    for trial in range(60):
+        rows = int(rng.integers(1, 129))
+        hkv = int(rng.choice([1, 8, 32]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        lens = rng.integers(1, 20000, rows)
+        nq = np.maximum(0, (lens - 128) // 32 * 32)
+        nb, nres = nq // 32, lens - nq
+        cost = np.array([planner.shim_unit_cost(int(a), int(r)) for a, r in zip(nb, nres)], np.int64)
+        forced = int(rng.choice([0, 0, 0, 3, 50]))
+        planner.shim_plan_rows(hkv, group, 128, rows, cost.ctypes.data_as(ctypes.c_void_p), int(nb.max()), 256,
+                               forced, out.ctypes.data_as(ctypes.c_void_p), cmax_buf.ctypes.data_as(ctypes.c_void_p))
+        n, qg, nw = int(out[0]), int(out[2]), int(out[3])
+        cmax = int(cmax_buf[0])
+        assert cmax == cost.max() and 1 <= n <= 256
+        if forced:
+            assert n == forced
+        wgs = 0
+        for r in range(rows):
+            nr = int(planner.shim_row_split_count(int(cost[r]), cmax, n))
+            assert 1 <= nr <= n
+            if cost[r] == cmax:
+                assert nr == n
+            assert cost[r] / nr <= cmax / n + 1e-9
+            prev = 0
+            for s_ in range(nr):
+                planner.shim_split_range(int(nb[r]), int((nres[r] + 31) // 32), 2, nr, s_,
+                                         rng_buf.ctypes.data_as(ctypes.c_void_p))
+                assert int(rng_buf[0]) == prev and int(rng_buf[1]) >= prev
+                prev = int(rng_buf[1])
+            assert prev == nb[r]
+            wgs += nr * hkv * (group // qg)
+        if not forced:
+            # the largest n whose work-groups fit one round of 256 * 8 / nw (n = 1 if none does)
+            target = 256 * 8 // nw
+            cap = min(256, max(1, int(nb.max()) // (2 * nw)))
+            assert n == 1 or wgs <= target, (n, wgs, target)
+            if n < cap:
+                more = sum(int(planner.shim_row_split_count(int(c), cmax, n + 1)) for c in cost) * hkv * (group // qg)
+                assert more > target, (n, more, target)
 
 
 SANITIZED_MAIN = r"""

@@ -336,3 +336,106 @@ def test_full_stack_layer(layer):
         ref = oc.attend(_unit_rows(q.cpu(), b, h, group), q_is_bf16=True)
         got = out[b:b + 1, h * group:(h + 1) * group].cpu().numpy()
         assert_attention_close(got, ref)
+
+
+# ------------------------------------------------------- sequences of different lengths
+
+def _row_oracles(k, v, lens, Hq, bits, max_tokens, R):
+    """One batch-of-one oracle cache per row, holding that row's own tokens."""
+    B, Hkv, _, d = k.shape
+    ocs = []
+    for b in range(B):
+        oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R)
+        if lens[b]:
+            oc.append(k[b:b + 1, :, :lens[b]].contiguous(), v[b:b + 1, :, :lens[b]].contiguous())
+        ocs.append(oc)
+    return ocs
+
+
+def _check_rows(cache, ocs, out, q, q_bf16=False):
+    Hkv = cache.cfg.n_kv_heads
+    for b, oc in enumerate(ocs):
+        assert cache.row_state(b)[:2] == oc.state(), (b, cache.row_state(b), oc.state())
+        assert_attention_close(out[b:b + 1].cpu().numpy(), oc.attend(q[b:b + 1], q_is_bf16=q_bf16))
+
+
+def _check_bytes(cache, ocs):
+    Hkv = cache.cfg.n_kv_heads
+    for b, oc in enumerate(ocs):
+        for h in range(Hkv):
+            compare_unit(cache, oc, b * Hkv + h, h)
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,d,bits,R,lens", [
+    (5, 2, 2, 128, 2, 128, [1, 33, 160, 161, 700]),   # MHA vector kernel, pairs of blocks
+    (4, 2, 8, 128, 4, 128, [700, 5, 192, 2000]),      # four query heads per KV head (matrix cores), b = 4
+    (3, 1, 4, 128, 2, 32, [64, 1000, 31]),            # four-query kernel at b = 2, small residual
+    (3, 2, 4, 64, 2, 64, [300, 1, 97]),               # d = 64, two query heads per KV head
+    (2, 1, 2, 256, 4, 128, [129, 517]),               # d = 256
+])
+def test_ragged_rows_parity(B, Hkv, Hq, d, bits, R, lens):
+    """Sequences of different lengths in one batch (the per-row entry points):
+    a ragged prefill (kivi_append_rows), attention at several forced split
+    counts (short rows see empty splits), decode steps whose flushes fall on
+    different steps per row, a row emptied and refilled with a new sequence,
+    and a uniform append and flush on the ragged batch. Each row against an
+    oracle cache of that row alone: attention within the bar, bytes exact."""
+    _announce("ragged", B, Hkv, Hq, d, bits, R, lens)
+    steps = 40
+    T = max(lens)
+    max_tokens = T + steps + 80
+    wl = KVWorkload(B, Hkv, d, seed=sum(lens) + d + bits, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    ocs = _row_oracles(k, v, lens, Hq, bits, max_tokens, R)
+    q = wl.q(Hq, step=0)
+    for n in (0, 1, 3, 17):
+        cache.set_attend_splits(n)
+        out = cache.attend(q.to(DEV))
+        torch.cuda.synchronize()
+        _check_rows(cache, ocs, out, q)
+    cache.set_attend_splits(0)
+    _check_bytes(cache, ocs)
+    assert cache.flush() == max(oc.flush() for oc in ocs)
+    for i in range(steps):
+        if i == 15:
+            # row 1 ends; a new sequence of 70 tokens takes its place
+            cache.reset_row(1)
+            kn, vn = wl.kv(5000, 70)
+            ntok = [0] * B
+            ntok[1] = 70
+            cache.append_rows(kn.to(DEV), vn.to(DEV), ntok)
+            ocs[1] = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R)
+            ocs[1].append(kn[1:2].contiguous(), vn[1:2].contiguous())
+        kt, vt = wl.kv(T + i, 1)
+        qi = wl.q(Hq, step=i + 1, dtype=torch.bfloat16 if i % 2 else torch.float16)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), qi.to(DEV))
+        flushed = 0
+        for b, oc in enumerate(ocs):
+            oc.append(kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+            nt, nq = oc.state()
+            if nt - nq >= R + 32:
+                flushed = max(flushed, oc.flush())
+        assert cache.last_flushed == flushed
+        if i % 6 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            _check_rows(cache, ocs, out, qi, q_bf16=qi.dtype == torch.bfloat16)
+    # the same number of tokens appended to every row of the ragged batch, then a flush
+    ka, va = wl.kv(9000, 45)
+    cache.append(ka.to(DEV), va.to(DEV))
+    for b, oc in enumerate(ocs):
+        oc.append(ka[b:b + 1].contiguous(), va[b:b + 1].contiguous())
+    assert cache.flush() == max(oc.flush() for oc in ocs)
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    _check_rows(cache, ocs, out, q)
+    _check_bytes(cache, ocs)
+    with pytest.raises(kv.KiviError) as e:
+        cache.state()
+    assert e.value.status == "KIVI_E_RAGGED"
+    # an emptied row makes attention fail before any launch
+    cache.reset_row(0)
+    with pytest.raises(kv.KiviError) as e:
+        cache.attend(q.to(DEV))
+    assert e.value.status == "KIVI_E_EMPTY"
