@@ -191,7 +191,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_7b_layer",
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
-                             "gqa_ragged"])
+                             "gqa_ragged", "gqa_paged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--profile", action="store_true",
@@ -207,7 +207,7 @@ def main():
     import torch
 
     import kv_cache_compression_kivi_amd as kv
-    from kivi_inputs import CONFIGS, KVWorkload, row_lengths
+    from kivi_inputs import CONFIGS, KVWorkload, page_order, row_lengths
 
     kv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -238,7 +238,13 @@ def main():
             bits = layer_bits[layer]
             wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], layer=layer + 1000 * r, device=dev)
             k, v = wl.kv(0, T)
-            c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev)
+            if cfg.get("paged"):
+                # a pool page for every block a row can hold, the table taking them in a seeded random order
+                mb = max_tokens // 32
+                c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev, n_pages=B * mb)
+                c.set_block_table(page_order(B * mb, cfg["seed"] + 1000 * len(caches)).reshape(B, mb).to(dev))
+            else:
+                c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev)
             if cfg.get("ragged"):
                 c.append_rows(k, v, lens)
             else:
@@ -399,6 +405,7 @@ def main():
                    "bits": layer_bits if layers > 1 else layer_bits[0], "layers": layers,
                    "k_block": 32, "v_group": 32, "residual": 128, "q_dtype": str(q_dtype).replace("torch.", ""),
                    "step": "append 1 token + flush when due + decode attention, per layer",
+                   "blocks": "paged (pool pages in random order)" if cfg.get("paged") else "one region per unit",
                    "rotating_caches": n_rot},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "quantize_append_tokens_per_s": round(pf_tok_s, 1),

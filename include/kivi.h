@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KIVI_ABI_VERSION 2
+#define KIVI_ABI_VERSION 3
 
 typedef enum {
     KIVI_OK = 0,
@@ -66,7 +66,13 @@ enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
  * kivi_decode_step add the same number of tokens to every row, while
  * kivi_append_rows and kivi_reset_row let rows differ in length (a batch of
  * at most KIVI_MAX_RAGGED_BATCH rows then). Each row follows the same rules
- * (residual ring, flushes) as a batch of one. */
+ * (residual ring, flushes) as a batch of one.
+ *
+ * Paged blocks (n_pages > 0), for serving: the quantized blocks live in a
+ * pool of n_pages pages instead of one region per unit. A page holds one
+ * key block (G tokens) of one sequence for all its KV heads, and a block
+ * table that the caller owns maps (row, block) to a page; see
+ * kivi_set_block_table. Requires batch <= KIVI_MAX_RAGGED_BATCH. */
 typedef struct {
     int32_t batch;       /* B */
     int32_t n_kv_heads;  /* Hkv; a "unit" is one (batch row, KV head): unit = b * Hkv + h */
@@ -78,13 +84,17 @@ typedef struct {
     int32_t residual;    /* R: tokens kept fp16 after a flush */
     int32_t max_tokens;  /* capacity of every sequence */
     int32_t max_splits;  /* split-K partial slots per query head (0 = default) */
+    int32_t n_pages;     /* 0: one contiguous region per unit; > 0: pages in the shared pool */
 } kivi_config;
 
 /* Device-memory layout of a cache, a pure function of the config. All offsets
  * are in bytes from the start of the cache memory and are multiples of 256.
  *
  * Quantized blocks: unit u, key block j (tokens [jG, jG+G)) is one record at
- *   off_blocks + u * unit_stride + j * block_bytes, holding in order:
+ *   off_blocks + u * unit_stride + j * block_bytes (n_pages = 0), or, with
+ *   paged blocks, at off_blocks + (table[b][j] * Hkv + h) * block_bytes for
+ *   unit u = b * Hkv + h (a page is page_bytes = Hkv * block_bytes, the pool
+ *   n_pages pages, and unit_stride is 0). A record holds in order:
  *     kcode [G][W] uint32   W = head_dim * bits / 32 words per token (token-major)
  *     vcode [head_dim][bits] uint32   bits words per channel (channel-major)
  *     ksz   [head_dim][2] float32   (scale, zero) of each channel over the block
@@ -109,6 +119,8 @@ typedef struct {
     int64_t ring_slots; /* R + G */
     size_t off_partial, partial_stride;
     int32_t max_splits;
+    int32_t n_pages;    /* pages in the pool (0: not paged) */
+    size_t page_bytes;  /* Hkv * block_bytes (paged) */
 } kivi_layout;
 
 /* Counters of a cache. Tokens [0, n_quant) are quantized, [n_quant, n_tokens)
@@ -154,6 +166,21 @@ int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, v
  * rows would differ in length with batch > KIVI_MAX_RAGGED_BATCH. */
 int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int32_t* ntok, int32_t max_ntok,
                      void* stream);
+
+/* The block table of a paged cache: device int32 [batch][stride] (stride >=
+ * max_blocks), caller-owned, read by the kernels of every later call on the
+ * handle. Entry [b][j] is the page that holds row b's key block j. Before a
+ * call quantizes block j of row b (an append or flush that takes the row past
+ * (j + 1) G quantized tokens) and for as long as the row holds it, the entry
+ * must name a page in [0, n_pages) that no other (row, block) of the cache
+ * uses; rows may take pages in any order, and a page freed by kivi_reset_row
+ * may go to another row. The kernels clamp entries into [0, n_pages), so a
+ * wrong table gives wrong results, never an access outside the pool. Call it
+ * again to move the table; the caller orders its writes to the table before
+ * the calls that read it on the stream. KIVI_E_INVAL on a cache that is not
+ * paged; every append, flush or attention on a paged cache without a table
+ * returns KIVI_E_INVAL. */
+int kivi_set_block_table(kivi_cache* cache, const int32_t* table, int32_t stride);
 
 /* Empty sequence `row` (host counters only; launches nothing), so that a new
  * sequence can take the row. KIVI_E_UNSUPPORTED if the rows would then differ

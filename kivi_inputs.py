@@ -32,7 +32,9 @@ tokens T, T+1, ... is reproducible from (S, L) and the positions alone.
 
 Batches whose sequences differ in length (a serving batch) draw one length per
 batch row, uniform over the integers [T_min, T_max], from a generator seeded
-with hash(S, 3); row b then holds tokens [0, len[b]) of its chunk draws.
+with hash(S, 3); row b then holds tokens [0, len[b]) of its chunk draws. A
+paged cache's block table takes the pages in a random order: a permutation of
+the pool drawn from a generator seeded with hash(S, 4).
 """
 
 from __future__ import annotations
@@ -106,6 +108,13 @@ def row_lengths(batch: int, t_min: int, t_max: int, seed: int) -> list:
     return [int(x) for x in torch.randint(t_min, t_max + 1, (batch,), generator=g)]
 
 
+def page_order(n_pages: int, seed: int) -> torch.Tensor:
+    """Seeded random permutation of page indices [0, n_pages), int32."""
+    g = torch.Generator()
+    g.manual_seed(_mix(seed, 4))
+    return torch.randperm(n_pages, generator=g).to(torch.int32)
+
+
 # The workloads the method is measured on. `T` is the number of tokens
 # appended before the decode attention; "prefill" means append(T) then flush.
 CONFIGS = {
@@ -120,4 +129,8 @@ CONFIGS = {
     # uniform over [512, 8192] tokens (T is the longest possible).
     "gqa_ragged": dict(batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=6,
                        ragged=(512, 8192)),
+    # The same serving batch with paged blocks: every row's blocks on pages of a
+    # shared pool, taken in a random order.
+    "gqa_paged": dict(batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=6,
+                      ragged=(512, 8192), paged=True),
 }

@@ -35,6 +35,7 @@ from ._native import (  # noqa: F401
     kivi_plan_attend,
     kivi_query_row,
     kivi_reset_row,
+    kivi_set_block_table,
     kivi_set_attend_splits,
     kivi_state,
     library_path,

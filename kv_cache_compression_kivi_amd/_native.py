@@ -27,7 +27,7 @@ class KiviError(RuntimeError):
 class kivi_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_kv_heads", "n_q_heads", "head_dim", "bits", "k_block", "v_group",
-        "residual", "max_tokens", "max_splits")]
+        "residual", "max_tokens", "max_splits", "n_pages")]
 
 
 class kivi_layout(ctypes.Structure):
@@ -41,6 +41,7 @@ class kivi_layout(ctypes.Structure):
         ("ring_slots", ctypes.c_int64),
         ("off_partial", ctypes.c_size_t), ("partial_stride", ctypes.c_size_t),
         ("max_splits", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32), ("page_bytes", ctypes.c_size_t),
     ]
 
 
@@ -70,6 +71,7 @@ _SIGS = {
     "kivi_decode_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]),
     "kivi_append_rows": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _P]),
     "kivi_reset_row": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "kivi_set_block_table": (ctypes.c_int, [_P, _P, ctypes.c_int32]),
     "kivi_query_row": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(kivi_state)]),
 }
 
@@ -147,6 +149,10 @@ def kivi_append_rows(h: int, k_ptr: int, v_ptr: int, ntok, max_ntok: int, stream
                                            arr, max_ntok, ctypes.c_void_p(stream)))
 
 
+def kivi_set_block_table(h: int, table_ptr: int, stride: int) -> None:
+    _check(load_library().kivi_set_block_table(ctypes.c_void_p(h), ctypes.c_void_p(table_ptr), stride))
+
+
 def kivi_reset_row(h: int, row: int) -> None:
     _check(load_library().kivi_reset_row(ctypes.c_void_p(h), row))
 
@@ -201,9 +207,9 @@ def kivi_set_attend_splits(h: int, n_key_splits: int) -> None:
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual=128, k_block=32,
-                v_group=32, max_splits=0) -> kivi_config:
+                v_group=32, max_splits=0, n_pages=0) -> kivi_config:
     return kivi_config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_block, v_group, residual, max_tokens,
-                       max_splits)
+                       max_splits, n_pages)
 
 
 class KiviCache:
@@ -214,10 +220,11 @@ class KiviCache:
     """
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual=128,
-                 k_block=32, v_group=32, max_splits=0, device="cuda", memory=None):
+                 k_block=32, v_group=32, max_splits=0, device="cuda", memory=None, n_pages=0):
         import torch
         self.cfg = make_config(batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual,
-                               k_block, v_group, max_splits)
+                               k_block, v_group, max_splits, n_pages)
+        self.block_table = None
         self.nbytes = kivi_cache_bytes(self.cfg)
         self.layout = kivi_cache_layout(self.cfg)
         if memory is None:
@@ -267,6 +274,16 @@ class KiviCache:
         if len(ntok) != self.cfg.batch:
             raise ValueError(f"ntok must have {self.cfg.batch} entries, got {len(ntok)}")
         kivi_append_rows(self.handle, k.data_ptr(), v.data_ptr(), ntok, int(k.shape[2]), self._stream(stream))
+
+    def set_block_table(self, table):
+        """Paged caches: `table` is a device int32 [batch, stride] tensor (stride >=
+        max_blocks) mapping (row, block) to a page; it is kept referenced here."""
+        import torch
+        if table.dtype != torch.int32 or not table.is_cuda or not table.is_contiguous() or table.dim() != 2 \
+                or table.shape[0] != self.cfg.batch:
+            raise ValueError("the block table must be a contiguous int32 [batch, stride] device tensor")
+        kivi_set_block_table(self.handle, table.data_ptr(), int(table.shape[1]))
+        self.block_table = table
 
     def reset_row(self, row):
         kivi_reset_row(self.handle, row)

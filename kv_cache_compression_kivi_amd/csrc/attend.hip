@@ -263,10 +263,21 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const uint8_t* ubase = g.base + g.off_blocks + (size_t)u * g.unit_stride;
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)cnt.n_blocks * L::bytes);
     const LaneOffsets lo = lane_offsets<D, BITS, CW>(lane, w, tl);
+    // key block j into r: an offset into the unit's records, or (paged blocks,
+    // built with a row table) its own page's record
+    auto issue = [&](int j, B& r) {
+        if constexpr (RAGGED) {
+            if (g.table) {
+                load_block<D, BITS>(records(g.base + record_offset(g, u, j), L::bytes), 0u, lo, r);
+                return;
+            }
+        }
+        load_block<D, BITS>(rs, (uint32_t)(j * L::bytes), lo, r);
+    };
     B rr[PF];
 #pragma unroll
     for (int k = 0; k < NP; ++k)
-        if (j0 + k * NWAVES < j1) load_block<D, BITS>(rs, (uint32_t)((j0 + k * NWAVES) * L::bytes), lo, rr[k]);
+        if (j0 + k * NWAVES < j1) issue(j0 + k * NWAVES, rr[k]);
 
     // residual chunks (fp16 rows from the ring) are computed first, while the
     // first blocks are in flight (memory is idle once the last block lands, so
@@ -518,7 +529,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
 #pragma unroll
             for (int e = 0; e < NP; ++e) {
                 const int jn = jj + (NP + e) * NWAVES;
-                if (jn < j1) load_block<D, BITS>(rs, (uint32_t)(jn * L::bytes), lo, rr[(1 - h) * NP + e]);
+                if (jn < j1) issue(jn, rr[(1 - h) * NP + e]);
             }
             if (NP == 2 && jj + NWAVES < j1)
                 blocks_math(std::integral_constant<int, NP>(), &rr[h * NP]);

@@ -247,6 +247,13 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
     static_assert(QG * D * 4 <= L::bytes, "the output rows fit in one slot");
     auto stage = [&](int j, int k) {
+        if constexpr (RAGGED) {
+            if (g.table) {  // paged blocks: the block's own page
+                stage_record<NL>(records(g.base + record_offset(g, u, j), L::bytes), 0u, stage_lds + k * L::bytes,
+                                 16u * lane);
+                return;
+            }
+        }
         stage_record<NL>(rs, (uint32_t)j * L::bytes, stage_lds + k * L::bytes, 16u * lane);
     };
     // this lane's shares of a staged block

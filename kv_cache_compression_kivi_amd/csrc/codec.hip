@@ -117,7 +117,7 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     }
     __syncthreads();
 
-    uint8_t* rec = g.base + g.off_blocks + (size_t)u * g.unit_stride + (size_t)j * g.block_bytes;
+    uint8_t* rec = g.base + record_offset(g, u, j);
     uint8_t codes[kG];  // kG == kVG
     if (tid < D) {
         const int c = tid;

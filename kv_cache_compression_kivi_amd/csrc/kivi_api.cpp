@@ -23,6 +23,9 @@ struct kivi_cache {
     size_t bytes;
     // per batch row (sequence): tokens held, and how many of them are quantized
     std::vector<int64_t> nt, nq;
+    // paged blocks: the caller's device block table [batch][table_stride]
+    const int32_t* table;
+    int64_t table_stride;
     int32_t forced_splits;
     bool poisoned;
 };
@@ -62,13 +65,24 @@ kivi::CacheGeom geom(const kivi_cache* c) {
     g.n_q_heads = c->cfg.n_q_heads;
     g.head_dim = c->cfg.head_dim;
     g.bits = c->cfg.bits;
+    g.table = c->cfg.n_pages > 0 ? c->table : nullptr;
+    g.table_stride = c->table_stride;
+    g.n_pages = c->cfg.n_pages;
     return g;
+}
+
+bool paged(const kivi_cache* c) { return c->cfg.n_pages > 0; }
+
+// A paged cache's calls need the block table.
+int check_table(const kivi_cache* c) {
+    if (paged(c) && !c->table) return fail(KIVI_E_INVAL, "paged cache without a block table (kivi_set_block_table)");
+    return KIVI_OK;
 }
 
 int check_handle(const kivi_cache* c) {
     if (!c) return fail(KIVI_E_INVAL, "cache handle is NULL");
     if (c->poisoned) return fail(KIVI_E_STATE, "cache saw an earlier device failure; reset it");
-    return KIVI_OK;
+    return check_table(c);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -251,7 +265,8 @@ int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, v
         for (int b = 0; b < B; ++b) t_new[b] = (*appended)[b] ? cache->nt[b] - 1 : -1;
     a.rows.n = 0;
     a.cost_max = cost_max;
-    if (rows_agree(cache) && all_same(t_new)) {
+    // paged blocks are read by the kernels built with a row table
+    if (!paged(cache) && rows_agree(cache) && all_same(t_new)) {
         a.n_tokens = cache->nt[0];
         a.n_quant = cache->nq[0];
         a.n_blocks = cache->nq[0] / cache->cfg.k_block;
@@ -333,6 +348,8 @@ int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_
     c->bytes = bytes;
     c->nt.assign(cfg->batch, 0);
     c->nq.assign(cfg->batch, 0);
+    c->table = nullptr;
+    c->table_stride = 0;
     c->forced_splits = 0;
     c->poisoned = false;
     *out = c;
@@ -353,10 +370,23 @@ int kivi_cache_reset(kivi_cache* cache) {
     return KIVI_OK;
 }
 
+int kivi_set_block_table(kivi_cache* cache, const int32_t* table, int32_t stride) {
+    if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
+    if (!paged(cache)) return fail(KIVI_E_INVAL, "the cache is not paged (n_pages = 0)");
+    if (!table || ((uintptr_t)table & 3u) != 0) return fail(KIVI_E_INVAL, "table must be a 4-byte aligned device pointer");
+    if (stride < cache->L.max_blocks)
+        return fail(KIVI_E_INVAL, "stride " + std::to_string(stride) + " < max_blocks " +
+                                      std::to_string(cache->L.max_blocks));
+    cache->table = table;
+    cache->table_stride = stride;
+    return KIVI_OK;
+}
+
 int kivi_reset_row(kivi_cache* cache, int32_t row) {
-    int rc = check_handle(cache);
+    if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
+    if (cache->poisoned) return fail(KIVI_E_STATE, "cache saw an earlier device failure; reset it");
+    int rc = check_row(cache, row);
     if (rc != KIVI_OK) return rc;
-    if ((rc = check_row(cache, row)) != KIVI_OK) return rc;
     const int64_t nt = cache->nt[row], nq = cache->nq[row];
     cache->nt[row] = 0;
     cache->nq[row] = 0;

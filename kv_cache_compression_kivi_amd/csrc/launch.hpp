@@ -20,7 +20,27 @@ struct CacheGeom {
     size_t off_partial, partial_stride;  // partial_stride in bytes
     int32_t max_splits;
     int32_t batch, n_kv_heads, n_q_heads, head_dim, bits;
+    // paged blocks: the caller's block table [batch][table_stride] of page
+    // indices into a pool of n_pages pages (Hkv records each); null when each
+    // unit has its own region
+    const int32_t* table;
+    int64_t table_stride;
+    int32_t n_pages;
 };
+
+// Byte offset, from the cache memory's start, of unit u's key block j. A
+// paged block's table entry is read through the scalar cache (the table is
+// constant during a launch), clamped into the pool.
+__device__ inline size_t record_offset(const CacheGeom& g, int64_t u, int64_t j) {
+    if (g.table) {
+        const int64_t b = u / g.n_kv_heads, h = u % g.n_kv_heads;
+        typedef const __attribute__((address_space(4))) int32_t* const_i32;
+        int32_t p = ((const_i32)g.table)[b * g.table_stride + j];
+        p = p < 0 ? 0 : (p >= g.n_pages ? g.n_pages - 1 : p);
+        return g.off_blocks + ((size_t)p * g.n_kv_heads + (size_t)h) * g.block_bytes;
+    }
+    return g.off_blocks + (size_t)u * g.unit_stride + (size_t)j * g.block_bytes;
+}
 
 // Sequences of one batch may hold different numbers of tokens. A launch over
 // such a batch carries one entry per batch row in a row table, passed with

@@ -64,6 +64,14 @@ inline int validate_config(const kivi_config* c, std::string& err) {
     }
     // the attention kernel addresses one sequence's key-block records as one
     // buffer with 32-bit offsets
+    if (c->n_pages < 0) {
+        err = "n_pages must be >= 0";
+        return KIVI_E_INVAL;
+    }
+    if (c->n_pages > 0 && c->batch > KIVI_MAX_RAGGED_BATCH) {
+        err = "paged blocks need batch <= " + std::to_string(KIVI_MAX_RAGGED_BATCH);
+        return KIVI_E_UNSUPPORTED;
+    }
     const int64_t W = (int64_t)c->head_dim * c->bits / 32;
     const int64_t block_bytes = 2 * 32 * W * 4 + (int64_t)c->head_dim * 8 + 32 * (c->head_dim / 32) * 8;
     if ((int64_t)(c->max_tokens / c->k_block) * block_bytes > (int64_t)0xffffffff) {
@@ -84,9 +92,19 @@ inline void compute_layout(const kivi_config* c, kivi_layout* L) {
     L->block_bytes = L->rec_vsz + G * (d / (size_t)c->v_group) * 8;
     L->max_blocks = c->max_tokens / c->k_block;
     L->off_blocks = 0;
-    L->unit_stride = align_up((size_t)L->max_blocks * L->block_bytes);
+    L->n_pages = c->n_pages;
+    size_t blocks_bytes;
+    if (c->n_pages > 0) {  // a pool of pages, each one block of every KV head of a sequence
+        L->unit_stride = 0;
+        L->page_bytes = (size_t)c->n_kv_heads * L->block_bytes;
+        blocks_bytes = (size_t)c->n_pages * L->page_bytes;
+    } else {
+        L->unit_stride = align_up((size_t)L->max_blocks * L->block_bytes);
+        L->page_bytes = 0;
+        blocks_bytes = (size_t)units * L->unit_stride;
+    }
     L->ring_slots = (int64_t)c->residual + c->k_block;
-    L->off_ring = align_up(L->off_blocks + (size_t)units * L->unit_stride);
+    L->off_ring = align_up(L->off_blocks + blocks_bytes);
     L->ring_unit_stride = align_up((size_t)L->ring_slots * 4 * d);
     L->off_partial = align_up(L->off_ring + (size_t)units * L->ring_unit_stride);
     L->max_splits = c->max_splits ? c->max_splits : kDefaultMaxSplits;

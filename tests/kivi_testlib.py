@@ -19,8 +19,16 @@ def gpu_unit_blocks(cache, unit: int, n_blocks: int):
     vsz [nb,G,d/32,2] f32), read through the layout the C ABI reports."""
     L, c = cache.layout, cache.cfg
     G, d, W = c.k_block, c.head_dim, c.head_dim * c.bits // 32
-    start = L.off_blocks + unit * L.unit_stride
-    raw = cache.memory[start:start + n_blocks * L.block_bytes].cpu().numpy().reshape(n_blocks, L.block_bytes)
+    if c.n_pages > 0:
+        # paged: block j of unit u = b * Hkv + h lives in page table[b][j], record h of the page
+        b, h = divmod(unit, c.n_kv_heads)
+        pages = cache.block_table[b, :n_blocks].cpu().numpy()
+        mem = cache.memory
+        raw = np.stack([mem[L.off_blocks + (int(p) * c.n_kv_heads + h) * L.block_bytes:][:L.block_bytes].cpu().numpy()
+                        for p in pages]) if n_blocks else np.zeros((0, L.block_bytes), np.uint8)
+    else:
+        start = L.off_blocks + unit * L.unit_stride
+        raw = cache.memory[start:start + n_blocks * L.block_bytes].cpu().numpy().reshape(n_blocks, L.block_bytes)
     kcode = raw[:, L.rec_kcode:L.rec_kcode + G * W * 4].copy().view(np.uint32).reshape(n_blocks, G, W)
     vcode = raw[:, L.rec_vcode:L.rec_vcode + G * W * 4].copy().view(np.uint32).reshape(n_blocks, d, c.bits)
     ksz = raw[:, L.rec_ksz:L.rec_ksz + d * 8].copy().view(np.float32).reshape(n_blocks, d, 2)

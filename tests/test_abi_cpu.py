@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(native):
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(native.EXPORTED)
-    assert native.kivi_abi_version() == 2
+    assert native.kivi_abi_version() == 3
     nm = subprocess.run(["nm", "-D", "--defined-only", native.library_path()], capture_output=True, text=True).stdout
     for name in declared:
         assert re.search(r"\bT " + name + r"\b", nm), name
@@ -185,6 +185,45 @@ def test_ragged_batch_limit(native):
     finally:
         native.kivi_cache_destroy(h)
     assert "#define KIVI_MAX_RAGGED_BATCH 128" in open(HEADER, encoding="utf-8").read()
+
+
+def test_paged_layout_and_validation(native):
+    """Paged blocks: the pool replaces the per-unit regions in the layout, and
+    the block-table rules are enforced before anything is launched."""
+    for bad, status in [(dict(n_pages=-1), "KIVI_E_INVAL"),
+                        (dict(n_pages=10, batch=129, n_kv_heads=1, n_q_heads=1), "KIVI_E_UNSUPPORTED")]:
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_cache_bytes(_cfg(native, **bad))
+        assert e.value.status == status
+    cfg = _cfg(native, n_pages=37)  # batch 2, 4 KV heads, d 128, b 2, 1000 tokens
+    L = native.kivi_cache_layout(cfg)
+    assert L.n_pages == 37 and L.unit_stride == 0 and L.page_bytes == 4 * L.block_bytes == 4 * 4096
+    assert L.off_ring >= 37 * L.page_bytes and L.off_ring % 256 == 0
+    flat = native.kivi_cache_layout(_cfg(native))
+    assert flat.n_pages == 0 and flat.page_bytes == 0
+    assert L.total_bytes - L.off_ring == flat.total_bytes - flat.off_ring  # ring and partials unchanged
+    n = native.kivi_cache_bytes(cfg)
+    fake = 1 << 40
+    h = native.kivi_cache_create(cfg, fake, n)
+    try:
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_append(h, fake, fake, 1)
+        assert e.value.status == "KIVI_E_INVAL" and "block table" in native.kivi_last_error()
+        for ptr, stride in [(0, 31), (fake + 2, 31), (fake, 30)]:
+            with pytest.raises(native.KiviError) as e:
+                native.kivi_set_block_table(h, ptr, stride)
+            assert e.value.status == "KIVI_E_INVAL"
+        native.kivi_set_block_table(h, fake, 31)  # max_blocks = 1000 // 32 = 31
+        native.kivi_append_rows(h, fake, fake, [0, 0], 1)  # nothing to append: no launch
+    finally:
+        native.kivi_cache_destroy(h)
+    h = native.kivi_cache_create(_cfg(native), fake, native.kivi_cache_bytes(_cfg(native)))
+    try:
+        with pytest.raises(native.KiviError) as e:
+            native.kivi_set_block_table(h, fake, 31)
+        assert e.value.status == "KIVI_E_INVAL"
+    finally:
+        native.kivi_cache_destroy(h)
 
 
 # ---------------------------------------------------------------- host planner

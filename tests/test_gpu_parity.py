@@ -439,3 +439,82 @@ def test_ragged_rows_parity(B, Hkv, Hq, d, bits, R, lens):
     with pytest.raises(kv.KiviError) as e:
         cache.attend(q.to(DEV))
     assert e.value.status == "KIVI_E_EMPTY"
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,d,bits,R,lens", [
+    (4, 2, 2, 128, 2, 128, [700, 33, 161, 1]),        # MHA vector kernel
+    (3, 2, 8, 128, 4, 128, [450, 2000, 5]),           # four query heads per KV head (matrix cores)
+    (3, 2, 4, 64, 2, 32, [97, 640, 300]),             # d = 64, two query heads per KV head
+])
+def test_paged_blocks_parity(B, Hkv, Hq, d, bits, R, lens):
+    """Paged blocks: every (row, block) maps through a caller-owned block table
+    to a page of a shared pool, in scrambled order with spare pages. A ragged
+    prefill, attention at several split counts, decode steps whose flushes
+    write new pages, and a row emptied and refilled on other pages (some freed
+    by itself, some spare). Each row against an oracle cache of that row alone;
+    the bytes are read back page by page through the table."""
+    _announce("paged", B, Hkv, Hq, d, bits, R, lens)
+    steps = 40
+    T = max(lens)
+    max_tokens = T + steps + 80
+    max_blocks = max_tokens // 32
+    stride = max_blocks + 3
+    n_pages = B * max_blocks + 9
+    rng = np.random.default_rng(sum(lens) + bits)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    table = np.full((B, stride), -1, np.int32)   # -1 in unused entries: the kernels never need them
+    table[:, :max_blocks] = perm[:B * max_blocks].reshape(B, max_blocks)
+    spare = list(perm[B * max_blocks:])
+    wl = KVWorkload(B, Hkv, d, seed=sum(lens) + 3 * d, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV, n_pages=n_pages)
+    assert cache.layout.unit_stride == 0 and cache.layout.page_bytes == Hkv * cache.layout.block_bytes
+    tab = torch.from_numpy(table).to(DEV)
+    cache.set_block_table(tab)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    ocs = _row_oracles(k, v, lens, Hq, bits, max_tokens, R)
+    q = wl.q(Hq, step=0)
+    for n in (0, 1, 3, 17):
+        cache.set_attend_splits(n)
+        out = cache.attend(q.to(DEV))
+        torch.cuda.synchronize()
+        _check_rows(cache, ocs, out, q)
+    cache.set_attend_splits(0)
+    _check_bytes(cache, ocs)
+    for i in range(steps):
+        if i == 15:
+            # row 1 ends; its new sequence takes half of its old pages (reversed) and the spare ones
+            cache.reset_row(1)
+            old = list(table[1, :max_blocks])
+            new = (old[::-2] + spare + old[-2::-2])[:max_blocks]
+            spare = [p for p in old + spare if p not in set(new)]
+            table[1, :max_blocks] = np.array(new, np.int32)
+            tab.copy_(torch.from_numpy(table).to(DEV))
+            kn, vn = wl.kv(5000, 99)
+            ntok = [0] * B
+            ntok[1] = 99
+            cache.append_rows(kn.to(DEV), vn.to(DEV), ntok)
+            ocs[1] = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R)
+            ocs[1].append(kn[1:2].contiguous(), vn[1:2].contiguous())
+        kt, vt = wl.kv(T + i, 1)
+        qi = wl.q(Hq, step=i + 1)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), qi.to(DEV))
+        for b, oc in enumerate(ocs):
+            oc.append(kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+            nt, nq = oc.state()
+            if nt - nq >= R + 32:
+                oc.flush()
+        if i % 6 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            _check_rows(cache, ocs, out, qi)
+    torch.cuda.synchronize()
+    _check_bytes(cache, ocs)
+    # a paged cache refuses work without a table; a contiguous one refuses a table
+    plain = kv.KiviCache(1, 1, 1, d, bits, max_tokens=64, device=DEV)
+    with pytest.raises(kv.KiviError) as e:
+        plain.set_block_table(tab[:1].contiguous())
+    assert e.value.status == "KIVI_E_INVAL"
+    fresh = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV, n_pages=n_pages)
+    with pytest.raises(kv.KiviError) as e:
+        fresh.append_rows(k.to(DEV), v.to(DEV), lens)
+    assert e.value.status == "KIVI_E_INVAL"
