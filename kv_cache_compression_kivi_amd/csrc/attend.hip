@@ -264,11 +264,18 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
     const __amdgpu_buffer_rsrc_t rs = records(ubase, (uint64_t)cnt.n_blocks * L::bytes);
     const LaneOffsets lo = lane_offsets<D, BITS, CW>(lane, w, tl);
     // key block j into r: an offset into the unit's records, or (paged blocks,
-    // built with a row table) its own page's record
+    // built with a row table) its own page's record. A wave issues its blocks
+    // in order, j0, j0 + NWAVES, ...: each block's table entry was read one
+    // call earlier, and the call reads the next one, so no call waits on it.
+    int32_t pg_next = 0;
+    if constexpr (RAGGED)
+        if (g.table && j0 < j1) pg_next = table_entry(g, b, j0);
     auto issue = [&](int j, B& r) {
         if constexpr (RAGGED) {
             if (g.table) {
-                load_block<D, BITS>(records(g.base + record_offset(g, u, j), L::bytes), 0u, lo, r);
+                const int32_t p = pg_next;
+                if (j + NWAVES < j1) pg_next = table_entry(g, b, j + NWAVES);
+                load_block<D, BITS>(records(g.base + page_offset(g, p, h), L::bytes), 0u, lo, r);
                 return;
             }
         }

@@ -246,10 +246,18 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     // a wave's output rows at the end, in its first slot (no staging load is in flight then)
     auto s_o = [&](int wv) { return reinterpret_cast<float(*)[D]>(&s_stage[wv][0][0]); };
     static_assert(QG * D * 4 <= L::bytes, "the output rows fit in one slot");
+    // paged blocks (built with a row table): the block's own page. A wave
+    // stages its blocks in order, j0, j0 + NWAVES, ...: each block's table
+    // entry was read one call earlier, and the call reads the next one.
+    int32_t pg_next = 0;
+    if constexpr (RAGGED)
+        if (g.table && j0 < j1) pg_next = table_entry(g, b, j0);
     auto stage = [&](int j, int k) {
         if constexpr (RAGGED) {
-            if (g.table) {  // paged blocks: the block's own page
-                stage_record<NL>(records(g.base + record_offset(g, u, j), L::bytes), 0u, stage_lds + k * L::bytes,
+            if (g.table) {
+                const int32_t p = pg_next;
+                if (j + NWAVES < j1) pg_next = table_entry(g, b, j + NWAVES);
+                stage_record<NL>(records(g.base + page_offset(g, p, h), L::bytes), 0u, stage_lds + k * L::bytes,
                                  16u * lane);
                 return;
             }

@@ -28,17 +28,22 @@ struct CacheGeom {
     int32_t n_pages;
 };
 
-// Byte offset, from the cache memory's start, of unit u's key block j. A
-// paged block's table entry is read through the scalar cache (the table is
-// constant during a launch), clamped into the pool.
+// Paged blocks: the table entry of batch row b's key block j, read through
+// the scalar cache (the table is constant during a launch).
+__device__ inline int32_t table_entry(const CacheGeom& g, int64_t b, int64_t j) {
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    return ((const_i32)g.table)[b * g.table_stride + j];
+}
+
+// Byte offset of KV head h's record in page p, the entry clamped into the pool.
+__device__ inline size_t page_offset(const CacheGeom& g, int32_t p, int64_t h) {
+    p = p < 0 ? 0 : (p >= g.n_pages ? g.n_pages - 1 : p);
+    return g.off_blocks + ((size_t)p * g.n_kv_heads + (size_t)h) * g.block_bytes;
+}
+
+// Byte offset, from the cache memory's start, of unit u's key block j.
 __device__ inline size_t record_offset(const CacheGeom& g, int64_t u, int64_t j) {
-    if (g.table) {
-        const int64_t b = u / g.n_kv_heads, h = u % g.n_kv_heads;
-        typedef const __attribute__((address_space(4))) int32_t* const_i32;
-        int32_t p = ((const_i32)g.table)[b * g.table_stride + j];
-        p = p < 0 ? 0 : (p >= g.n_pages ? g.n_pages - 1 : p);
-        return g.off_blocks + ((size_t)p * g.n_kv_heads + (size_t)h) * g.block_bytes;
-    }
+    if (g.table) return page_offset(g, table_entry(g, u / g.n_kv_heads, j), u % g.n_kv_heads);
     return g.off_blocks + (size_t)u * g.unit_stride + (size_t)j * g.block_bytes;
 }
 
