@@ -372,6 +372,7 @@ def _check_bytes(cache, ocs):
     (3, 1, 4, 128, 2, 32, [64, 1000, 31]),            # four-query kernel at b = 2, small residual
     (3, 2, 4, 64, 2, 64, [300, 1, 97]),               # d = 64, two query heads per KV head
     (2, 1, 2, 256, 4, 128, [129, 517]),               # d = 256
+    (2, 1, 4, 256, 2, 64, [300, 45]),                 # four query heads on the vector kernel (d = 256)
 ])
 def test_ragged_rows_parity(B, Hkv, Hq, d, bits, R, lens):
     """Sequences of different lengths in one batch (the per-row entry points):
@@ -445,6 +446,7 @@ def test_ragged_rows_parity(B, Hkv, Hq, d, bits, R, lens):
     (4, 2, 2, 128, 2, 128, [700, 33, 161, 1]),        # MHA vector kernel
     (3, 2, 8, 128, 4, 128, [450, 2000, 5]),           # four query heads per KV head (matrix cores)
     (3, 2, 4, 64, 2, 32, [97, 640, 300]),             # d = 64, two query heads per KV head
+    (2, 1, 4, 256, 4, 64, [45, 300]),                 # d = 256, four query heads on the vector kernel
 ])
 def test_paged_blocks_parity(B, Hkv, Hq, d, bits, R, lens):
     """Paged blocks: every (row, block) maps through a caller-owned block table
