@@ -68,6 +68,10 @@ enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
  * at most KIVI_MAX_RAGGED_BATCH rows then). Each row follows the same rules
  * (residual ring, flushes) as a batch of one.
  *
+ * Serving batches follow the page's Production Deployment Guide (KIVI inside a
+ * vLLM inference server): sequences of different lengths share a batch, and
+ * each keeps its own residual buffer (section 残差バッファ).
+ *
  * Paged blocks (n_pages > 0), for serving: the quantized blocks live in a
  * pool of n_pages pages instead of one region per unit. A page holds one
  * key block (G tokens) of one sequence for all its KV heads, and a block
@@ -158,7 +162,7 @@ int kivi_cache_reset(kivi_cache* cache);
 int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, void* stream);
 
 /* Append ntok[b] >= 0 tokens to sequence b, each row by the rules of
- * kivi_append. k, v: device fp16 [B][Hkv][max_ntok][d], contiguous; row b's
+ * kivi_append (each sequence's own residual buffer, section 残差バッファ). k, v: device fp16 [B][Hkv][max_ntok][d], contiguous; row b's
  * tokens are its first ntok[b] of the max_ntok slots. ntok: host array of B
  * entries, each in [0, max_ntok]. For prefilling sequences of different
  * lengths, or one row (the others 0) when a new sequence takes a freed row.
