@@ -33,8 +33,9 @@
 // lane tl owns tokens tl, tl + TL, ... of every 32-token chunk. Reductions use DPP inside
 // rows of 16 lanes and permlane swaps across rows: VALU only, no LDS traffic.
 // Block records are read with buffer loads: the unit's records are one
-// buffer, the block offset is a scalar and each lane's offsets are constants,
-// so no vector instruction goes to address arithmetic.
+// buffer (paged blocks: each block's page record is one), the block offset is
+// a scalar and each lane's offsets are constants, so no vector instruction
+// goes to address arithmetic.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 

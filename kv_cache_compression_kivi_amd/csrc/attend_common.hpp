@@ -173,7 +173,8 @@ struct BlockRegs {
     float2 vsz[TPL];             // (s, z) of each token's value group that holds column w
 };
 
-// The unit's records as one buffer (offsets past `bytes` read as zero).
+// `bytes` of records from `base` as one buffer: a unit's records, or one
+// paged block's record (offsets past `bytes` read as zero).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t records(const uint8_t* base, uint64_t bytes) {
     const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n, 0x00020000);
