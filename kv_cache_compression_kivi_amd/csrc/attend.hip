@@ -314,20 +314,24 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         }
 #pragma unroll
         for (int t = 0; t < kG; ++t) {
+            // tokens past the residual's end read the first token's slot and
+            // are zeroed: their weight is 0, and that slot may not hold a
+            // finite row yet (it is the new token's, written by this call)
             const int idx = ck * kG + t;
-            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            const bool tv = idx < (int)nres;
+            int slot = slot0 + (tv ? idx : 0);
             slot -= slot >= ring ? ring : 0;
             const uint8_t* vp = cnt.n_quant + idx == cnt.t_new
                                     ? reinterpret_cast<const uint8_t*>(a.v_new + u * D + cv0)
                                     : rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
             if constexpr (CPV == 1) {
-                vr[t][0] = *reinterpret_cast<const uint16_t*>(vp);
+                vr[t][0] = tv ? *reinterpret_cast<const uint16_t*>(vp) : 0u;
             } else if constexpr (CPV == 2) {
-                vr[t][0] = *reinterpret_cast<const uint32_t*>(vp);
+                vr[t][0] = tv ? *reinterpret_cast<const uint32_t*>(vp) : 0u;
             } else {
                 const uint2 x = *reinterpret_cast<const uint2*>(vp);
-                vr[t][0] = x.x;
-                vr[t][1] = x.y;
+                vr[t][0] = tv ? x.x : 0u;
+                vr[t][1] = tv ? x.y : 0u;
             }
         }
     };

@@ -565,12 +565,16 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
         uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
 #pragma unroll
         for (int t = 0; t < kG; ++t) {
+            // tokens past the residual's end are zeroed (weight 0; the slot they
+            // read may not hold a finite row yet)
             const int idx = ck * kG + t;
-            int slot = slot0 + (idx < (int)nres ? idx : 0);
+            const bool tv = idx < (int)nres;
+            int slot = slot0 + (tv ? idx : 0);
             slot -= slot >= ring ? ring : 0;
-            vr[t] = cnt.n_quant + idx == cnt.t_new
-                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
-                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
+            const uint32_t x = cnt.n_quant + idx == cnt.t_new
+                                   ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
+                                   : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
+            vr[t] = tv ? x : 0u;
         }
         float sc[QG][TPL];
 #pragma unroll

@@ -520,3 +520,108 @@ def test_paged_blocks_parity(B, Hkv, Hq, d, bits, R, lens):
     with pytest.raises(kv.KiviError) as e:
         fresh.append_rows(k.to(DEV), v.to(DEV), lens)
     assert e.value.status == "KIVI_E_INVAL"
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["regions", "paged"])
+@pytest.mark.parametrize("Hq,d,bits,R", [(2, 64, 4, 0), (8, 128, 2, 32), (4, 128, 4, 128)])
+def test_row_operations_random_walk(paged, Hq, d, bits, R):
+    """A seeded random sequence of per-row operations on a batch of 5 sequences:
+    ragged appends of 0-70 tokens a row, uniform appends, flushes, decode
+    steps, rows emptied (and, paged, moved onto other pages), attention at a
+    random forced split count. After every attention each row matches an
+    oracle cache of that row alone; at the end every unit's bytes match."""
+    _announce("random walk", paged, Hq, d, bits, R)
+    B, Hkv = 5, 2
+    max_tokens = 700
+    mb = max_tokens // 32
+    rng = np.random.default_rng(1000 * bits + d + R + paged)
+    wl = KVWorkload(B, Hkv, d, seed=int(rng.integers(1 << 30)), device="cpu")
+    kw = dict(max_tokens=max_tokens, residual=R, device=DEV)
+    if paged:
+        n_pages = B * mb + 11
+        kw["n_pages"] = n_pages
+        free = list(rng.permutation(n_pages).astype(np.int32))
+        table = np.zeros((B, mb), np.int32)
+        for b in range(B):
+            table[b] = [free.pop() for _ in range(mb)]
+        tab = torch.from_numpy(table).to(DEV)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, **kw)
+    if paged:
+        cache.set_block_table(tab)
+    ocs = [oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R) for _ in range(B)]
+    pos = 0
+    for step in range(60):
+        op = rng.choice(["rows", "rows", "uniform", "flush", "decode", "decode", "reset", "attend"])
+        lens = [oc.state()[0] for oc in ocs]
+        if op == "rows":
+            ntok = [int(x) if lens[b] + x <= max_tokens - 40 else 0 for b, x in enumerate(rng.integers(0, 71, B))]
+            k, v = wl.kv(pos, max(ntok) or 1)
+            pos += 71
+            cache.append_rows(k.to(DEV), v.to(DEV), ntok)
+            for b in range(B):
+                if ntok[b]:
+                    ocs[b].append(k[b:b + 1, :, :ntok[b]].contiguous(), v[b:b + 1, :, :ntok[b]].contiguous())
+        elif op == "uniform" and max(lens) + 9 <= max_tokens - 40:
+            k, v = wl.kv(pos, 9)
+            pos += 9
+            cache.append(k.to(DEV), v.to(DEV))
+            for b in range(B):
+                ocs[b].append(k[b:b + 1].contiguous(), v[b:b + 1].contiguous())
+        elif op == "flush":
+            assert cache.flush() == max(oc.flush() for oc in ocs)
+        elif op == "decode" and max(lens) + 1 <= max_tokens - 40:
+            k, v = wl.kv(pos, 1)
+            pos += 1
+            q = wl.q(Hq, step=step)
+            out = cache.decode_step(k.to(DEV), v.to(DEV), q.to(DEV))
+            for b in range(B):
+                ocs[b].append(k[b:b + 1].contiguous(), v[b:b + 1].contiguous())
+                nt, nq = ocs[b].state()
+                if nt - nq >= R + 32:
+                    ocs[b].flush()
+            torch.cuda.synchronize()
+            _check_rows(cache, ocs, out, q)
+        elif op == "reset":
+            b = int(rng.integers(B))
+            cache.reset_row(b)
+            ocs[b] = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R)
+            if paged:  # the row's pages go back to the pool; it takes others
+                free = list(table[b]) + free
+                rng.shuffle(free)
+                table[b] = [free.pop() for _ in range(mb)]
+                tab.copy_(torch.from_numpy(table).to(DEV))
+        elif op == "attend" and min(lens) > 0:
+            cache.set_attend_splits(int(rng.choice([0, 1, 2, 5, 13])))
+            q = wl.q(Hq, step=step, dtype=torch.bfloat16)
+            out = cache.attend(q.to(DEV))
+            torch.cuda.synchronize()
+            _check_rows(cache, ocs, out, q, q_bf16=True)
+            cache.set_attend_splits(0)
+        for b in range(B):
+            assert cache.row_state(b)[:2] == ocs[b].state(), (step, op, b)
+    torch.cuda.synchronize()
+    _check_bytes(cache, ocs)
+
+
+@pytest.mark.parametrize("Hq,bits", [(1, 2), (2, 4), (4, 2)], ids=["mha", "group2", "group4"])
+def test_unwritten_ring_slots_never_reach_the_output(Hq, bits):
+    """Cache memory filled with NaN bit patterns before use: decode steps from an
+    empty cache read partial residual chunks whose unused token lanes point at
+    ring slots this call has not written yet. Their weight is zero, and so must
+    be their contribution: outputs stay finite and match the oracle."""
+    _announce("unwritten slots", Hq, bits)
+    B, Hkv, d, steps = 2, 2, 128, 40
+    wl = KVWorkload(B, Hkv, d, seed=77 + Hq, device="cpu")
+    cfg = kv._native.make_config(B, Hkv, Hkv * Hq, d, bits, steps)
+    mem = torch.full((kv.kivi_cache_bytes(cfg),), 0xFF, dtype=torch.uint8, device=DEV)  # fp16 0xFFFF is a NaN
+    cache = kv.KiviCache(B, Hkv, Hkv * Hq, d, bits, max_tokens=steps, device=DEV, memory=mem)
+    oc = oracle.OracleCache(B, Hkv, Hkv * Hq, d, bits, max_tokens=steps)
+    for i in range(steps):
+        kt, vt = wl.kv(i, 1)
+        q = wl.q(Hkv * Hq, step=i)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), q.to(DEV))
+        oc.append(kt, vt)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.isfinite(got).all(), i
+        assert_attention_close(got, oc.attend(q))
