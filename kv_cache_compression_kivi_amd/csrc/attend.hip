@@ -303,10 +303,11 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         for (int i = 0; i < TPL; ++i) {
             const int idx = ck * kG + tl + TL * i;
             valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);  // idx < ring: one wrap at most
+            const int ie = valid[i] ? idx : (int)nres - 1;  // past the end: the last token's row
+            int slot = slot0 + ie;  // ie < ring: one wrap at most
             slot -= slot >= ring ? ring : 0;
             // the token appended by this call comes from its input row
-            const uint4* kp = cnt.n_quant + idx == cnt.t_new
+            const uint4* kp = cnt.n_quant + ie == cnt.t_new
                                   ? reinterpret_cast<const uint4*>(a.k_new + u * D + CW * w)
                                   : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 2 * CW * w);
 #pragma unroll
@@ -314,24 +315,25 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         }
 #pragma unroll
         for (int t = 0; t < kG; ++t) {
-            // tokens past the residual's end read the first token's slot and
-            // are zeroed: their weight is 0, and that slot may not hold a
-            // finite row yet (it is the new token's, written by this call)
+            // tokens past the residual's end (weight 0) read the last token's
+            // row, which is finite: it is in the ring, or it is the new token's
+            // input row (the first residual slot is not written yet when the
+            // new token is the only one)
             const int idx = ck * kG + t;
-            const bool tv = idx < (int)nres;
-            int slot = slot0 + (tv ? idx : 0);
+            const int ie = idx < (int)nres ? idx : (int)nres - 1;
+            int slot = slot0 + ie;
             slot -= slot >= ring ? ring : 0;
-            const uint8_t* vp = cnt.n_quant + idx == cnt.t_new
+            const uint8_t* vp = cnt.n_quant + ie == cnt.t_new
                                     ? reinterpret_cast<const uint8_t*>(a.v_new + u * D + cv0)
                                     : rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0;
             if constexpr (CPV == 1) {
-                vr[t][0] = tv ? *reinterpret_cast<const uint16_t*>(vp) : 0u;
+                vr[t][0] = *reinterpret_cast<const uint16_t*>(vp);
             } else if constexpr (CPV == 2) {
-                vr[t][0] = tv ? *reinterpret_cast<const uint32_t*>(vp) : 0u;
+                vr[t][0] = *reinterpret_cast<const uint32_t*>(vp);
             } else {
                 const uint2 x = *reinterpret_cast<const uint2*>(vp);
-                vr[t][0] = tv ? x.x : 0u;
-                vr[t][1] = tv ? x.y : 0u;
+                vr[t][0] = x.x;
+                vr[t][1] = x.y;
             }
         }
     };

@@ -554,9 +554,10 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
         for (int i = 0; i < TPL; ++i) {
             const int idx = ck * kG + tl + TL * i;
             valid[i] = idx < (int)nres;
-            int slot = slot0 + (valid[i] ? idx : 0);
+            const int ie = valid[i] ? idx : (int)nres - 1;  // past the end: the last token's row
+            int slot = slot0 + ie;
             slot -= slot >= ring ? ring : 0;
-            const uint4* kp = cnt.n_quant + idx == cnt.t_new
+            const uint4* kp = cnt.n_quant + ie == cnt.t_new
                                   ? reinterpret_cast<const uint4*>(a.k_new + u * D + 16 * w)
                                   : reinterpret_cast<const uint4*>(rbase + (size_t)slot * 4 * D + 32 * w);
             kraw[i][0] = kp[0];
@@ -565,16 +566,16 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
         uint32_t vr[kG];  // fp16 values of channels cv0, cv0 + 1, token t
 #pragma unroll
         for (int t = 0; t < kG; ++t) {
-            // tokens past the residual's end are zeroed (weight 0; the slot they
-            // read may not hold a finite row yet)
+            // tokens past the residual's end (weight 0) read the last token's
+            // row, which is finite (the first residual slot is not written yet
+            // when the new token is the only one)
             const int idx = ck * kG + t;
-            const bool tv = idx < (int)nres;
-            int slot = slot0 + (tv ? idx : 0);
+            const int ie = idx < (int)nres ? idx : (int)nres - 1;
+            int slot = slot0 + ie;
             slot -= slot >= ring ? ring : 0;
-            const uint32_t x = cnt.n_quant + idx == cnt.t_new
-                                   ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
-                                   : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
-            vr[t] = tv ? x : 0u;
+            vr[t] = cnt.n_quant + ie == cnt.t_new
+                        ? *reinterpret_cast<const uint32_t*>(a.v_new + u * D + cv0)
+                        : *reinterpret_cast<const uint32_t*>(rbase + (size_t)slot * 4 * D + 2 * D + 2 * cv0);
         }
         float sc[QG][TPL];
 #pragma unroll
