@@ -153,7 +153,7 @@ __device__ __forceinline__ void wait_staged(int later) {
 // Two 4-wave work-groups per CU (up to 256 VGPRs a lane: the value digit
 // sums stay in matrix-core accumulators across blocks).
 template <int D, int BITS, int NWAVES, bool RAGGED>
-__global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(const AttendArgs a) {
     constexpr int QG = 4;
     using B = BlockRegs<D, BITS>;
     using R = GqaRegs<D, BITS>;
@@ -713,13 +713,18 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void attend_gqa_kernel(const Attend
     }
 }
 
+// Rows that agree: two 4-wave work-groups per CU. With a row table (rows of
+// different lengths, paged blocks): one 8-wave work-group per CU, so that a
+// long row left running alone on its CU still has two waves per SIMD
+// (measured on MI355X: 1.5% faster on a 64-row serving batch, 5% paged).
 template <int BITS>
 hipError_t gqa_launch(const AttendArgs& a, hipStream_t s) {
     constexpr int NW = attend_waves(4, 128);
+    constexpr int NWR = attend_waves_rows(4, 128);
     const int group = a.g.n_q_heads / a.g.n_kv_heads;
     const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / 4));
     if (a.rows.n)
-        attend_gqa_kernel<128, BITS, NW, true><<<grid, 64 * NW, 0, s>>>(a);
+        attend_gqa_kernel<128, BITS, NWR, true><<<grid, 64 * NWR, 0, s>>>(a);
     else
         attend_gqa_kernel<128, BITS, NW, false><<<grid, 64 * NW, 0, s>>>(a);
     return hipGetLastError();

@@ -227,7 +227,7 @@ kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
     const int B = c->cfg.batch;
     const int32_t group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
     const int64_t G = c->cfg.k_block;
-    if (rows_agree(c)) {
+    if (rows_agree(c) && !paged(c)) {  // paged caches launch with a row table
         if (cost_max) *cost_max = kivi::unit_cost(c->nq[0] / G, c->nt[0] - c->nq[0]);
         return kivi::plan_attend((int64_t)B * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
                                  c->L.max_splits, c->forced_splits);

@@ -197,6 +197,7 @@ inline AttendPlan plan_attend_rows(int64_t n_kv_heads, int32_t group, int32_t he
                                    int64_t* cost_max) {
     AttendPlan p;
     attend_shape(group, head_dim, &p.qg, &p.nwaves);
+    p.nwaves = attend_waves_rows(p.qg, head_dim);
     const int64_t wgs_per_row = n_kv_heads * (group / p.qg);  // work-groups of one split of one row
     int64_t cmax = 1;
     for (int64_t r = 0; r < rows; ++r) cmax = cost[r] > cmax ? cost[r] : cmax;

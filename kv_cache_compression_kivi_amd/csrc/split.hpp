@@ -64,6 +64,13 @@ KIVI_HD constexpr int attend_waves(int qg, int head_dim) {
     return qg == 4 ? 4 : (qg == 2 && head_dim > 128 ? 4 : 8);
 }
 
+// Waves per work-group of the attention kernels launched with a row table
+// (rows of different lengths, paged blocks): 8 for the four-query kernel at
+// d = 128 (one work-group per CU), else as attend_waves.
+KIVI_HD constexpr int attend_waves_rows(int qg, int head_dim) {
+    return qg == 4 && head_dim == 128 ? 8 : attend_waves(qg, head_dim);
+}
+
 // Key blocks wave w of nw holds out of nbw.
 KIVI_HD inline int64_t wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return nbw / nw + (w < nbw % nw ? 1 : 0); }
 
