@@ -15,6 +15,9 @@
 #include "planner.hpp"
 
 static_assert(kivi::kMaxRaggedRows == KIVI_MAX_RAGGED_BATCH, "row tables hold the largest ragged batch");
+// the row tables ride in the kernel arguments, whose block is at most 4 KiB
+static_assert(sizeof(kivi::QuantArgs) <= 4096 && sizeof(kivi::RingArgs) <= 4096 && sizeof(kivi::AttendArgs) <= 4096,
+              "kernel arguments fit the 4 KiB argument block");
 
 struct kivi_cache {
     kivi_config cfg;
