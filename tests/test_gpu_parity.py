@@ -625,3 +625,51 @@ def test_unwritten_ring_slots_never_reach_the_output(Hq, bits):
         got = out.cpu().numpy()
         assert np.isfinite(got).all(), i
         assert_attention_close(got, oc.attend(q))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_degenerate_and_extreme_groups(bits):
+    """Key channels and value groups that are constant (s floored at 1e-8), all
+    zero with mixed signs of zero, at the fp16 extremes (+-65504, one range
+    spanning both), made of fp16 subnormals, or holding a single outlier.
+    Codes, scales, zeros and residual rows bit-exact against the oracle; the
+    attention (a zero query, so every weight is equal and the outputs stay near
+    the values' means) within the bar where the values are moderate."""
+    _announce("degenerate", bits)
+    d, T = 128, 32 * 5 + 128 + 7
+    rng = np.random.default_rng(99 + bits)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    x[:, 0] = 3.0                                          # constant channel
+    x[:, 1] = 0.0
+    x[::2, 1] = -0.0                                       # signed zeros
+    x[:, 2] = rng.choice([65504.0, -65504.0], size=T)      # the whole fp16 range
+    x[:, 3] = 65504.0
+    x[:, 4] = rng.integers(1, 1024, T) * 2.0 ** -24        # fp16 subnormals
+    x[:, 5] = 0.0
+    x[::37, 5] = 1000.0                                    # a lone outlier per block
+    x[7, :] = 2.5                                          # a constant token (value groups)
+    x[11, 32:64] = -65504.0
+    k = torch.from_numpy(x.astype(np.float16)).reshape(1, 1, T, d)
+    v = torch.from_numpy(np.ascontiguousarray(x[::-1]).astype(np.float16)).reshape(1, 1, T, d)
+    cache = kv.KiviCache(1, 1, 1, d, bits, max_tokens=T, device=DEV)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache(1, 1, 1, d, bits, max_tokens=T)
+    oc.append(k, v)
+    oc.flush()
+    compare_unit(cache, oc, 0, 0)
+    # attention over moderate values: zero the extreme value channels for this part
+    vm = v.clone()
+    vm[..., 2:4] = 0
+    vm[0, 0, T - 1 - 11, 32:64] = 0
+    cm = kv.KiviCache(1, 1, 1, d, bits, max_tokens=T, device=DEV)
+    cm.append(k.to(DEV), vm.to(DEV))
+    om = oracle.OracleCache(1, 1, 1, d, bits, max_tokens=T)
+    om.append(k, vm)
+    q = torch.zeros(1, 1, d, dtype=torch.float16)
+    out = cm.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_attention_close(got, om.attend(q))
