@@ -673,3 +673,26 @@ def test_degenerate_and_extreme_groups(bits):
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
     assert_attention_close(got, om.attend(q))
+
+
+@pytest.mark.parametrize("Hq", [1, 4], ids=["mha", "group4"])
+def test_maximum_split_count(Hq):
+    """The largest split count a config allows (max_splits = 4096), forced on a
+    cache of 4100 key blocks: about one block per split, most splits without a
+    residual, the merge over 4096 partials per query head."""
+    _announce("max splits", Hq)
+    T = 32 * 4100 + 50
+    wl = KVWorkload(1, 1, 128, seed=4096 + Hq, device="cpu")
+    k, v = wl.kv(0, T)
+    q = wl.q(Hq)
+    cache = kv.KiviCache(1, 1, Hq, 128, 2, max_tokens=T, max_splits=4096, device=DEV)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    cache.set_attend_splits(4096)
+    assert cache.plan_attend()[0] == 4096
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache(1, 1, Hq, 128, 2, max_tokens=T)
+    oc.append(k, v)
+    oc.flush()
+    assert_attention_close(out.cpu().numpy(), oc.attend(q))
