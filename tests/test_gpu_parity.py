@@ -696,3 +696,26 @@ def test_maximum_split_count(Hq):
     oc.append(k, v)
     oc.flush()
     assert_attention_close(out.cpu().numpy(), oc.attend(q))
+
+
+def test_largest_unit_count():
+    """The largest number of units a cache allows (batch * n_kv_heads = 65504 of
+    at most 65535): the launch grids' unit dimension at its limit. Sampled units
+    (first, middle, last) against the oracle, bytes and attention."""
+    B, Hkv, Hq, d, T = 2047, 32, 32, 128, 200
+    _announce("largest unit count", B * Hkv)
+    wl = KVWorkload(B, Hkv, d, seed=65504, device=DEV)
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, 2, max_tokens=T, device=DEV)
+    cache.append(k, v)
+    cache.flush()
+    q = wl.q(Hq)
+    out = cache.attend(q)
+    torch.cuda.synchronize()
+    for u in (0, 33333, B * Hkv - 1):
+        b, h = divmod(u, Hkv)
+        oc = oracle.OracleCache(1, 1, 1, d, 2, max_tokens=T)
+        oc.append(k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu())
+        oc.flush()
+        compare_unit(cache, oc, u, 0)
+        assert_attention_close(out[b:b + 1, h:h + 1].cpu().numpy(), oc.attend(q[b:b + 1, h:h + 1].cpu()))
