@@ -471,7 +471,37 @@ int main() {
             if (prev != nq / 32) return 5;
         }
     }
-    kivi_config c{8, 32, 32, 128, 2, 32, 32, 128, 4096, 0};
+    // rows of different lengths: the row plan and each row's splits cover its blocks
+    for (int trial = 0; trial < 3000; ++trial) {
+        x = x * 1103515245u + 12345u;
+        const int rows = 1 + (x >> 16) % 128;
+        int64_t cost[128], nbs[128], nrs[128], nb_max = 0;
+        for (int r = 0; r < rows; ++r) {
+            x = x * 1103515245u + 12345u;
+            const int64_t len = 1 + (x >> 8) % 200000;
+            const int64_t nq = len >= 160 ? (len - 128) / 32 * 32 : 0;
+            nbs[r] = nq / 32;
+            nrs[r] = len - nq;
+            cost[r] = kivi::unit_cost(nbs[r], nrs[r]);
+            nb_max = nbs[r] > nb_max ? nbs[r] : nb_max;
+        }
+        int64_t cmax = 0;
+        kivi::AttendPlan a = kivi::plan_attend_rows(1 + (x >> 4) % 32, 1 << ((x >> 2) % 4), 128, rows, cost, nb_max,
+                                                    4096, (x >> 3) % 7 == 0 ? 1 + (x >> 5) % 300 : 0, &cmax);
+        if (a.n_split < 1 || a.n_split > 4096) return 6;
+        for (int r = 0; r < rows; ++r) {
+            const int64_t n = kivi::row_split_count(cost[r], cmax, a.n_split);
+            if (n < 1 || n > a.n_split) return 7;
+            int64_t b0, b1, prev = 0;
+            for (int64_t s = 0; s < n; ++s) {
+                kivi::split_range(nbs[r], (nrs[r] + 31) / 32, kivi::kResidualChunkCost, n, s, &b0, &b1);
+                if (b0 != prev || b1 < b0) return 8;
+                prev = b1;
+            }
+            if (prev != nbs[r]) return 9;
+        }
+    }
+    kivi_config c{8, 32, 32, 128, 2, 32, 32, 128, 4096, 0, 0};
     std::string err;
     if (kivi::validate_config(&c, err) != KIVI_OK) return 3;
     kivi_layout L;
