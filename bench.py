@@ -3,6 +3,11 @@
 Metric: decode-attention effective HBM GB/s (and % of the 8 TB/s peak), plus
 quantize-append tokens/s.
 
+Default workload: the full-stack decode step (32 layers x batch 128 x 8 KV
+heads / 32 query heads x head_dim 128 x 4096 cached tokens, layers 0-15 at
+b = 2 and 16-31 at b = 4, bf16 queries), the largest configuration that fits
+one GPU; --workload picks another.
+
 A timed step is one decode step of the whole path over one batch: append one
 token per sequence (residual ring), flush when a whole 32-token group lies
 beyond the newest 128 (quantize-and-pack keys per channel, values per token),
@@ -103,83 +108,187 @@ def _kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(workload):
+def _traffic_from_profile(workload, bits=None):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when there is none or the kernels changed since."""
+    summary (of the b-bit layers' launches when `bits` is given), or None when
+    there is none or the kernels changed since."""
     path = os.path.join(ROOT, "profiles", f"attend_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
+    key = "hbm_bytes_per_launch" + (f"_b{bits}" if bits is not None else "")
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    t = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != _kernel_source_hash():
         return None
     return float(t.group(1))
 
 
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _cpu_baseline(cfg, seconds=8.0):
     """The oracle as it is, on the host cores: prefill-quantize and attention
-    over one batch row (all KV heads) of the workload, attention repeated until
-    about `seconds` have passed. Reported in the same units as the GPU line."""
-    import torch
-
+    over one batch row (all KV heads) of one layer of the workload, attention
+    repeated until about `seconds` have passed, once on every thread and once
+    on a single thread. The sample's byte and token rates stand for the whole
+    workload's: every (batch row, KV head) unit costs the oracle the same, so
+    bytes, tokens and time all scale by the same unit count. Reported in the
+    GPU line's units."""
     import oracle
     from kivi_inputs import KVWorkload
 
-    Hkv, Hq, d, T, bits = cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"], cfg.get("bits", 2)
+    Hkv, Hq, d, T = cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"]
+    bits = cfg.get("bits", cfg.get("layer_bits", [2])[0])
+    q_bf16 = cfg.get("q_dtype") == "bf16"
+    import torch
     wl = KVWorkload(1, Hkv, d, seed=cfg["seed"], device="cpu")
     k, v = wl.kv(0, T)
-    q = wl.q(Hq)
-    oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
-    t0 = time.perf_counter()
-    oc.append(k, v)
-    oc.flush()
-    t_prefill = time.perf_counter() - t0
-    nt, nq = oc.state()
-    nbytes = attend_bytes(Hkv, Hq, d, bits, nq, nt - nq)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oc.attend(q)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    del torch
+    q = wl.q(Hq, dtype=torch.bfloat16 if q_bf16 else torch.float16)
+    n_all = oracle.num_threads()
+
+    def run(threads, secs):
+        oracle.set_num_threads(threads)
+        oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
+        t0 = time.perf_counter()
+        oc.append(k, v)
+        oc.flush()
+        t_prefill = time.perf_counter() - t0
+        nt, nq = oc.state()
+        nbytes = attend_bytes(Hkv, Hq, d, bits, nq, nt - nq)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oc.attend(q, q_is_bf16=q_bf16)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                break
+        return nbytes * n / el / 1e9, T / t_prefill, n, el
+
+    try:
+        gbs, tok_s, n, el = run(n_all, seconds)
+        gbs1, tok_s1, n1, el1 = run(1, seconds / 2)
+    finally:
+        oracle.set_num_threads(n_all)
     return {
-        "value": round(nbytes * n / el / 1e9, 4),
+        "value": round(gbs, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": n_all,
         "kind": "oracle",
-        "sample": f"1 batch row x {Hkv} KV heads x {T} tokens of the workload; attention repeated {n} times "
-                  f"in {el:.1f} s; prefill-quantize of the same sample {Hkv * T / t_prefill:.0f} tokens/s",
-        "quantize_append_tokens_per_s": round(Hkv * T / t_prefill, 1),
+        "sample": f"1 batch row x {Hkv} KV heads x {T} tokens of one b={bits} layer of the workload "
+                  f"(rates stand for the whole workload: units cost the oracle alike, so bytes, tokens and "
+                  f"time scale together); attention repeated {n} times in {el:.1f} s on {n_all} threads and "
+                  f"{n1} times in {el1:.1f} s on 1 thread",
+        "cpu_model": _cpu_model(),
+        "single_thread_gbs": round(gbs1, 4),
+        "quantize_append_tokens_per_s": round(tok_s, 1),
+        "quantize_append_tokens_per_s_single_thread": round(tok_s1, 1),
     }
 
 
-def _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows, d, q0, out, n_att=None):
-    """The attention launches alone: n_att back-to-back kivi_attend_decode
-    calls over the rotating caches, bracketed by one pair of HIP events on the
-    stream they run on. Returns (ms per call, algorithmic bytes per call, n)."""
+def _attend_kernel_name(c):
+    """The kernel a cache's kivi_attend_decode launches, and its merge."""
+    cfg = c.cfg
+    n_split = c.plan_attend()[0]
+    gqa4 = (cfg.n_q_heads // cfg.n_kv_heads) % 4 == 0 and cfg.head_dim == 128
+    name = "attend_gqa_kernel (four query heads, int8 matrix cores)" if gqa4 else "attend_kernel"
+    return name + (" + combine_kernel (merge of %d splits)" % n_split if n_split > 1 else ", one split")
+
+
+def _arith_dtype(caches):
+    """The arithmetic the attention path computes in."""
+    c = caches[0].cfg
+    if (c.n_q_heads // c.n_kv_heads) % 4 == 0 and c.head_dim == 128:
+        return ("i8 x i8 -> i32 (codes against 3 signed-byte digits of 23-bit fixed-point folded queries "
+                "and weights) + f32 softmax and sums")
+    return "f32 (fp16 code halves in fp32 FMAs)"
+
+
+def _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, rounds):
+    """Back-to-back kivi_attend_decode launches over the caches `idx` (in
+    order, `rounds` times), bracketed by one pair of HIP events on the stream
+    they run on. Returns (us per launch, algorithmic bytes per launch, n)."""
+    import ctypes
+
     import torch
 
-    n_caches = len(caches)
-    if n_att is None:
-        n_att = max(2 * n_caches, min(200, 20 * n_caches))
-    per_cache = [cache_attend_bytes(c) for c in caches]
-    att_bytes = sum(per_cache[i % n_caches] for i in range(n_att))
-    for i in range(min(n_caches, 8)):  # warm the launch path
-        caches[i].attend(q0, out=out)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(n_att):
-        rc = lib.kivi_attend_decode(handles[i % n_caches], qp[i % len(qp)], qd, outp, sp)
+    handles = [ctypes.c_void_p(caches[i].handle) for i in idx]
+    per = [cache_attend_bytes(caches[i]) for i in idx]
+    for h in handles[:8]:  # warm the launch path
+        rc = lib.kivi_attend_decode(h, qp[0], qd, outp, sp)
         if rc != 0:
             raise kv.KiviError(rc, kv.kivi_last_error())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = rounds * len(idx)
+    ev0.record(stream)
+    for r in range(rounds):
+        for k, h in enumerate(handles):
+            rc = lib.kivi_attend_decode(h, qp[(r * len(idx) + k) % len(qp)], qd, outp, sp)
+            if rc != 0:
+                raise kv.KiviError(rc, kv.kivi_last_error())
     ev1.record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / n_att, att_bytes / n_att, n_att
+    return ev0.elapsed_time(ev1) * 1e3 / n, sum(per) / len(per), n
+
+
+def _time_attend_single(kv, lib, caches, idx, qp, qd, outp, sp):
+    """Each launch between its own pair of HIP events, the host waiting for
+    it before the next: us per launch (no overlap with a neighbour)."""
+    import ctypes
+
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ts = []
+    for k, i in enumerate(idx):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.kivi_attend_decode(ctypes.c_void_p(caches[i].handle), qp[k % len(qp)], qd, outp, sp)
+        if rc != 0:
+            raise kv.KiviError(rc, kv.kivi_last_error())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return sum(ts) / len(ts)
+
+
+def _stream_probe(dev, nbytes=256 << 20):
+    """The box's plain streaming rates on `nbytes` buffers (torch's copy and
+    sum kernels, HIP events, best of 5): copy GB/s counts the bytes read plus
+    written, sum GB/s the bytes read. Context for the attention roofline."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    best_copy = best_sum = float("inf")
+    for _ in range(5):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        best_copy = min(best_copy, ev[0].elapsed_time(ev[1]))
+        ev[0].record()
+        torch.sum(src, out=acc)
+        ev[1].record()
+        torch.cuda.synchronize()
+        best_sum = min(best_sum, ev[0].elapsed_time(ev[1]))
+    del src, dst
+    return {"bytes": nbytes, "copy_gbs": round(2 * nbytes / (best_copy * 1e-3) / 1e9, 1),
+            "sum_read_gbs": round(nbytes / (best_sum * 1e-3) / 1e9, 1), "how": "torch copy_ / sum, best of 5"}
 
 
 # ---------------------------------------------------------------- main
@@ -187,9 +296,10 @@ def _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default: 100 for full_stack, 200 otherwise)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama2_7b_layer",
+    ap.add_argument("--workload", default="full_stack",
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
                              "gqa_ragged", "gqa_paged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -203,13 +313,17 @@ def main():
         print("bench.py measures one GPU: the KV cache units are independent per (batch row, KV head), "
               "so a multi-GPU run would shard them with no communication; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = 100 if args.workload == "full_stack" else 200
+
+    import ctypes
 
     import torch
 
     import kv_cache_compression_kivi_amd as kv
     from kivi_inputs import CONFIGS, KVWorkload, page_order, row_lengths
 
-    kv.load_library()
+    lib = kv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     cfg = dict(CONFIGS[args.workload])
@@ -226,11 +340,13 @@ def main():
     per_step_bytes = sum(attend_bytes(Hkv, Hq, d, b, max(0, (t - 128) // 32 * 32), t - max(0, (t - 128) // 32 * 32))
                          for b in layer_bits for t in lens)
     n_rot = 1 if per_step_bytes >= (1 << 30) else min(16, int(-(-(1 << 30) // per_step_bytes)))
-    n_caches = n_rot * layers
     max_tokens = T + -(-total_steps // n_rot) + 64
     print(f"[bench] workload {args.workload}: {layers} layer(s) x {n_rot} rotation(s), "
           f"{per_step_bytes / 1e6:.1f} MB per step", file=sys.stderr, flush=True)
 
+    # the layers whose prefill is timed (and whose inputs are kept): the first and last of each bit width
+    pf_layers = sorted({min(i for i in range(layers) if layer_bits[i] == b) for b in set(layer_bits)} |
+                       {max(i for i in range(layers) if layer_bits[i] == b) for b in set(layer_bits)})
     caches = []
     prefill_inputs = {}
     for r in range(n_rot):
@@ -251,7 +367,7 @@ def main():
                 c.append(k, v)
             c.flush()
             caches.append(c)
-            if r == 0 and layer in (0, layers - 1):
+            if r == 0 and layer in pf_layers[:1] + pf_layers[-1:]:
                 prefill_inputs[layer] = (k, v)
             del k, v
     torch.cuda.synchronize()
@@ -263,16 +379,12 @@ def main():
     queries = [wl0.q(Hq, step=i, dtype=q_dtype) for i in range(pool)]
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    s_ptr = stream.cuda_stream
-
-    lib = kv.load_library()
-    import ctypes
     qd = kv.KIVI_BF16 if q_dtype == torch.bfloat16 else kv.KIVI_F16
     nfl = ctypes.c_int32()
     kvp = [(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr())) for a, b in new_kv]
     qp = [ctypes.c_void_p(x.data_ptr()) for x in queries]
     outp = ctypes.c_void_p(out.data_ptr())
-    sp = ctypes.c_void_p(s_ptr)
+    sp = ctypes.c_void_p(stream.cuda_stream)
     handles = [ctypes.c_void_p(c.handle) for c in caches]
 
     def run_step(i):
@@ -317,39 +429,57 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = bytes_total / wall / 1e9
 
-    att_avg_ms, att_bytes_avg, n_att = _time_attend(kv, lib, caches, handles, qp, qd, outp, stream, sp, units, rows, d,
-                                                    queries[0], out)
-    att_gbs = att_bytes_avg / (att_avg_ms * 1e-3) / 1e9
+    # the attention launches alone: every cache in step order, back to back
+    rounds = max(2, min(200 // len(caches), 25)) if len(caches) < 200 else 1
+    rounds = max(rounds, 5) if layers > 1 else max(rounds, -(-160 // len(caches)))
+    att_us, att_bytes, n_att = _time_attend(kv, lib, caches, list(range(len(caches))), qp, qd, outp, sp, out,
+                                            rounds)
+    att_gbs = att_bytes / (att_us * 1e-6) / 1e9
+    # and per bit width (their kernels differ), when the layers mix them
+    by_bits = {}
+    if len(set(layer_bits)) > 1:
+        for bw in sorted(set(layer_bits)):
+            idx = [i for i in range(len(caches)) if caches[i].cfg.bits == bw]
+            us, nb, n = _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, max(5, rounds))
+            by_bits[str(bw)] = {"kernel": _attend_kernel_name(caches[idx[0]]), "layers": len(idx),
+                                "achieved": round(nb / (us * 1e-6) / 1e9, 2),
+                                "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                "algorithmic_bytes_per_launch": int(nb), "avg_launch_us": round(us, 3),
+                                "timed_launches": n}
+    single_us = _time_attend_single(kv, lib, caches, list(range(min(len(caches), 32))), qp, qd, outp, sp)
     if args.profile:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)  # known traffic: 256 MiB read + 256 MiB written per copy
         torch.cuda.synchronize()
-        print(f"[bench] profile: the last {n_att} attention calls carry {att_bytes_avg:.0f} algorithmic bytes "
-              f"each ({att_avg_ms * 1e3:.2f} us); then 3 copies of {256 << 20} bytes", file=sys.stderr, flush=True)
+        print(f"[bench] profile: the last {n_att} attention calls (before the single-launch ones) carry "
+              f"{att_bytes:.0f} algorithmic bytes each ({att_us:.2f} us back to back, {single_us:.2f} us one at a "
+              f"time); then 3 copies of {256 << 20} bytes", file=sys.stderr, flush=True)
         return
 
-    # prefill quantize-append: append(T) + flush into an empty cache
-    n_pf = min(len(caches), max(4, n_rot))
-    pf_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_pf)]
-    pf_bytes = 0
-    for i in range(n_pf):
+    # prefill quantize-append: append(T) + flush into an empty cache, on the
+    # first and last layer of each bit width (the first and last input kept)
+    pf_idx = pf_layers if layers > 1 else list(range(min(len(caches), max(4, n_rot))))
+    pf_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in pf_idx]
+    pf_bytes = pf_tokens = pf_unit_tokens = 0
+    for e, i in zip(pf_ev, pf_idx):
         c = caches[i]
-        layer = i % layers
-        k, v = prefill_inputs.get(layer, prefill_inputs[0])
+        k, v = prefill_inputs.get(i % layers, prefill_inputs[min(prefill_inputs)])
         c.reset()
-        pf_ev[i][0].record(stream)
+        e[0].record(stream)
         if cfg.get("ragged"):
             c.append_rows(k, v, lens)
         else:
             c.append(k, v)
         c.flush()
-        pf_ev[i][1].record(stream)
+        e[1].record(stream)
         pf_bytes += sum(prefill_bytes(Hkv * w, d, c.cfg.bits, nt, nq) for nt, nq, _, w in row_groups(c))
+        pf_tokens += sum(lens)
+        pf_unit_tokens += Hkv * sum(lens)
     torch.cuda.synchronize()
     pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
-    pf_tok_s = n_pf * Hkv * sum(lens) / (pf_ms * 1e-3)
+    pf_tok_s = pf_tokens / (pf_ms * 1e-3)
     pf_gbs = pf_bytes / (pf_ms * 1e-3) / 1e9
 
     # single-token appends (ring writes only) and one 32-token flush, on the
@@ -357,34 +487,34 @@ def main():
     # is full and the flush then quantizes exactly one group (rows at one length only)
     ap_us = fl_us = fl_gbs = None
     if not cfg.get("ragged"):
-        ap_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_pf)]
+        ap_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in pf_idx]
         n_ap = 32
-        for i in range(n_pf):
+        for e, i in zip(ap_ev, pf_idx):
             h = handles[i]
             assert caches[i].state()[2] == 128
-            ap_ev[i][0].record(stream)
+            e[0].record(stream)
             for t in range(n_ap):
                 kp, vp = kvp[t % pool]
                 rc = lib.kivi_append(h, kp, vp, 1, sp)
                 if rc != 0:
                     raise kv.KiviError(rc, kv.kivi_last_error())
-            ap_ev[i][1].record(stream)
+            e[1].record(stream)
             rc = lib.kivi_flush(h, sp, ctypes.byref(nfl))
             if rc != 0:
                 raise kv.KiviError(rc, kv.kivi_last_error())
-            ap_ev[i][2].record(stream)
+            e[2].record(stream)
             assert nfl.value == 32, nfl.value
         torch.cuda.synchronize()
-        ap_us = sum(e[0].elapsed_time(e[1]) for e in ap_ev) * 1e3 / (n_pf * n_ap)
-        fl_us = sum(e[1].elapsed_time(e[2]) for e in ap_ev) * 1e3 / n_pf
-        fl_gbs = sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in range(n_pf)) / n_pf / (fl_us * 1e-6) / 1e9
+        ap_us = sum(e[0].elapsed_time(e[1]) for e in ap_ev) * 1e3 / (len(pf_idx) * n_ap)
+        fl_us = sum(e[1].elapsed_time(e[2]) for e in ap_ev) * 1e3 / len(pf_idx)
+        fl_gbs = (sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in pf_idx) / len(pf_idx) /
+                  (fl_us * 1e-6) / 1e9)
 
+    probe = _stream_probe(dev)
     traffic = _traffic_from_profile(args.workload)
-    plan = caches[0].plan_attend()
-    gqa4 = (Hq // Hkv) % 4 == 0 and d == 128
-    attend_kernel_name = ("kivi_attend_decode = " + ("attend_gqa_kernel (four query heads, int8 matrix cores)"
-                                                     if gqa4 else "attend_kernel") +
-                          (" + combine_kernel (merge of %d splits)" % plan[0] if plan[0] > 1 else ", one split"))
+    if by_bits:
+        for bw, e in by_bits.items():
+            e["traffic"] = _traffic_from_profile(args.workload, bits=bw)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -396,7 +526,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": _arith_dtype(caches),
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_kv_heads": Hkv, "n_q_heads": Hq, "head_dim": d,
                    "tokens": T if not cfg.get("ragged") else {"per_row": "uniform over [%d, %d]" % tuple(cfg["ragged"]),
@@ -408,24 +538,32 @@ def main():
                    "blocks": "paged (pool pages in random order)" if cfg.get("paged") else "one region per unit",
                    "rotating_caches": n_rot},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        # prefill: append(T) + flush into an empty cache; a token is one sequence's token (B*T per layer)
         "quantize_append_tokens_per_s": round(pf_tok_s, 1),
+        "quantize_append_unit_tokens_per_s": round(pf_unit_tokens / (pf_ms * 1e-3), 1),
         "quantize_append_gbs": round(pf_gbs, 2),
+        "quantize_append_pct_of_peak": round(100.0 * pf_gbs / PEAK_HBM_GBS, 2),
+        "quantize_append_layers_timed": pf_idx if layers > 1 else None,
         "append_1_token_us": round(ap_us, 3) if ap_us else None,
-        "append_1_token_tokens_per_s": round(units / (ap_us * 1e-6), 1) if ap_us else None,
+        # B tokens per call (one per sequence)
+        "append_1_token_tokens_per_s": round(B / (ap_us * 1e-6), 1) if ap_us else None,
         "flush_32_tokens_us": round(fl_us, 3) if fl_us else None,
         "flush_32_tokens_gbs": round(fl_gbs, 2) if fl_gbs else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": attend_kernel_name,
+            "kernel": "kivi_attend_decode = " + " / ".join(sorted({_attend_kernel_name(c) for c in caches})),
             "achieved": round(att_gbs, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(att_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(att_bytes_avg),
-            "avg_launch_us": round(att_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(att_bytes),
+            "avg_launch_us": round(att_us, 3),
             "timed_launches": n_att,
+            "single_launch_us": round(single_us, 3),
+            "by_bits": by_bits or None,
         },
+        "stream_probe": probe,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -143,7 +143,9 @@ int kivi_cache_layout(const kivi_config* cfg, kivi_layout* layout);
 
 /* Make a handle over caller-owned device memory `dev_mem` of `bytes` bytes
  * (at least kivi_cache_bytes; 256-byte aligned). Launches nothing. The cache
- * starts empty. dev_mem must outlive the handle. */
+ * starts empty. dev_mem must outlive the handle. The split plans of
+ * kivi_attend_decode fill the compute units of the device that is current
+ * when the handle is made (256 when no device answers). */
 int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_cache** out);
 
 /* Frees the host handle only (the device memory stays the caller's). */
@@ -152,7 +154,10 @@ int kivi_cache_destroy(kivi_cache* cache);
 /* Empty the cache (host counters only; launches nothing). */
 int kivi_cache_reset(kivi_cache* cache);
 
-/* Append ntok >= 1 tokens to every sequence. k, v: device fp16 [B][Hkv][ntok][d],
+/* Append ntok >= 1 tokens to every sequence (page sections 残差バッファ（Residual
+ * Buffer）: new tokens enter the fp16 residual; Per-Channel量子化 / Per-Token量子化:
+ * the keys and values of a group that leaves it are quantized per channel /
+ * per token with section 量子化アルゴリズム's Q). k, v: device fp16 [B][Hkv][ntok][d],
  * contiguous. The result is defined token by token: the ring holds R + G
  * slots, and a token arriving when it is full first quantizes the oldest G
  * residual tokens (per-channel key blocks, per-token value groups). Tokens
@@ -193,10 +198,16 @@ int kivi_reset_row(kivi_cache* cache, int32_t row);
 
 /* Quantize, in every row, the oldest floor((n_resid - R) / G) * G residual
  * tokens (none if n_resid < R + G); *n_flushed (may be NULL) receives the
- * largest count of a row. */
+ * largest count of a row. Page sections 残差バッファ（Residual Buffer）(only the
+ * newest R tokens need stay fp16) and Per-Token量子化（Value Cache）(values are
+ * quantized once a whole group of G tokens has accumulated); the codes follow
+ * section 量子化アルゴリズム. */
 int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
 
-/* Decode attention of one query per head over every cached token:
+/* Decode attention of one query per head over every cached token (page
+ * section 残差バッファ（Residual Buffer）: one softmax over the quantized part
+ * and the fp16 residual together, scaled by 1/sqrt(d); section 量子化アルゴリズム:
+ * D(x) = s x + z):
  * out[b][i] = sum_t softmax_t(q[b][i] . k_t / sqrt(d)) v_t, with k_t, v_t the
  * dequantized (s * code + z, in fp32) or residual fp16 rows of KV head
  * i / (Hq / Hkv). q: device [B][Hq][d] of q_dtype (KIVI_F16 / KIVI_BF16);
@@ -206,7 +217,10 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
  * over its own tokens. KIVI_E_EMPTY if a sequence holds no token. */
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
 
-/* One decode step in one call: kivi_append of one token per sequence (k, v:
+/* One decode step in one call (page section 残差バッファ（Residual Buffer）: the
+ * new token joins the fp16 residual, a group leaving the newest R is
+ * quantized, and the query attends over both parts):
+ * kivi_append of one token per sequence (k, v:
  * device fp16 [B][Hkv][1][d]), then kivi_flush if a whole group of G tokens
  * lies beyond the newest R (so the residual cycles through R .. R+G-1 tokens
  * at attention time), then kivi_attend_decode. *n_flushed (may be NULL)

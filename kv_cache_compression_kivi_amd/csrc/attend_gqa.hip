@@ -348,6 +348,11 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) acc_v[vt] = v4i32{0, 0, 0, 0};
     int ew = INT_MIN / 2;
+    // blocks added to acc_v since the last wave-wide fold: kGqaFoldBlocks
+    // bounds it, so the int32 sums cannot overflow however long the wave's
+    // share (a fold of some rows only, on a new maximum, leaves it counting;
+    // it stays wave-uniform, in a scalar register)
+    int since_fold = 0;
     // o_blk += 2^(ew - 22) sum_d 2^(8d) acc_v[d], then the sums restart
     auto fold = [&]() {
         const float vs = ldexpf(1.0f, ew - 22);
@@ -414,6 +419,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
         if (ev > ew || ev < ew - 2) {
             fold();
             ew = ev;
+            since_fold = 0;
         }
         wave_lds_order();
         // 2. scores of query rho and token rt of each tile: the digit sums of
@@ -542,6 +548,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
             wave_lds_order();  // the slot's reads stay before the operand stores into it
             key_math(r, k);
             value_math(r, k);
+            if (++since_fold == (int)kGqaFoldBlocks) {
+                fold();
+                since_fold = 0;
+            }
             if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
         }
     }

@@ -30,6 +30,8 @@ struct kivi_cache {
     const int32_t* table;
     int64_t table_stride;
     int32_t forced_splits;
+    // compute units of the device current at create time (the split plans fill them)
+    int32_t cus;
     bool poisoned;
 };
 
@@ -233,13 +235,13 @@ kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
     if (rows_agree(c) && !paged(c)) {  // paged caches launch with a row table
         if (cost_max) *cost_max = kivi::unit_cost(c->nq[0] / G, c->nt[0] - c->nq[0]);
         return kivi::plan_attend((int64_t)B * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
-                                 c->L.max_splits, c->forced_splits);
+                                 c->L.max_splits, c->forced_splits, c->cus);
     }
     std::vector<int64_t> cost(B);
     for (int b = 0; b < B; ++b) cost[b] = kivi::unit_cost(c->nq[b] / G, c->nt[b] - c->nq[b]);
     int64_t cm = 1;
     kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, B, cost.data(),
-                                                max_of(c->nq) / G, c->L.max_splits, c->forced_splits, &cm);
+                                                max_of(c->nq) / G, c->L.max_splits, c->forced_splits, c->cus, &cm);
     if (cost_max) *cost_max = cm;
     return p;
 }
@@ -295,6 +297,18 @@ int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, v
     hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(cache, "attend launch", e);
     return KIVI_OK;
+}
+
+// Compute units of the current device, or kDefaultCUs (an MI355X's 256) when
+// no device answers (host-only use: the plan then only matters to the tests).
+int32_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return kivi::kDefaultCUs;
+    }
+    return n;
 }
 
 int check_row(const kivi_cache* c, int32_t row) {
@@ -354,6 +368,7 @@ int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_
     c->table = nullptr;
     c->table_stride = 0;
     c->forced_splits = 0;
+    c->cus = device_cus();
     c->poisoned = false;
     *out = c;
     return KIVI_OK;

@@ -24,6 +24,8 @@
 namespace kivi {
 
 constexpr int32_t kDefaultMaxSplits = 256;
+// Compute units assumed when no device can be asked (an MI355X has 256).
+constexpr int32_t kDefaultCUs = 256;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -156,13 +158,17 @@ inline void attend_shape(int32_t group, int32_t head_dim, int32_t* qg, int32_t* 
     *nwaves = attend_waves(*qg, head_dim);
 }
 
-// Split-K plan. Enough work-groups for 8 waves on each of the 256 CUs (one
-// 8-wave work-group or two 4-wave ones per CU), at least 2 key blocks per
-// wave in every split, at most max_splits partials per query head; no split
-// (and no merge launch) when the units alone fill the chip. forced > 0 fixes
-// the split count instead.
+// Waves per CU the split plans aim for: one 8-wave work-group or two 4-wave
+// ones on every compute unit.
+constexpr int64_t kWavesPerCU = 8;
+
+// Split-K plan. Enough work-groups for 8 waves on each of the device's `cus`
+// compute units (one 8-wave work-group or two 4-wave ones per CU), at least 2
+// key blocks per wave in every split, at most max_splits partials per query
+// head; no split (and no merge launch) when the units alone fill the chip.
+// forced > 0 fixes the split count instead.
 inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, int64_t n_blocks,
-                              int32_t max_splits, int32_t forced) {
+                              int32_t max_splits, int32_t forced, int32_t cus) {
     AttendPlan p;
     attend_shape(group, head_dim, &p.qg, &p.nwaves);
     const int64_t wgs_per_split = units * (group / p.qg);
@@ -170,7 +176,7 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
     if (forced > 0) {
         n = forced;
     } else {
-        const int64_t target_waves = 256 * 8;
+        const int64_t target_waves = (int64_t)(cus > 0 ? cus : 1) * kWavesPerCU;
         n = (target_waves + wgs_per_split * p.nwaves - 1) / (wgs_per_split * p.nwaves);
         const int64_t cap = n_blocks / (2 * p.nwaves);
         if (n > cap) n = cap;
@@ -186,7 +192,7 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
 // row r; nb_max: the longest row's key blocks). n is the split count of the
 // costliest row and each row takes its share (row_split_count), so that the
 // work-groups carry about equal work. n is the largest count whose work-groups
-// still fit one round over the CUs (as for rows that agree: 8 waves a CU), at
+// still fit one round over the `cus` CUs (as for rows that agree: 8 waves a CU), at
 // least 1: then every work-group starts at once, and the costliest rows'
 // work-groups, dispatched first, pair with short ones on their CUs (measured
 // on MI355X: more splits, with a second round of work-groups and the merge,
@@ -194,7 +200,7 @@ inline AttendPlan plan_attend(int64_t units, int32_t group, int32_t head_dim, in
 // wave in the costliest row's splits, at most max_splits; forced > 0 fixes n.
 inline AttendPlan plan_attend_rows(int64_t n_kv_heads, int32_t group, int32_t head_dim, int64_t rows,
                                    const int64_t* cost, int64_t nb_max, int32_t max_splits, int32_t forced,
-                                   int64_t* cost_max) {
+                                   int32_t cus, int64_t* cost_max) {
     AttendPlan p;
     attend_shape(group, head_dim, &p.qg, &p.nwaves);
     p.nwaves = attend_waves_rows(p.qg, head_dim);
@@ -210,7 +216,7 @@ inline AttendPlan plan_attend_rows(int64_t n_kv_heads, int32_t group, int32_t he
     if (forced > 0) {
         n = forced;
     } else {
-        const int64_t target_wgs = 256 * 8 / p.nwaves;
+        const int64_t target_wgs = (int64_t)(cus > 0 ? cus : 1) * kWavesPerCU / p.nwaves;
         int64_t hi = nb_max / (2 * p.nwaves);
         if (hi > max_splits) hi = max_splits;
         // the largest n in [1, hi] with wgs(n) <= target (wgs grows with n)

@@ -71,6 +71,14 @@ KIVI_HD constexpr int attend_waves_rows(int qg, int head_dim) {
     return qg == 4 && head_dim == 128 ? 8 : attend_waves(qg, head_dim);
 }
 
+// The four-query kernel keeps its value digit sums in int32 from block to
+// block. One block adds at most 128 (a signed digit) * 15 (a 4-bit code) * 32
+// (tokens) = 61440 to a sum in magnitude, so the sums are folded into fp32 at
+// least every kGqaFoldBlocks blocks: 32768 * 61440 < 2^31.
+constexpr int64_t kGqaFoldBlocks = 32768;
+constexpr int64_t kGqaBlockDigitSumMax = 128 * 15 * 32;
+static_assert(kGqaFoldBlocks * kGqaBlockDigitSumMax < (int64_t)1 << 31, "value digit sums stay in int32");
+
 // Key blocks wave w of nw holds out of nbw.
 KIVI_HD inline int64_t wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return nbw / nw + (w < nbw % nw ? 1 : 0); }
 

@@ -63,6 +63,7 @@ def lib():
         l.or_attend.restype = i32
         l.or_attend.argtypes = [P, P, i32, P]
         l.or_num_threads.restype = i32
+        l.or_set_num_threads.argtypes = [i32]
         _lib = l
     return _lib
 
@@ -133,6 +134,11 @@ def unpack_row(words, d: int, bits: int) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's later calls."""
+    lib().or_set_num_threads(int(n))
 
 
 class OracleCache:

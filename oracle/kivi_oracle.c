@@ -330,3 +330,12 @@ int or_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the OpenMP loops above use from now on (n >= 1). */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -84,6 +84,8 @@ int or_attend(const or_cache* c, const uint16_t* q, int q_is_bf16, double* out);
 
 /* Number of OpenMP threads or_attend and or_append use (1 without OpenMP). */
 int or_num_threads(void);
+/* Sets the number of OpenMP threads later calls use (n >= 1). */
+void or_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

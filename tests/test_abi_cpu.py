@@ -238,8 +238,8 @@ void shim_plan_append(int64_t nt, int64_t nq, int64_t ntok, int64_t R, int64_t G
 }
 int64_t shim_plan_flush(int64_t nt, int64_t nq, int64_t R, int64_t G) { return kivi::plan_flush(nt, nq, R, G); }
 void shim_plan_attend(int64_t units, int32_t group, int32_t d, int64_t nb, int32_t max_splits, int32_t forced,
-                      int32_t* out) {
-    kivi::AttendPlan p = kivi::plan_attend(units, group, d, nb, max_splits, forced);
+                      int32_t cus, int32_t* out) {
+    kivi::AttendPlan p = kivi::plan_attend(units, group, d, nb, max_splits, forced, cus);
     out[0] = p.n_split; out[1] = p.blocks_per_split; out[2] = p.qg; out[3] = p.nwaves;
 }
 void shim_split_range(int64_t nb, int64_t nrc, int64_t cost, int64_t n, int64_t s, int64_t* out) {
@@ -250,12 +250,14 @@ int64_t shim_residual_wave(int64_t c, int64_t nw) {
     return kivi::residual_wave(c, nw);
 }
 void shim_plan_rows(int64_t hkv, int32_t group, int32_t d, int64_t rows, const int64_t* cost, int64_t nb_max,
-                    int32_t max_splits, int32_t forced, int32_t* out, int64_t* cost_max) {
-    kivi::AttendPlan p = kivi::plan_attend_rows(hkv, group, d, rows, cost, nb_max, max_splits, forced, cost_max);
+                    int32_t max_splits, int32_t forced, int32_t cus, int32_t* out, int64_t* cost_max) {
+    kivi::AttendPlan p = kivi::plan_attend_rows(hkv, group, d, rows, cost, nb_max, max_splits, forced, cus, cost_max);
     out[0] = p.n_split; out[1] = p.blocks_per_split; out[2] = p.qg; out[3] = p.nwaves;
 }
 int64_t shim_row_split_count(int64_t c, int64_t cm, int64_t n) { return kivi::row_split_count(c, cm, n); }
 int64_t shim_unit_cost(int64_t nb, int64_t nres) { return kivi::unit_cost(nb, nres); }
+int64_t shim_gqa_fold_blocks() { return kivi::kGqaFoldBlocks; }
+int64_t shim_gqa_block_digit_sum_max() { return kivi::kGqaBlockDigitSumMax; }
 }
 """
 
@@ -276,18 +278,20 @@ def planner(tmp_path_factory):
     lib.shim_plan_flush.argtypes = [i64] * 4
     lib.shim_plan_flush.restype = i64
     i32 = ctypes.c_int32
-    lib.shim_plan_attend.argtypes = [i64, i32, i32, i64, i32, i32, ctypes.c_void_p]
+    lib.shim_plan_attend.argtypes = [i64, i32, i32, i64, i32, i32, i32, ctypes.c_void_p]
     lib.shim_split_range.argtypes = [i64] * 5 + [ctypes.c_void_p]
     lib.shim_wave_blocks.argtypes = [i64] * 3
     lib.shim_wave_blocks.restype = i64
     lib.shim_residual_wave.argtypes = [i64] * 2
     lib.shim_residual_wave.restype = i64
-    lib.shim_plan_rows.argtypes = [i64, i32, i32, i64, ctypes.c_void_p, i64, i32, i32, ctypes.c_void_p,
+    lib.shim_plan_rows.argtypes = [i64, i32, i32, i64, ctypes.c_void_p, i64, i32, i32, i32, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.shim_row_split_count.argtypes = [i64] * 3
     lib.shim_row_split_count.restype = i64
     lib.shim_unit_cost.argtypes = [i64] * 2
     lib.shim_unit_cost.restype = i64
+    lib.shim_gqa_fold_blocks.restype = i64
+    lib.shim_gqa_block_digit_sum_max.restype = i64
     return lib
 
 
@@ -331,22 +335,47 @@ def test_planner_config_states(planner):
         assert nq == want
 
 
-def test_attend_plan(planner):
+@pytest.mark.parametrize("cus", [256, 32, 80, 304])
+def test_attend_plan(planner, cus):
     out = np.zeros(4, np.int32)
     p = out.ctypes.data_as(ctypes.c_void_p)
-    # (units, group, head_dim, key blocks) -> the automatic split count of the five workloads
-    for args, want in [((1, 1, 128, 28), 1), ((256, 1, 128, 124), 1), ((32, 1, 128, 4092), 8),
-                       ((512, 4, 128, 255), 1), ((1024, 4, 128, 124), 1)]:
-        planner.shim_plan_attend(*args, 256, 0, p)
-        assert int(out[0]) == want, (args, out)
-    for units, group, d in [(1, 1, 128), (7, 2, 64), (3, 4, 256), (2, 3, 128)]:
+    # (units, group, head_dim, key blocks) -> the automatic split count of the five workloads on 256 CUs
+    if cus == 256:
+        for args, want in [((1, 1, 128, 28), 1), ((256, 1, 128, 124), 1), ((32, 1, 128, 4092), 8),
+                           ((512, 4, 128, 255), 1), ((1024, 4, 128, 124), 1)]:
+            planner.shim_plan_attend(*args, 256, 0, cus, p)
+            assert int(out[0]) == want, (args, out)
+    for units, group, d in [(1, 1, 128), (7, 2, 64), (3, 4, 256), (2, 3, 128), (32, 1, 128)]:
         for nb in (0, 1, 31, 4092):
             for forced in (0, 1, 3, 17, 300):
-                planner.shim_plan_attend(units, group, d, nb, 256, forced, p)
+                planner.shim_plan_attend(units, group, d, nb, 256, forced, cus, p)
                 n, bps, qg, nw = (int(x) for x in out)
                 assert 1 <= n <= 256 and group % qg == 0 and nw in (4, 8, 16)
                 if forced:
                     assert n == min(forced, 256)
+                else:
+                    # one round of work-groups over the device's CUs (8 waves each), unless the
+                    # two-blocks-per-wave floor or max_splits caps it, and never below 1
+                    wgs_per_split = units * (group // qg)
+                    want = -(-(cus * 8) // (wgs_per_split * nw))
+                    want = max(1, min(want, nb // (2 * nw), 256))
+                    assert n == want, (units, group, d, nb, cus, n, want)
+
+
+def test_gqa_value_sums_fit_int32(planner):
+    """The four-query kernel's int32 value digit sums: a block adds at most
+    |digit| * code * tokens = 128 * (2^4 - 1) * 32 to a sum (signed-byte
+    digits, 4-bit codes, 32 tokens a block), and the kernel folds the sums into
+    fp32 at least every kGqaFoldBlocks blocks, so no sum can leave int32
+    whatever a wave's share of blocks (a forced single split over a unit of
+    millions of tokens included)."""
+    per_block = 128 * ((1 << 4) - 1) * 32
+    assert planner.shim_gqa_block_digit_sum_max() == per_block
+    k = planner.shim_gqa_fold_blocks()
+    assert 1 <= k and k * per_block < 2 ** 31
+    # the largest wave share a config allows: 4 GiB of b = 2 records in one split, over 4 waves
+    max_blocks_per_unit = (1 << 32) // 4096
+    assert max_blocks_per_unit // 4 > k  # the bound, not the share, is what keeps the sums in range
 
 
 @pytest.mark.parametrize("cost", [2, 4])
@@ -407,8 +436,10 @@ def test_ragged_split_plan(planner):
         nb, nres = nq // 32, lens - nq
         cost = np.array([planner.shim_unit_cost(int(a), int(r)) for a, r in zip(nb, nres)], np.int64)
         forced = int(rng.choice([0, 0, 0, 3, 50]))
+        cus = int(rng.choice([256, 256, 32, 304]))
         planner.shim_plan_rows(hkv, group, 128, rows, cost.ctypes.data_as(ctypes.c_void_p), int(nb.max()), 256,
-                               forced, out.ctypes.data_as(ctypes.c_void_p), cmax_buf.ctypes.data_as(ctypes.c_void_p))
+                               forced, cus, out.ctypes.data_as(ctypes.c_void_p),
+                               cmax_buf.ctypes.data_as(ctypes.c_void_p))
         n, qg, nw = int(out[0]), int(out[2]), int(out[3])
         cmax = int(cmax_buf[0])
         assert cmax == cost.max() and 1 <= n <= 256
@@ -430,8 +461,8 @@ def test_ragged_split_plan(planner):
             assert prev == nb[r]
             wgs += nr * hkv * (group // qg)
         if not forced:
-            # the largest n whose work-groups fit one round of 256 * 8 / nw (n = 1 if none does)
-            target = 256 * 8 // nw
+            # the largest n whose work-groups fit one round of cus * 8 / nw (n = 1 if none does)
+            target = cus * 8 // nw
             cap = min(256, max(1, int(nb.max()) // (2 * nw)))
             assert n == 1 or wgs <= target, (n, wgs, target)
             if n < cap:
@@ -460,7 +491,7 @@ int main() {
                 nt = p.nt1; nq = p.nq1;
             }
             kivi::AttendPlan a = kivi::plan_attend(1 + (x >> 4) % 2000, 1 << ((x >> 2) % 4), 128, nq / 32, 256,
-                                                   (x >> 3) % 5);
+                                                   (x >> 3) % 5, 32 + (x >> 6) % 300);
             if (a.n_split < 1 || a.n_split > 256) return 2;
             int64_t b0, b1, prev = 0;
             for (int s = 0; s < a.n_split; ++s) {
@@ -487,7 +518,8 @@ int main() {
         }
         int64_t cmax = 0;
         kivi::AttendPlan a = kivi::plan_attend_rows(1 + (x >> 4) % 32, 1 << ((x >> 2) % 4), 128, rows, cost, nb_max,
-                                                    4096, (x >> 3) % 7 == 0 ? 1 + (x >> 5) % 300 : 0, &cmax);
+                                                    4096, (x >> 3) % 7 == 0 ? 1 + (x >> 5) % 300 : 0,
+                                                    32 + (x >> 6) % 300, &cmax);
         if (a.n_split < 1 || a.n_split > 4096) return 6;
         for (int r = 0; r < rows; ++r) {
             const int64_t n = kivi::row_split_count(cost[r], cmax, a.n_split);

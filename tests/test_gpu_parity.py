@@ -177,19 +177,27 @@ def test_quantizer_ties_and_near_ties(bits):
     compare_unit(cache, oc, 0, 0)
 
 
-@pytest.mark.parametrize("B,Hkv,Hq,d,bits,R,T0,steps", [
-    (2, 2, 2, 128, 2, 128, 200, 70),   # MHA, flushes at the steps that complete a group past R
-    (1, 2, 8, 128, 4, 32, 40, 40),     # GQA (matrix-core kernel), small residual
-    (2, 1, 1, 64, 2, 0, 5, 40),        # no residual: a flush takes the new token itself
-    (1, 1, 4, 256, 2, 64, 100, 35),    # d = 256, GQA on the vector path
+@pytest.mark.parametrize("B,Hkv,Hq,d,bits,R,T0,steps,splits", [
+    (2, 2, 2, 128, 2, 128, 200, 70, 0),   # MHA, flushes at the steps that complete a group past R
+    (1, 2, 8, 128, 4, 32, 40, 40, 0),     # GQA (matrix-core kernel), small residual
+    (2, 1, 1, 64, 2, 0, 5, 40, 0),        # no residual: a flush takes the new token itself
+    (1, 1, 4, 256, 2, 64, 100, 35, 0),    # d = 256, GQA on the vector path
+    # forced split counts: the new token is written by the last split, the
+    # splits are merged by the combine kernel, and some splits hold no block
+    (2, 2, 2, 128, 2, 128, 600, 40, 3),   # MHA, 3 splits
+    (1, 2, 8, 128, 4, 32, 300, 40, 17),   # GQA matrix cores, 17 splits (more than the blocks of early steps)
+    (2, 1, 2, 64, 2, 0, 500, 40, 5),      # no residual, two query heads per KV head, 5 splits
+    (1, 1, 1, 256, 4, 64, 700, 35, 17),   # d = 256, 17 splits
 ])
-def test_decode_step_parity(B, Hkv, Hq, d, bits, R, T0, steps):
+def test_decode_step_parity(B, Hkv, Hq, d, bits, R, T0, steps, splits):
     """kivi_decode_step (quantize when due, then one attention launch that also
-    writes the new token into the ring) against the oracle run token by token:
-    attention at every few steps, the whole cache bit-exact at the end."""
-    _announce("decode_step", B, Hkv, Hq, d, bits, R, T0, steps)
+    writes the new token into the ring, then the merge when split) against the
+    oracle run token by token: attention at every few steps, the whole cache
+    bit-exact at the end."""
+    _announce("decode_step", B, Hkv, Hq, d, bits, R, T0, steps, splits)
     wl = KVWorkload(B, Hkv, d, seed=11 + R, device="cpu")
     cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T0 + steps, residual=R, device=DEV)
+    cache.set_attend_splits(splits)
     oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T0 + steps, residual=R)
     k, v = wl.kv(0, T0)
     cache.append(k.to(DEV), v.to(DEV))
@@ -275,6 +283,11 @@ def test_workload_full_size(name, units):
 
 
 def test_gqa_streaming_full_size():
+    """The GQA streaming workload at full size through kivi_decode_step, the
+    call the benchmark times: prefill, then 256 steps of (append one token,
+    flush when a group lies beyond the newest 128, attend) in one call each.
+    Sampled units against their oracle caches at several steps, bytes at the
+    end."""
     cfg = CONFIGS["gqa_streaming"]
     _announce("gqa_streaming")
     B, Hkv, Hq, d, T0, bits = (cfg[x] for x in ("batch", "n_kv_heads", "n_q_heads", "head_dim", "T", "bits"))
@@ -293,16 +306,16 @@ def test_gqa_streaming_full_size():
     check_at = {1, 31, 32, 33, steps}
     for i in range(1, steps + 1):
         kt, vt = wl.kv(T0 + i - 1, 1)
-        cache.append(kt, vt)
+        q = wl.q(Hq, step=i)
+        out = cache.decode_step(kt, vt, q)
+        flushed = 0
         for u in units:
             b, h = divmod(u, Hkv)
             ocs[u].append(kt[b:b + 1, h:h + 1].cpu(), vt[b:b + 1, h:h + 1].cpu())
-        if i % 32 == 0:
-            n = cache.flush()
-            for u in units:
-                assert ocs[u].flush() == n
-        q = wl.q(Hq, step=i)
-        out = cache.attend(q)
+            nt, nq = ocs[u].state()
+            if nt - nq >= 128 + 32:
+                flushed = ocs[u].flush()
+        assert cache.last_flushed == flushed
         if i in check_at:
             torch.cuda.synchronize()
             print(f"  step {i} state {cache.state()}", flush=True)
@@ -323,19 +336,44 @@ def test_full_stack_layer(layer):
     _announce("full_stack layer", layer, "bits", bits)
     B, Hkv, Hq, d, T = cfg["batch"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"]
     group = Hq // Hkv
-    wl, cache, k, v = _full_prefill(cfg, bits=bits, layer=layer)
+    steps = 33  # the 32nd decode step flushes a group
+    wl, cache, k, v = _full_prefill(dict(cfg, decode_steps=steps), bits=bits, layer=layer)
     q = wl.q(Hq, dtype=torch.bfloat16)
     out = cache.attend(q)
     torch.cuda.synchronize()
+    ocs = {}
     for u in [5, 1023]:
         b, h = divmod(u, Hkv)
-        oc = oracle.OracleCache(1, 1, group, d, bits, max_tokens=T)
+        oc = oracle.OracleCache(1, 1, group, d, bits, max_tokens=T + steps)
         oc.append(k[b:b + 1, h:h + 1].cpu(), v[b:b + 1, h:h + 1].cpu())
         oc.flush()
         compare_unit(cache, oc, u, 0)
         ref = oc.attend(_unit_rows(q.cpu(), b, h, group), q_is_bf16=True)
         got = out[b:b + 1, h * group:(h + 1) * group].cpu().numpy()
         assert_attention_close(got, ref)
+        ocs[u] = oc
+    del k, v
+    # then the benchmark's decode steps (kivi_decode_step), across a flush
+    for i in range(1, steps + 1):
+        kt, vt = wl.kv(T + i - 1, 1)
+        qi = wl.q(Hq, step=i, dtype=torch.bfloat16)
+        out = cache.decode_step(kt, vt, qi)
+        for u, oc in ocs.items():
+            b, h = divmod(u, Hkv)
+            oc.append(kt[b:b + 1, h:h + 1].cpu(), vt[b:b + 1, h:h + 1].cpu())
+            nt, nq = oc.state()
+            if nt - nq >= 128 + 32:
+                assert oc.flush() == cache.last_flushed == 32
+        if i in (1, 32, steps):
+            torch.cuda.synchronize()
+            for u, oc in ocs.items():
+                b, h = divmod(u, Hkv)
+                ref = oc.attend(_unit_rows(qi.cpu(), b, h, group), q_is_bf16=True)
+                got = out[b:b + 1, h * group:(h + 1) * group].cpu().numpy()
+                assert_attention_close(got, ref)
+    torch.cuda.synchronize()
+    for u, oc in ocs.items():
+        compare_unit(cache, oc, u, 0)
 
 
 # ------------------------------------------------------- sequences of different lengths
