@@ -282,13 +282,48 @@ def _stream_probe(dev, nbytes=256 << 20):
         torch.cuda.synchronize()
         best_copy = min(best_copy, ev[0].elapsed_time(ev[1]))
         ev[0].record()
-        torch.sum(src, out=acc)
+        torch.sum(src, dim=0, out=acc)
         ev[1].record()
         torch.cuda.synchronize()
         best_sum = min(best_sum, ev[0].elapsed_time(ev[1]))
     del src, dst
     return {"bytes": nbytes, "copy_gbs": round(2 * nbytes / (best_copy * 1e-3) / 1e9, 1),
             "sum_read_gbs": round(nbytes / (best_sum * 1e-3) / 1e9, 1), "how": "torch copy_ / sum, best of 5"}
+
+
+def _profile_prefill(workload, n):
+    """n prefills of the workload's first layer into one cache, each timed with
+    its own pair of HIP events (for a profile of the quantizer alone)."""
+    import torch
+
+    import kv_cache_compression_kivi_amd as kv
+    from kivi_inputs import CONFIGS, KVWorkload
+
+    kv.load_library()
+    cfg = dict(CONFIGS[workload])
+    B, Hkv, Hq, d, T = cfg["batch"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"]
+    bits = cfg.get("bits", cfg.get("layer_bits", [2])[0])
+    dev = torch.device("cuda:0")
+    wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], device=dev)
+    k, v = wl.kv(0, T)
+    c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=dev)
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(n):
+        c.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        c.append(k, v)
+        c.flush()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    nt, nq, _ = c.state()
+    nb = prefill_bytes(B * Hkv, d, bits, nt, nq)
+    avg = sum(ts[1:]) / max(1, n - 1)
+    print(f"[bench] prefill profile {workload}: {n} prefills of B={B} x Hkv={Hkv} x T={T} (b={bits}); after the "
+          f"first, {avg:.2f} us each by HIP events, {nb} algorithmic bytes -> {nb / (avg * 1e-6) / 1e9:.1f} GB/s, "
+          f"{B * T / (avg * 1e-6):.4g} tokens/s (B*T)", file=sys.stderr, flush=True)
 
 
 # ---------------------------------------------------------------- main
@@ -304,6 +339,10 @@ def main():
                              "gqa_ragged", "gqa_paged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--profile-prefill", type=int, default=0, metavar="N",
+                    help="for profiles of the quantizer: N prefills (append(T) + flush into an emptied cache) of "
+                         "the workload's first layer, each between its own HIP events, then exit (no decode steps, "
+                         "no JSON line)")
     ap.add_argument("--profile", action="store_true",
                     help="for hardware-counter runs: the decode steps and attention launches of the default "
                          "run, then a plain 256 MiB device copy (the counters' calibration); no prefill "
@@ -315,6 +354,9 @@ def main():
         sys.exit(2)
     if args.steps is None:
         args.steps = 100 if args.workload == "full_stack" else 200
+    if args.profile_prefill:
+        _profile_prefill(args.workload, args.profile_prefill)
+        return
 
     import ctypes
 
