@@ -217,6 +217,24 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
  * over its own tokens. KIVI_E_EMPTY if a sequence holds no token. */
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
 
+/* Bytes of the library's own device scratch used by kivi_attend_decode_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define KIVI_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* kivi_attend_decode for callers that cannot allocate device memory or
+ * would rather not have the library touch the cache's partial region: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same kernels, split plan and result (bit for bit) as
+ * kivi_attend_decode, but the split partials go to the library's static
+ * device scratch of KIVI_NOALLOC_SCRATCH_BYTES instead of the cache's
+ * partial region. Calls no hipMalloc or other allocating routine; its first
+ * call on a device looks up that device's scratch address. KIVI_E_NOMEM
+ * (before any launch) when batch * n_q_heads * n_split * partial_stride
+ * exceeds the scratch (a plan of one split needs none). Every call on one
+ * GPU shares that GPU's scratch, which holds the last call's partials:
+ * calls that overlap on one GPU (other streams, other threads) race. */
+int kivi_attend_decode_noalloc(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
+
 /* One decode step in one call (page section 残差バッファ（Residual Buffer）: the
  * new token joins the fp16 residual, a group leaving the newest R is
  * quantized, and the query attends over both parts):

@@ -20,6 +20,7 @@ from ._native import (  # noqa: F401
     kivi_append,
     kivi_append_rows,
     kivi_attend_decode,
+    kivi_attend_decode_noalloc,
     kivi_cache_bytes,
     kivi_cache_create,
     kivi_cache_destroy,

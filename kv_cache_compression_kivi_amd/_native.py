@@ -64,6 +64,7 @@ _SIGS = {
     "kivi_append": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P]),
     "kivi_flush": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
     "kivi_attend_decode": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P]),
+    "kivi_attend_decode_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P]),
     "kivi_cache_query": (ctypes.c_int, [_P, ctypes.POINTER(kivi_state)]),
     "kivi_plan_append": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(kivi_state)]),
     "kivi_plan_attend": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
@@ -172,6 +173,11 @@ def kivi_flush(h: int, stream: int = 0) -> int:
 def kivi_attend_decode(h: int, q_ptr: int, q_dtype: int, out_ptr: int, stream: int = 0) -> None:
     _check(load_library().kivi_attend_decode(ctypes.c_void_p(h), ctypes.c_void_p(q_ptr), q_dtype,
                                              ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+
+def kivi_attend_decode_noalloc(h: int, q_ptr: int, q_dtype: int, out_ptr: int, stream: int = 0) -> None:
+    _check(load_library().kivi_attend_decode_noalloc(ctypes.c_void_p(h), ctypes.c_void_p(q_ptr), q_dtype,
+                                                     ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
 
 
 def kivi_decode_step(h: int, k_ptr: int, v_ptr: int, q_ptr: int, q_dtype: int, out_ptr: int,

@@ -40,9 +40,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "attend_common.hpp"
+#include "kivi.h"
 #include "split.hpp"
 
 namespace kivi {
@@ -599,8 +601,7 @@ __global__ __launch_bounds__(64 * NWAVES) void attend_kernel(const AttendArgs a)
         if (a.n_split == 1) {
             a.out[(row0 + gq) * D + c] = O / Lsum;
         } else {
-            float* rec = reinterpret_cast<float*>(g.base + g.off_partial +
-                                                  ((row0 + gq) * g.max_splits + split) * g.partial_stride);
+            float* rec = reinterpret_cast<float*>(g.partial + ((row0 + gq) * g.partial_splits + split) * g.partial_stride);
             rec[c] = O;
             if (c == 0) {
                 rec[D] = M;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const AttendArgs a) {
     const size_t row = blockIdx.x;
     const int c = threadIdx.x;
     const size_t stride = g.partial_stride / 4;
-    const float* rb = reinterpret_cast<const float*>(g.base + g.off_partial) + row * g.max_splits * stride;
+    const float* rb = reinterpret_cast<const float*>(g.partial) + row * g.partial_splits * stride;
     const int n_split = (int)row_counts<RAGGED>(a, (int64_t)(row / g.n_q_heads)).n_split;  // this batch row's splits
     float M = -INFINITY, L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < n_split; s0 += CH) {
@@ -697,7 +698,35 @@ hipError_t attend_d(const AttendArgs& a, hipStream_t s) {
     return a.g.bits == 2 ? attend_db<D, 2>(a, s) : attend_db<D, 4>(a, s);
 }
 
+// Split partials of kivi_attend_decode_noalloc: device memory the library
+// brings itself, for callers that cannot allocate. Each GPU the library runs
+// on holds its own copy until the process ends; every call on a GPU shares it.
+static __device__ __align__(256) uint8_t scratch[KIVI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device copy's address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and is the only form passed to kernels.
+hipError_t static_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     // the kernel takes the record layout from (D, BITS); it must be the one the cache uses

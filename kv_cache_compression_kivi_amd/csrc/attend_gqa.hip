@@ -712,8 +712,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
         if (a.n_split == 1) {
             a.out[(row0 + gq) * D + c] = O / Lsum;
         } else {
-            float* rec = reinterpret_cast<float*>(g.base + g.off_partial +
-                                                  ((row0 + gq) * g.max_splits + split) * g.partial_stride);
+            float* rec = reinterpret_cast<float*>(g.partial + ((row0 + gq) * g.partial_splits + split) * g.partial_stride);
             rec[c] = O;
             if (c == 0) {
                 rec[D] = M;

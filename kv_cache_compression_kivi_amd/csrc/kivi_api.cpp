@@ -62,9 +62,9 @@ kivi::CacheGeom geom(const kivi_cache* c) {
     g.off_ring = c->L.off_ring;
     g.ring_unit_stride = c->L.ring_unit_stride;
     g.ring_slots = c->L.ring_slots;
-    g.off_partial = c->L.off_partial;
+    g.partial = c->mem + c->L.off_partial;
     g.partial_stride = c->L.partial_stride;
-    g.max_splits = c->L.max_splits;
+    g.partial_splits = c->L.max_splits;
     g.batch = c->cfg.batch;
     g.n_kv_heads = c->cfg.n_kv_heads;
     g.n_q_heads = c->cfg.n_q_heads;
@@ -228,6 +228,7 @@ int validate_q(const void* q, int32_t q_dtype, const float* out) {
 }
 
 // The split plan; *cost_max receives the costliest row's cost (rows that differ).
+// No heap allocation: rows that differ number at most kMaxRaggedRows.
 kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
     const int B = c->cfg.batch;
     const int32_t group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
@@ -237,25 +238,35 @@ kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
         return kivi::plan_attend((int64_t)B * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
                                  c->L.max_splits, c->forced_splits, c->cus);
     }
-    std::vector<int64_t> cost(B);
+    int64_t cost[kivi::kMaxRaggedRows];
     for (int b = 0; b < B; ++b) cost[b] = kivi::unit_cost(c->nq[b] / G, c->nt[b] - c->nq[b]);
     int64_t cm = 1;
-    kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, B, cost.data(),
+    kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, B, cost,
                                                 max_of(c->nq) / G, c->L.max_splits, c->forced_splits, c->cus, &cm);
     if (cost_max) *cost_max = cm;
     return p;
 }
 
+// Where an attention launch writes its split partials: the cache's partial
+// region (nullptr), or other device memory of `splits` slots per query head.
+struct PartialBuf {
+    uint8_t* base;
+    int32_t splits;
+};
+
 // The attention launch over the counters of the handle. With k_new / v_new,
 // the newest token of each row for which appended[b] holds (its token n_t - 1)
-// was appended by this call and is not in the ring yet.
+// was appended by this call and is not in the ring yet. No heap allocation.
 int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
-                const void* v_new, const std::vector<char>* appended) {
+                const void* v_new, const char* appended, const kivi::AttendPlan& p, int64_t cost_max,
+                PartialBuf pb = {nullptr, 0}) {
     const int B = cache->cfg.batch;
-    int64_t cost_max = 1;
-    kivi::AttendPlan p = attend_plan(cache, &cost_max);
     kivi::AttendArgs a;
     a.g = geom(cache);
+    if (pb.base) {
+        a.g.partial = pb.base;
+        a.g.partial_splits = pb.splits;
+    }
     a.q = static_cast<const uint16_t*>(q);
     a.q_bf16 = q_dtype == KIVI_BF16;
     a.out = out;
@@ -265,28 +276,29 @@ int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, v
     a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
-    std::vector<int64_t> t_new(B, -1);
-    if (appended)
-        for (int b = 0; b < B; ++b) t_new[b] = (*appended)[b] ? cache->nt[b] - 1 : -1;
+    auto t_new = [&](int b) -> int64_t { return appended && appended[b] ? cache->nt[b] - 1 : -1; };
+    bool t_same = true;
+    for (int b = 1; b < B && t_same; ++b) t_same = t_new(b) == t_new(0);
     a.rows.n = 0;
     a.cost_max = cost_max;
     // paged blocks are read by the kernels built with a row table
-    if (!paged(cache) && rows_agree(cache) && all_same(t_new)) {
+    if (!paged(cache) && rows_agree(cache) && t_same) {
         a.n_tokens = cache->nt[0];
         a.n_quant = cache->nq[0];
         a.n_blocks = cache->nq[0] / cache->cfg.k_block;
-        a.t_new = t_new[0];
+        a.t_new = t_new(0);
     } else {
+        // rows that differ (or per-row appended tokens): at most kMaxRaggedRows rows
         a.n_tokens = max_of(cache->nt);
         a.n_quant = max_of(cache->nq);
         a.n_blocks = a.n_quant / cache->cfg.k_block;
         a.t_new = -1;
         a.rows.n = B;
-        std::vector<int64_t> cost(B);
+        int64_t cost[kivi::kMaxRaggedRows];
         for (int b = 0; b < B; ++b) {
             a.rows.n_tokens[b] = (int32_t)cache->nt[b];
             a.rows.n_quant[b] = (int32_t)cache->nq[b];
-            a.rows.t_new[b] = (int32_t)t_new[b];
+            a.rows.t_new[b] = (int32_t)t_new(b);
             a.rows.order[b] = b;
             cost[b] = kivi::unit_cost(cache->nq[b] / cache->cfg.k_block, cache->nt[b] - cache->nq[b]);
         }
@@ -296,6 +308,18 @@ int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, v
     (void)hipGetLastError();
     hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(cache, "attend launch", e);
+    return KIVI_OK;
+}
+
+// Checks common to the attention entry points: handle, query, output, and no empty sequence.
+int check_attend(kivi_cache* cache, const void* q, int32_t q_dtype, const float* out) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if ((rc = validate_q(q, q_dtype, out)) != KIVI_OK) return rc;
+    for (int b = 0; b < cache->cfg.batch; ++b)
+        if (cache->nt[b] == 0)
+            return fail(KIVI_E_EMPTY, rows_agree(cache) ? std::string("attention on an empty cache")
+                                                        : "attention with sequence " + std::to_string(b) + " empty");
     return KIVI_OK;
 }
 
@@ -541,14 +565,36 @@ int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split) {
 }
 
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
-    int rc = check_handle(cache);
+    int rc = check_attend(cache, q, q_dtype, out);
     if (rc != KIVI_OK) return rc;
-    if ((rc = validate_q(q, q_dtype, out)) != KIVI_OK) return rc;
-    for (int b = 0; b < cache->cfg.batch; ++b)
-        if (cache->nt[b] == 0)
-            return fail(KIVI_E_EMPTY, rows_agree(cache) ? std::string("attention on an empty cache")
-                                                        : "attention with sequence " + std::to_string(b) + " empty");
-    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr);
+    int64_t cost_max = 1;
+    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
+    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, p, cost_max);
+}
+
+int kivi_attend_decode_noalloc(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
+    int rc = check_attend(cache, q, q_dtype, out);
+    if (rc != KIVI_OK) return rc;
+    int64_t cost_max = 1;
+    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
+    PartialBuf pb = {nullptr, 0};
+    if (p.n_split > 1) {
+        // the partials of this call, n_split slots per query head, in the library's static scratch
+        const uint64_t need = (uint64_t)cache->cfg.batch * (uint64_t)cache->cfg.n_q_heads * (uint64_t)p.n_split *
+                              (uint64_t)cache->L.partial_stride;
+        if (need > (uint64_t)KIVI_NOALLOC_SCRATCH_BYTES)
+            return fail(KIVI_E_NOMEM, "split partials of " + std::to_string(need) + " bytes (batch * n_q_heads * " +
+                                          std::to_string(p.n_split) + " splits * " +
+                                          std::to_string(cache->L.partial_stride) +
+                                          ") exceed the static scratch of " +
+                                          std::to_string((uint64_t)KIVI_NOALLOC_SCRATCH_BYTES) + " bytes");
+        void* ptr = nullptr;
+        hipError_t e = kivi::static_scratch(&ptr);
+        if (e != hipSuccess) return fail(KIVI_E_DEVICE, std::string("static scratch: ") + hipGetErrorString(e));
+        pb.base = static_cast<uint8_t*>(ptr);
+        pb.splits = p.n_split;
+    }
+    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, p, cost_max, pb);
 }
 
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
@@ -591,7 +637,9 @@ int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void
     cache->nt = nt1;
     cache->nq = nq1;
     if (n_flushed) *n_flushed = (int32_t)fmax;
-    return attend_call(cache, q, q_dtype, out, stream, k, v, &appended);
+    int64_t cost_max = 1;
+    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
+    return attend_call(cache, q, q_dtype, out, stream, k, v, appended.data(), p, cost_max);
 }
 
 }  // extern "C"

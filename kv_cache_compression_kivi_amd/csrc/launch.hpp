@@ -17,8 +17,12 @@ struct CacheGeom {
     size_t rec_kcode, rec_vcode, rec_ksz, rec_vsz;
     size_t off_ring, ring_unit_stride;
     int64_t ring_slots;
-    size_t off_partial, partial_stride;  // partial_stride in bytes
-    int32_t max_splits;
+    // split-K partials of (batch row, query head) r, split s at
+    // partial + (r * partial_splits + s) * partial_stride (bytes): the cache's
+    // partial region, or the library's static scratch (kivi_attend_decode_noalloc)
+    uint8_t* partial;
+    size_t partial_stride;
+    int32_t partial_splits;
     int32_t batch, n_kv_heads, n_q_heads, head_dim, bits;
     // paged blocks: the caller's block table [batch][table_stride] of page
     // indices into a pool of n_pages pages (Hkv records each); null when each
@@ -160,6 +164,10 @@ __host__ __device__ inline RowCounts row_counts(const AttendArgs& a, int64_t b) 
     }
     return c;
 }
+
+// The library's static split-partial scratch on the current device
+// (kivi_attend_decode_noalloc): its device address, looked up once per device.
+hipError_t static_scratch(void** ptr);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingArgs& a, hipStream_t s);
