@@ -30,6 +30,7 @@ constexpr int kVG = 32;  // channels per value group
 // through the non-temporal (streaming) path (measured on MI355X: about 4%
 // faster prefill than plain loads and stores).
 typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u2 __attribute__((ext_vector_type(2)));
 typedef float nt_f2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
@@ -38,141 +39,235 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 
 // ------------------------------------------------------------------ codec
 
-// One group of N values -> (s, z) and its codes.
-//
-// The bytes are those of the IEEE steps (s = (max - min) / (2^b - 1) by true
-// division, code = rint((x - z) / s)), computed faster:
-//   - min and max with v_min / v_max: which zero (+0 or -0) they return never
-//     shows, since z = min + 0 drops the sign and a zero range clamps s;
-//   - q' = (x - z) * rcp(s), where rcp is within 1 ulp of 1/s, differs from the
-//     IEEE quotient q by at most (2^-23 + 2^-24) * 15.5 + 2^-20 < 2^-18 (codes
-//     <= 15), so rint(q') = rint(q) unless q' lies within 2^-18 of a half
-//     integer; within 2^-15 of one (ties included) the true division decides.
-template <int N, int BITS>
-__device__ __forceinline__ void quant_group(const float (&x)[N], float& s, float& z, uint8_t (&out)[N]) {
-    constexpr float kQmax = float((1 << BITS) - 1);
-    float mn = x[0], mx = x[0];
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+
+// Minimum and maximum of the 2N fp16 values held as N pairs (exact: the
+// extremes of fp16 values are fp16 values; which zero a tie of +0 and -0
+// returns never shows, since z = min + 0 drops the sign and a zero range
+// floors s).
+template <int N>
+__device__ __forceinline__ void minmax_pairs(const uint32_t (&p)[N], float& mn, float& mx) {
+    half2_t lo = as_h2(p[0]), hi = lo;
 #pragma unroll
     for (int i = 1; i < N; ++i) {
-        mn = fminf(mn, x[i]);
-        mx = fmaxf(mx, x[i]);
+        lo = __builtin_elementwise_min(lo, as_h2(p[i]));
+        hi = __builtin_elementwise_max(hi, as_h2(p[i]));
     }
+    mn = fminf((float)lo[0], (float)lo[1]);
+    mx = fmaxf((float)hi[0], (float)hi[1]);
+}
+
+// Scale and zero of a group from its extremes (IEEE division, no contraction),
+// and the reciprocal the fast code path multiplies by.
+template <int BITS>
+__device__ __forceinline__ void group_stats(float mn, float mx, float& s, float& z, float& rs) {
+    constexpr float kQmax = float((1 << BITS) - 1);
     s = (mx - mn) / kQmax;
     if (!(s >= 1e-8f)) s = 1e-8f;
     z = mn + 0.0f;  // -0 -> +0
-    const float rs = __builtin_amdgcn_rcpf(s);
+    rs = __builtin_amdgcn_rcpf(s);
+}
+
+// x - z for the fp16 half `hi` (0: bits 0..15, 1: bits 16..31) of `pair`,
+// rounded once to fp32: v_fma_mix_f32 widens the half exactly (subnormals
+// included) and computes x * 1 - z with one rounding, the correctly rounded
+// difference.
+template <int HI>
+__device__ __forceinline__ float half_minus(uint32_t pair, float z) {
+    float r;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(z));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(z));
+    return r;
+}
+
+// One packed word of N codes: code i = clamp(rint((x_i - z_i) / s_i), 0, 2^b - 1)
+// at bits [b i, b i + b). xp(i) gives a 32-bit word whose half (i & 1) is the
+// fp16 value x_i, zr(i) the pair (z_i, rcp(s_i)), sc(i) the scale s_i.
+//
+// The bytes are those of the IEEE steps, computed faster: t = x - z, then
+// p = t rcp(s). With rcp within 1 ulp of 1/s, p differs from the IEEE
+// quotient q by at most (2^-23 + 2^-24) 15.5 + 2^-20 < 2^-18 (codes <= 15),
+// so rint(p) = rint(q) unless p lies within 2^-18 of a half integer.
+// |p - rint(p)| is exact and at most 1/2; when its largest value over the
+// word exceeds 1/2 - 2^-15 in some lane (ties included), the wave redoes the
+// word by true division.
+// The clamp of the definition never binds on this path: 0 <= t <= max - min,
+// so 0 <= p <= (2^b - 1)(1 + 2^-22) and rint(p) is in [0, 2^b - 1] (with s
+// floored at 1e-8, p is smaller still). The division path keeps it.
+// Codes accumulate exactly in fp32, 16 bits per accumulator.
+template <int BITS, int N, class XP, class ZR, class SC>
+__device__ __forceinline__ uint32_t pack_codes(XP xp, ZR zr, SC sc) {
+    constexpr float kQmax = float((1 << BITS) - 1);
+    constexpr int H = 16 / BITS;  // codes per accumulator
+    static_assert(N == 2 * H, "a word is two 16-bit halves");
+    float acc[2] = {0.0f, 0.0f};
+    float dmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const float t = x[i] - z;
-        float r = __builtin_rintf(t * rs);
-        if (fabsf(fabsf(t * rs - r) - 0.5f) < 0x1p-15f) r = __builtin_rintf(t / s);
-        r = r < 0.0f ? 0.0f : r;
-        r = r > kQmax ? kQmax : r;
-        out[i] = (uint8_t)r;
+        const float2 q = zr(i);
+        const float t = (i & 1) ? half_minus<1>(xp(i), q.x) : half_minus<0>(xp(i), q.x);
+        const float p = t * q.y;
+        const float r = __builtin_rintf(p);
+        dmax = fmaxf(dmax, fabsf(p - r));
+        acc[i / H] = __builtin_fmaf(r, (float)(1 << (BITS * (i % H))), acc[i / H]);
     }
+    if (__builtin_amdgcn_ballot_w64(dmax > 0.5f - 0x1p-15f)) {
+        acc[0] = acc[1] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float t = (i & 1) ? half_minus<1>(xp(i), zr(i).x) : half_minus<0>(xp(i), zr(i).x);
+            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t / sc(i)), 0.0f, kQmax);
+            acc[i / H] = __builtin_fmaf(r, (float)(1 << (BITS * (i % H))), acc[i / H]);
+        }
+    }
+    return (uint32_t)acc[0] | (uint32_t)acc[1] << 16;
 }
 
 // One work-group per (key block j, unit): 2*D threads (with a row table, block
-// j0[row] + blockIdx.x of the unit's batch row, if below j1[row]). Threads [0, D) take
-// one key channel each over the block's 32 tokens; threads [D, 2D) take one
-// (token, 32-channel value group) each. Then all threads pack words.
+// j0[row] + blockIdx.x of the unit's batch row, if below j1[row]). The block's
+// 32 key and value rows are staged in LDS, then each thread plays two roles:
+//   channel thread c (tid < D): the statistics of key channel c over the
+//     block, then the packed value words of channel c (the block's 32 tokens,
+//     channel-major);
+//   token thread (t, g) (tid >= D): the statistics of value group g of token
+//     t, then the packed key words of token t's channels [32g, 32g + 32)
+//     (token-major).
+// Each thread's codes are built from the other role's statistics, so one
+// barrier separates the two halves, and every word is packed in registers.
+// (Measured on MI355X: a persistent variant that loads the next block's rows
+// into registers while coding the current one ran 10% slower: its registers
+// left four work-groups per CU instead of seven.)
 template <int D, int BITS>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     constexpr int NG = D / kVG;
-    constexpr int W = D * BITS / 32;
-    constexpr int PER = 32 / BITS;
+    constexpr int PER = 32 / BITS;  // codes per word
+    constexpr int NWG = kG / PER;   // words per 32 codes (= BITS)
     constexpr int NT = 2 * D;
-    constexpr int CPR = D / 8;  // 16-byte chunks per fp16 row
-    // fp16 rows of the block; once read, the same memory holds the codes (bytes)
-    __shared__ __align__(16) uint16_t sk[kG * D];
-    __shared__ __align__(16) uint16_t sv[kG * D];
-    uint8_t* const ck = reinterpret_cast<uint8_t*>(sk);
-    uint8_t* const cv = reinterpret_cast<uint8_t*>(sv);
+    constexpr int CPR = D / 8;      // 16-byte chunks per fp16 row
+    // staged rows, padded by 16 bytes so that the 32 rows start on different banks
+    constexpr int DP = D + 8;
+    __shared__ __align__(16) uint16_t sk[kG * DP];
+    __shared__ __align__(16) uint16_t sv[kG * DP];
+    // statistics for the codes: key (z, rcp s) of channel c at kzr[c + 2 (c / 32)]
+    // (the 32-channel groups, read together by the lanes of a wave, start on
+    // different banks), key s; value (z, rcp s) and s per group and token (rows
+    // padded apart for the same reason)
+    __shared__ __align__(16) float2 kzr[D + 2 * NG];
+    __shared__ __align__(16) float ks[D];
+    __shared__ __align__(16) float2 vzr[NG][kG + 2];
+    __shared__ __align__(16) float vs[NG][kG];
 
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
     const int64_t u = blockIdx.y;
     // this unit's blocks and ring boundary: its batch row's, when rows differ
-    const int64_t brow = u / g.n_kv_heads;
+    // (units, rows and a sequence's tokens all fit in 32 bits)
+    const int brow = (int)((uint32_t)blockIdx.y / (uint32_t)g.n_kv_heads);
     const int64_t j = (a.rows.n ? a.rows.j0[brow] : a.j0) + blockIdx.x;
     if (a.rows.n && j >= a.rows.j1[brow]) return;  // the whole work-group
     const int64_t ring_end = a.rows.n ? a.rows.ring_end[brow] : a.ring_end;
 
-    for (int idx = tid; idx < kG * CPR; idx += NT) {
+    // ring slot of the block's first token (one division per work-group)
+    const int64_t tok0 = j * kG;
+    const int rs0 = (int)((uint32_t)tok0 % (uint32_t)g.ring_slots);
+    const uint8_t* ring = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
+    const uint16_t* kin = a.k + (u * a.ntok - ring_end) * D;  // input row of token tok: kin + tok * D
+    const uint16_t* vin = a.v + (u * a.ntok - ring_end) * D;
+#pragma unroll
+    for (int it = 0; it < kG * CPR / NT; ++it) {
+        const int idx = tid + it * NT;
         const int t = idx / CPR, c16 = idx % CPR;
-        const int64_t tok = j * kG + t;
-        const uint4 *ks, *vs;
+        const int64_t tok = tok0 + t;
+        const uint4 *kp, *vp;
         if (tok < ring_end) {
-            const uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
-                                  (size_t)(tok % g.ring_slots) * 4 * D;
-            ks = reinterpret_cast<const uint4*>(slot) + c16;
-            vs = reinterpret_cast<const uint4*>(slot + 2 * D) + c16;
+            int slot = rs0 + t;  // t < 32 <= ring slots: one wrap at most
+            slot -= slot >= (int)g.ring_slots ? (int)g.ring_slots : 0;
+            const uint8_t* row = ring + (size_t)slot * 4 * D;
+            kp = reinterpret_cast<const uint4*>(row) + c16;
+            vp = reinterpret_cast<const uint4*>(row + 2 * D) + c16;
         } else {
-            const int64_t row = u * a.ntok + (tok - ring_end);
-            ks = reinterpret_cast<const uint4*>(a.k + row * D) + c16;
-            vs = reinterpret_cast<const uint4*>(a.v + row * D) + c16;
+            kp = reinterpret_cast<const uint4*>(kin + tok * D) + c16;
+            vp = reinterpret_cast<const uint4*>(vin + tok * D) + c16;
         }
-        reinterpret_cast<nt_u4*>(sk)[idx] = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(ks));
-        reinterpret_cast<nt_u4*>(sv)[idx] = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(vs));
+        *reinterpret_cast<nt_u4*>(&sk[t * DP + c16 * 8]) = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(kp));
+        *reinterpret_cast<nt_u4*>(&sv[t * DP + c16 * 8]) = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(vp));
     }
     __syncthreads();
 
     uint8_t* rec = g.base + record_offset(g, u, j);
-    uint8_t codes[kG];  // kG == kVG
-    if (tid < D) {
-        const int c = tid;
-        float x[kG];
+    const bool chan = tid < D;
+    const int c = tid;                    // channel thread
+    const int tg = tid - D;               // token thread: token t, group gg
+    const int t = tg / NG, gg = tg % NG;
+    if (chan) {
+        // key channel c over the 32 tokens (token i paired with token i + 16)
+        uint32_t p[kG / 2];
+        const _Float16* hk = reinterpret_cast<const _Float16*>(sk);
 #pragma unroll
-        for (int t = 0; t < kG; ++t) x[t] = half_bits_to_float(sk[t * D + c]);
-        float s, z;
-        quant_group<kG, BITS>(x, s, z, codes);
+        for (int i = 0; i < kG / 2; ++i) {
+            const half2_t x = {hk[i * DP + c], hk[(i + 16) * DP + c]};
+            p[i] = __builtin_bit_cast(uint32_t, x);
+        }
+        float mn, mx, s, z, r;
+        minmax_pairs(p, mn, mx);
+        group_stats<BITS>(mn, mx, s, z, r);
+        kzr[c + 2 * (c / kVG)] = make_float2(z, r);
+        ks[c] = s;
         __builtin_nontemporal_store(nt_f2{s, z}, reinterpret_cast<nt_f2*>(rec + g.rec_ksz) + c);
     } else {
-        const int idx = tid - D;
-        const int t = idx / NG, grp = idx % NG;
-        float x[kVG];
+        // value group gg of token t: 32 contiguous channels
+        uint32_t p[kVG / 2];
+        const uint4* row = reinterpret_cast<const uint4*>(&sv[t * DP + gg * kVG]);
 #pragma unroll
-        for (int i = 0; i < kVG; ++i) x[i] = half_bits_to_float(sv[t * D + grp * kVG + i]);
-        float s, z;
-        quant_group<kVG, BITS>(x, s, z, codes);
-        __builtin_nontemporal_store(nt_f2{s, z}, reinterpret_cast<nt_f2*>(rec + g.rec_vsz) + t * NG + grp);
-    }
-    __syncthreads();  // every thread is done reading the fp16 rows
-    if (tid < D) {
-#pragma unroll
-        for (int t = 0; t < kG; ++t) ck[t * D + tid] = codes[t];
-    } else {
-        const int idx = tid - D;
-        const int t = idx / NG, grp = idx % NG;
-#pragma unroll
-        for (int i = 0; i < kVG; i += 4)
-            *reinterpret_cast<uint32_t*>(&cv[t * D + grp * kVG + i]) =
-                (uint32_t)codes[i] | (uint32_t)codes[i + 1] << 8 | (uint32_t)codes[i + 2] << 16 |
-                (uint32_t)codes[i + 3] << 24;
+        for (int i = 0; i < kVG / 8; ++i) {
+            const uint4 x = row[i];
+            p[4 * i] = x.x;
+            p[4 * i + 1] = x.y;
+            p[4 * i + 2] = x.z;
+            p[4 * i + 3] = x.w;
+        }
+        float mn, mx, s, z, r;
+        minmax_pairs(p, mn, mx);
+        group_stats<BITS>(mn, mx, s, z, r);
+        vzr[gg][t] = make_float2(z, r);
+        vs[gg][t] = s;
+        __builtin_nontemporal_store(nt_f2{s, z}, reinterpret_cast<nt_f2*>(rec + g.rec_vsz) + tg);
     }
     __syncthreads();
 
-    // Pack (the record layout of kivi.h), code i of a word at bits [BITS*i, BITS*i + BITS):
-    //   key words token-major, word w of token t holds channels [w*PER, (w+1)*PER);
-    //   value words channel-major, word k of channel c holds tokens [k*PER, (k+1)*PER).
-    uint32_t* kw = reinterpret_cast<uint32_t*>(rec + g.rec_kcode);
-    uint32_t* vw = reinterpret_cast<uint32_t*>(rec + g.rec_vcode);
-    for (int idx = tid; idx < 2 * kG * W; idx += NT) {
-        uint32_t word = 0;
-        if (idx < kG * W) {
-            const int t = idx / W, w = idx % W;
-            const uint8_t* cs = ck + t * D + w * PER;
+    // Codes, packed as the record layout of kivi.h has them (code i of a word
+    // at bits [BITS*i, BITS*i + BITS)):
+    //   value words channel-major: word k of channel c holds tokens [k*PER, (k+1)*PER);
+    //   key words token-major: word w of token t holds channels [w*PER, (w+1)*PER).
+    uint32_t words[NWG];
+    if (chan) {
+        const int grp = c / kVG;
+        const uint16_t* col = &sv[c];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i] << (BITS * i);
-            __builtin_nontemporal_store(word, kw + idx);
-        } else {
-            const int x = idx - kG * W;  // x = c * BITS + k
-            const int c = x / BITS, k = x % BITS;
-            const uint8_t* cs = cv + (k * PER) * D + c;
+        for (int k = 0; k < NWG; ++k)
+            words[k] = pack_codes<BITS, PER>(
+                [&](int i) { return (uint32_t)col[(k * PER + i) * DP] << (16 * (i & 1)); },
+                [&](int i) { return vzr[grp][k * PER + i]; }, [&](int i) { return vs[grp][k * PER + i]; });
+    } else {
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(&sk[t * DP + gg * kVG]);
 #pragma unroll
-            for (int i = 0; i < PER; ++i) word |= (uint32_t)cs[i * D] << (BITS * i);
-            __builtin_nontemporal_store(word, vw + x);
+        for (int k = 0; k < NWG; ++k) {
+            const int c0 = gg * kVG + k * PER;
+            words[k] = pack_codes<BITS, PER>([&](int i) { return row[(k * PER + i) / 2]; },
+                                             [&](int i) { return kzr[c0 + i + 2 * gg]; },
+                                             [&](int i) { return ks[c0 + i]; });
         }
+    }
+    // channel c's BITS value words, or token t's BITS key words of group gg
+    // (words gg*BITS .. gg*BITS + BITS - 1 of the token's row): both contiguous
+    uint32_t* dst = reinterpret_cast<uint32_t*>(rec + (chan ? g.rec_vcode : g.rec_kcode)) + (chan ? c : tg) * NWG;
+    if constexpr (NWG == 2) {
+        __builtin_nontemporal_store(nt_u2{words[0], words[1]}, reinterpret_cast<nt_u2*>(dst));
+    } else {
+        __builtin_nontemporal_store(nt_u4{words[0], words[1], words[2], words[3]}, reinterpret_cast<nt_u4*>(dst));
     }
 }
 
