@@ -64,6 +64,9 @@ def lib():
         l.or_attend.argtypes = [P, P, i32, P]
         l.or_num_threads.restype = i32
         l.or_set_num_threads.argtypes = [i32]
+        l.or_squat_token.argtypes = [P, P, P, P, i32, i32, P]
+        l.or_squat_replay.argtypes = [P, P, P, P, i32, i32, P, P, P]
+        l.or_cache_set_squat.argtypes = [P, P]
         _lib = l
     return _lib
 
@@ -141,6 +144,28 @@ def set_num_threads(n: int) -> None:
     lib().or_set_num_threads(int(n))
 
 
+def squat_token(k, s, z, g, bits: int) -> np.ndarray:
+    """SQuat-style codes of one key: k [d] fp32 (a widened fp16 key), s, z [d]
+    fp32 (its block's per-channel statistics), g [d, d] fp32 update coefficients."""
+    k, s, z = (np.ascontiguousarray(a, dtype=np.float32) for a in (k, s, z))
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    codes = np.empty(k.size, np.uint8)
+    lib().or_squat_token(_ptr(k), _ptr(s), _ptr(z), _ptr(g), k.size, bits, _ptr(codes))
+    return codes
+
+
+def squat_replay(k, s, z, g, bits: int, given):
+    """The oracle's walk along the codes `given`: (own decisions uint8 [d],
+    quotients (x - z) / s of its own trajectory, fp64 [d])."""
+    k, s, z = (np.ascontiguousarray(a, dtype=np.float32) for a in (k, s, z))
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    given = np.ascontiguousarray(given, dtype=np.uint8)
+    own = np.empty(k.size, np.uint8)
+    q = np.empty(k.size, np.float64)
+    lib().or_squat_replay(_ptr(k), _ptr(s), _ptr(z), _ptr(g), k.size, bits, _ptr(given), _ptr(own), _ptr(q))
+    return own, q
+
+
 class OracleCache:
     """The oracle's cache: full fp16 history per (batch, KV head) unit,
     quantized token by token as the residual ring overflows or is flushed."""
@@ -171,6 +196,13 @@ class OracleCache:
 
     def flush(self) -> int:
         return int(lib().or_flush(self._h))
+
+    def set_squat(self, g):
+        """Key blocks quantized from now on take SQuat-style codes with the
+        per-unit update coefficients g [units, d, d] (fp32)."""
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        assert g.shape == (self.batch * self.n_kv_heads, self.head_dim, self.head_dim)
+        lib().or_cache_set_squat(self._h, _ptr(g))
 
     def state(self):
         nt = ctypes.c_int64()

@@ -112,6 +112,8 @@ struct or_cache {
      * V stats [unit][max_tokens][d/vg] */
     uint8_t *k_codes, *v_codes;
     float *k_s, *k_z, *v_s, *v_z;
+    /* SQuat-style key coder: per unit d x d update coefficients, or NULL */
+    float* squat_g;
 };
 
 static int64_t units(const or_cache* c) { return (int64_t)c->B * c->Hkv; }
@@ -144,6 +146,7 @@ void or_cache_free(or_cache* c) {
     if (!c) return;
     free(c->k_hist); free(c->v_hist); free(c->k_codes); free(c->v_codes);
     free(c->k_s); free(c->k_z); free(c->v_s); free(c->v_z);
+    free(c->squat_g);
     free(c);
 }
 
@@ -164,6 +167,17 @@ static void quantize_key_block(or_cache* c, int64_t u, int64_t j) {
     }
     free(x);
     free(q);
+    if (c->squat_g) {
+        /* SQuat-style codes of the block's tokens, with the statistics just taken */
+        float* kf = (float*)malloc(sizeof(float) * (size_t)d);
+        for (int t = 0; t < G; ++t) {
+            const int64_t tok = j * G + t;
+            for (int ch = 0; ch < d; ++ch) kf[ch] = or_half_to_float(c->k_hist[(u * c->max_tokens + tok) * d + ch]);
+            or_squat_token(kf, &c->k_s[(u * max_blocks(c) + j) * d], &c->k_z[(u * max_blocks(c) + j) * d],
+                           &c->squat_g[(size_t)u * d * d], d, c->bits, &c->k_codes[(u * c->max_tokens + tok) * d]);
+        }
+        free(kf);
+    }
 }
 
 /* Section Per-Token量子化（Value Cache）: value statistics per token; here over
@@ -329,6 +343,74 @@ int or_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ---------------------------------------------------------------- SQuat-style keys */
+
+/* The SQuat explainer page (aibr.jp, "SQuat": KV cache quantization whose
+ * error is kept orthogonal to a query subspace), section 3 中核となる技術的要素:
+ * a key is quantized element by element, and after each element the elements
+ * not yet quantized are corrected by the closed-form optimal update, so that
+ * the error stays (as far as the remaining elements allow) orthogonal to the
+ * query subspace; scales and zero points are stored as in plain low-bit
+ * quantization.
+ *
+ * Reading taken here (the page gives no formulas): element c of a key, in
+ * channel order, is coded with the KIVI group (s_c, z_c) of its channel and
+ * block (section 量子化アルゴリズム of the KIVI page); with delta = x_c -
+ * D(code), D(code) = fma(s_c, code, z_c) in fp32, every later element j > c
+ * becomes x_j = fma(-delta, g[c][j], x_j) in fp32, where g (d x d, fp32, only
+ * j > c used) are the update coefficients of the quadratic objective
+ * ||U^T e||^2 + lambda ||e||^2 (U: the query subspace basis), computed by the
+ * caller. The code of an element is decided exactly as in or_quant_group:
+ * clamp(rint((x - z) / s), 0, 2^b - 1) in fp32. */
+static uint8_t squat_code(float x, float s, float z, float qmax) {
+    float r = rintf((x - z) / s);
+    if (r < 0.0f) r = 0.0f;
+    if (r > qmax) r = qmax;
+    return (uint8_t)r;
+}
+
+void or_squat_token(const float* k, const float* s, const float* z, const float* g, int d, int bits,
+                    uint8_t* codes) {
+    const float qmax = (float)((1 << bits) - 1);
+    float* x = (float*)malloc(sizeof(float) * (size_t)d);
+    memcpy(x, k, sizeof(float) * (size_t)d);
+    for (int c = 0; c < d; ++c) {
+        codes[c] = squat_code(x[c], s[c], z[c], qmax);
+        const float delta = x[c] - fmaf(s[c], (float)codes[c], z[c]);
+        for (int j = c + 1; j < d; ++j) x[j] = fmaf(-delta, g[(size_t)c * d + j], x[j]);
+    }
+    free(x);
+}
+
+/* The same walk, but following the codes `given` (e.g. another
+ * implementation's) instead of its own decisions. For each element it writes
+ * the quotient (x_c - z_c) / s_c of its own trajectory (in fp64, from the fp32
+ * x_c) to q[c], and its own fp32 decision to own[c]; the caller judges a
+ * given code that differs from `own` by the quotient's distance to the
+ * rounding boundary between the two. */
+void or_squat_replay(const float* k, const float* s, const float* z, const float* g, int d, int bits,
+                     const uint8_t* given, uint8_t* own, double* q) {
+    const float qmax = (float)((1 << bits) - 1);
+    float* x = (float*)malloc(sizeof(float) * (size_t)d);
+    memcpy(x, k, sizeof(float) * (size_t)d);
+    for (int c = 0; c < d; ++c) {
+        own[c] = squat_code(x[c], s[c], z[c], qmax);
+        q[c] = ((double)x[c] - (double)z[c]) / (double)s[c];
+        const float delta = x[c] - fmaf(s[c], (float)given[c], z[c]);
+        for (int j = c + 1; j < d; ++j) x[j] = fmaf(-delta, g[(size_t)c * d + j], x[j]);
+    }
+    free(x);
+}
+
+/* Key coder of the cache: with per-unit coefficients set (or_cache_set_squat),
+ * every key block quantized afterwards takes its channel statistics as
+ * before and its codes token by token from or_squat_token. */
+void or_cache_set_squat(or_cache* c, const float* g) {
+    const size_t n = (size_t)(c->B * c->Hkv) * (size_t)c->d * (size_t)c->d;
+    if (!c->squat_g) c->squat_g = (float*)malloc(sizeof(float) * n);
+    memcpy(c->squat_g, g, sizeof(float) * n);
 }
 
 /* Threads the OpenMP loops above use from now on (n >= 1). */

@@ -59,6 +59,9 @@ void or_pack_rows(const uint8_t* codes, int64_t rows, int d, int bits, uint32_t*
 
 /* The cache: B sequences x Hkv heads ("units"), each with its full fp16 history. */
 typedef struct or_cache or_cache;
+/* Key blocks quantized from now on take SQuat-style codes with the per-unit
+ * coefficients g ([units][d][d] fp32, copied). */
+void or_cache_set_squat(or_cache* c, const float* g);
 
 or_cache* or_cache_new(int batch, int n_kv_heads, int n_q_heads, int head_dim, int bits,
                        int k_block, int v_group, int residual, int max_tokens);
@@ -86,6 +89,18 @@ int or_attend(const or_cache* c, const uint16_t* q, int q_is_bf16, double* out);
 int or_num_threads(void);
 /* Sets the number of OpenMP threads later calls use (n >= 1). */
 void or_set_num_threads(int n);
+
+/* SQuat-style key codes (the SQuat explainer page, section 3 中核となる技術的要素):
+ * one key of d fp32 values (widened fp16), coded element by element in channel
+ * order with its block's per-channel (s, z); after element c the later
+ * elements move by -delta * g[c][j] (fp32 fma), delta = x_c - fma(s_c, code, z_c).
+ * g: d x d fp32 row-major (only j > c read). */
+void or_squat_token(const float* k, const float* s, const float* z, const float* g, int d, int bits,
+                    uint8_t* codes);
+/* The walk of or_squat_token along the codes `given`: own[c] its own decision at
+ * each element, q[c] its quotient (x_c - z_c) / s_c in fp64. */
+void or_squat_replay(const float* k, const float* s, const float* z, const float* g, int d, int bits,
+                     const uint8_t* given, uint8_t* own, double* q);
 
 #ifdef __cplusplus
 }

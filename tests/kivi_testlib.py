@@ -91,3 +91,28 @@ def assert_attention_close(got, want):
     max_abs, rel_l2 = attention_error(got, want)
     assert max_abs <= ATOL_MAX and rel_l2 <= REL_L2, f"max_abs {max_abs:.3e} rel_l2 {rel_l2:.3e}"
     return max_abs, rel_l2
+
+
+def squat_code_check(kf, s, z, g, bits, codes, tau=1e-3):
+    """Judges SQuat-style key codes from another implementation against the
+    oracle's walk. kf [T, d] fp32 keys, s, z [T, d] their blocks' per-channel
+    statistics (row t: token t's block), g [d, d] fp32 update coefficients,
+    codes [T, d]. The oracle walks each key along the given codes; a given code
+    that differs from the oracle's own decision there must be the neighbour
+    across a rounding boundary that the oracle's quotient lies within tau of
+    (in code units): the two implementations' coefficients differ in their last
+    bits, so either side of such a boundary is a correct rounding.
+    Returns (number of codes that differ, largest boundary distance among them);
+    raises AssertionError on a code that is not a valid rounding."""
+    n_diff, worst = 0, 0.0
+    for t in range(kf.shape[0]):
+        own, q = oracle.squat_replay(kf[t], s[t], z[t], g, bits, codes[t])
+        bad = np.nonzero(own != codes[t])[0]
+        for c in bad:
+            lo = min(int(own[c]), int(codes[t][c]))
+            assert abs(int(own[c]) - int(codes[t][c])) == 1, (t, c, own[c], codes[t][c], q[c])
+            dist = abs(q[c] - (lo + 0.5))
+            assert dist <= tau, (t, c, own[c], codes[t][c], q[c])
+            worst = max(worst, dist)
+        n_diff += bad.size
+    return n_diff, worst
