@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KIVI_ABI_VERSION 3
+#define KIVI_ABI_VERSION 4
 
 typedef enum {
     KIVI_OK = 0,
@@ -89,6 +89,8 @@ typedef struct {
     int32_t max_tokens;  /* capacity of every sequence */
     int32_t max_splits;  /* split-K partial slots per query head (0 = default) */
     int32_t n_pages;     /* 0: one contiguous region per unit; > 0: pages in the shared pool */
+    int32_t squat_rank;  /* 0: keys coded per element by rounding (KIVI); 1..32: the SQuat-style
+                            key coder with a query subspace of this rank (head_dim 64 or 128) */
 } kivi_config;
 
 /* Device-memory layout of a cache, a pure function of the config. All offsets
@@ -125,6 +127,9 @@ typedef struct {
     int32_t max_splits;
     int32_t n_pages;    /* pages in the pool (0: not paged) */
     size_t page_bytes;  /* Hkv * block_bytes (paged) */
+    size_t off_squat;   /* squat_rank > 0: unit u's head_dim x head_dim fp32 update coefficients at
+                           off_squat + u * head_dim^2 * 4 (row c, column j: the move of key element
+                           j per unit error of element c; 0 for j <= c) */
 } kivi_layout;
 
 /* Counters of a cache. Tokens [0, n_quant) are quantized, [n_quant, n_tokens)
@@ -216,6 +221,27 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed);
  * streams) are not allowed: they share the split partials. Each row attends
  * over its own tokens. KIVI_E_EMPTY if a sequence holds no token. */
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
+
+/* SQuat-style key coder (the SQuat explainer page, aibr.jp "SQuat", section 3
+ * 中核となる技術的要素): keys are quantized element by element, and after each
+ * element the elements not yet quantized take the closed-form optimal
+ * correction, keeping the error (as far as the remaining elements allow)
+ * orthogonal to a subspace of past queries. Scales, zeros, value codes and
+ * the record layout stay those of the plain coder, so attention reads such a
+ * cache unchanged.
+ * kivi_squat_build computes every unit's update coefficients from past
+ * queries: q device [B][Hq][n_q][head_dim] of q_dtype (each query head's n_q
+ * past queries, e.g. the prompt's), contiguous. Per unit (batch row, KV head):
+ * the rank-squat_rank subspace of largest second moment of its query heads'
+ * queries, then the coefficients of the objective ||U^T e||^2 + lambda ||e||^2
+ * of a key's error e (U the subspace basis); lambda > 0 bounds the correction
+ * once fewer free elements remain than the subspace has dimensions. Key
+ * blocks quantized by later calls (appends, flushes, decode steps) use them;
+ * blocks quantized before the first build keep plain codes. A new build
+ * replaces the coefficients of every row (e.g. after a row takes a new
+ * sequence). KIVI_E_INVAL on a cache with squat_rank = 0, n_q < 1 or lambda
+ * not a positive finite number. */
+int kivi_squat_build(kivi_cache* cache, const void* q, int32_t q_dtype, int32_t n_q, float lambda, void* stream);
 
 /* Bytes of the library's own device scratch used by kivi_attend_decode_noalloc
  * (one copy per GPU, held until the process ends). */

@@ -101,6 +101,26 @@ class KVWorkload:
         return q.to(dtype).contiguous()
 
 
+def query_history(workload: "KVWorkload", n_q_heads: int, n: int, rank: int = 8, noise: float = 0.1,
+                  dtype=torch.float16):
+    """Past queries [B, Hq, n, d] for the SQuat-style key coder, drawn with a
+    low-rank structure (the SQuat page describes the future queries as
+    concentrated in a subspace of past ones): the query heads that share KV
+    head h draw q = A_h z + noise, with A_h [d, rank] fixed per KV head
+    (columns scaled 3 .. 1), z ~ N(0, 1) per query, noise ~ N(0, noise^2) per
+    element. Generator seeded with hash(S, L, 5)."""
+    B, Hkv, d = workload.batch, workload.n_kv_heads, workload.head_dim
+    g = torch.Generator(device=workload.device)
+    g.manual_seed(_mix(workload.seed, workload.layer, 5))
+    a = torch.randn(Hkv, d, rank, generator=g, device=workload.device)
+    a = a * torch.linspace(3.0, 1.0, rank, device=workload.device)
+    z = torch.randn(B, n_q_heads, rank, n, generator=g, device=workload.device)
+    head_of = torch.arange(n_q_heads, device=workload.device) // (n_q_heads // Hkv)
+    q = torch.einsum("hdr,bhrn->bhnd", a[head_of], z)
+    q = q + noise * torch.randn(B, n_q_heads, n, d, generator=g, device=workload.device)
+    return q.to(dtype).contiguous()
+
+
 def row_lengths(batch: int, t_min: int, t_max: int, seed: int) -> list:
     """Seeded per-row sequence lengths, uniform over [t_min, t_max]."""
     g = torch.Generator()

@@ -38,6 +38,7 @@ from ._native import (  # noqa: F401
     kivi_reset_row,
     kivi_set_block_table,
     kivi_set_attend_splits,
+    kivi_squat_build,
     kivi_state,
     library_path,
     load_library,

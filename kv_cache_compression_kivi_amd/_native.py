@@ -27,7 +27,7 @@ class KiviError(RuntimeError):
 class kivi_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_kv_heads", "n_q_heads", "head_dim", "bits", "k_block", "v_group",
-        "residual", "max_tokens", "max_splits", "n_pages")]
+        "residual", "max_tokens", "max_splits", "n_pages", "squat_rank")]
 
 
 class kivi_layout(ctypes.Structure):
@@ -42,6 +42,7 @@ class kivi_layout(ctypes.Structure):
         ("off_partial", ctypes.c_size_t), ("partial_stride", ctypes.c_size_t),
         ("max_splits", ctypes.c_int32),
         ("n_pages", ctypes.c_int32), ("page_bytes", ctypes.c_size_t),
+        ("off_squat", ctypes.c_size_t),
     ]
 
 
@@ -65,6 +66,7 @@ _SIGS = {
     "kivi_flush": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
     "kivi_attend_decode": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P]),
     "kivi_attend_decode_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P]),
+    "kivi_squat_build": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P]),
     "kivi_cache_query": (ctypes.c_int, [_P, ctypes.POINTER(kivi_state)]),
     "kivi_plan_append": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(kivi_state)]),
     "kivi_plan_attend": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
@@ -212,10 +214,15 @@ def kivi_set_attend_splits(h: int, n_key_splits: int) -> None:
     _check(load_library().kivi_set_attend_splits(ctypes.c_void_p(h), n_key_splits))
 
 
+def kivi_squat_build(h: int, q_ptr: int, q_dtype: int, n_q: int, lam: float, stream: int = 0) -> None:
+    _check(load_library().kivi_squat_build(ctypes.c_void_p(h), ctypes.c_void_p(q_ptr), q_dtype, n_q, lam,
+                                           ctypes.c_void_p(stream)))
+
+
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual=128, k_block=32,
-                v_group=32, max_splits=0, n_pages=0) -> kivi_config:
+                v_group=32, max_splits=0, n_pages=0, squat_rank=0) -> kivi_config:
     return kivi_config(batch, n_kv_heads, n_q_heads, head_dim, bits, k_block, v_group, residual, max_tokens,
-                       max_splits, n_pages)
+                       max_splits, n_pages, squat_rank)
 
 
 class KiviCache:
@@ -226,10 +233,10 @@ class KiviCache:
     """
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual=128,
-                 k_block=32, v_group=32, max_splits=0, device="cuda", memory=None, n_pages=0):
+                 k_block=32, v_group=32, max_splits=0, device="cuda", memory=None, n_pages=0, squat_rank=0):
         import torch
         self.cfg = make_config(batch, n_kv_heads, n_q_heads, head_dim, bits, max_tokens, residual,
-                               k_block, v_group, max_splits, n_pages)
+                               k_block, v_group, max_splits, n_pages, squat_rank)
         self.block_table = None
         self.nbytes = kivi_cache_bytes(self.cfg)
         self.layout = kivi_cache_layout(self.cfg)
@@ -348,6 +355,25 @@ class KiviCache:
 
     def set_attend_splits(self, n):
         kivi_set_attend_splits(self.handle, n)
+
+    def squat_build(self, q_hist, lam=0.1, stream=None):
+        """Update coefficients of the SQuat-style key coder from past queries
+        q_hist [batch, n_q_heads, n_q, head_dim] (fp16 or bf16, on the device)."""
+        import torch
+        c = self.cfg
+        if q_hist.dtype not in (torch.float16, torch.bfloat16) or not q_hist.is_cuda or \
+                not q_hist.is_contiguous() or q_hist.dim() != 4 or \
+                tuple(q_hist.shape[:2]) != (c.batch, c.n_q_heads) or q_hist.shape[3] != c.head_dim:
+            raise ValueError("q_hist must be a contiguous fp16/bf16 [batch, n_q_heads, n_q, head_dim] device tensor")
+        kivi_squat_build(self.handle, q_hist.data_ptr(), KIVI_BF16 if q_hist.dtype == torch.bfloat16 else KIVI_F16,
+                         q_hist.shape[2], float(lam), self._stream(stream))
+
+    def squat_coefficients(self, unit):
+        """Unit's update coefficients [head_dim, head_dim] as the device holds them (fp32)."""
+        import torch
+        d = self.cfg.head_dim
+        start = self.layout.off_squat + unit * d * d * 4
+        return self.memory[start:start + d * d * 4].view(torch.float32).reshape(d, d)
 
     def reset(self):
         kivi_cache_reset(self.handle)

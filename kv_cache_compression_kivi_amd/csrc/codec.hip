@@ -33,10 +33,6 @@ typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
 typedef unsigned int nt_u2 __attribute__((ext_vector_type(2)));
 typedef float nt_f2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
-    return __half2float(__ushort_as_half(h));
-}
-
 // ------------------------------------------------------------------ codec
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -32,6 +32,8 @@ struct kivi_cache {
     int32_t forced_splits;
     // compute units of the device current at create time (the split plans fill them)
     int32_t cus;
+    // SQuat-style key coder: coefficients built (kivi_squat_build)
+    bool squat_ready;
     bool poisoned;
 };
 
@@ -73,6 +75,7 @@ kivi::CacheGeom geom(const kivi_cache* c) {
     g.table = c->cfg.n_pages > 0 ? c->table : nullptr;
     g.table_stride = c->table_stride;
     g.n_pages = c->cfg.n_pages;
+    g.off_squat = c->L.off_squat;
     return g;
 }
 
@@ -166,6 +169,12 @@ int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, i
         }
         hipError_t e = kivi::launch_quantize(a, s);
         if (e != hipSuccess) return device_fail(c, "quantize launch", e);
+        // SQuat-style key codes over the blocks just quantized (before the
+        // ring write below: they read ring slots it may overwrite)
+        if (c->cfg.squat_rank > 0 && c->squat_ready) {
+            e = kivi::launch_squat_codes(a, s);
+            if (e != hipSuccess) return device_fail(c, "squat codes launch", e);
+        }
     }
     if (ntk > 0) {
         kivi::RingArgs a;
@@ -393,6 +402,7 @@ int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_
     c->table_stride = 0;
     c->forced_splits = 0;
     c->cus = device_cus();
+    c->squat_ready = false;
     c->poisoned = false;
     *out = c;
     return KIVI_OK;
@@ -561,6 +571,28 @@ int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split) {
     if (n_split < 0 || n_split > cache->L.max_splits)
         return fail(KIVI_E_INVAL, "n_split must be in [0, max_splits]");
     cache->forced_splits = n_split;
+    return KIVI_OK;
+}
+
+int kivi_squat_build(kivi_cache* cache, const void* q, int32_t q_dtype, int32_t n_q, float lambda, void* stream) {
+    int rc = check_handle(cache);
+    if (rc != KIVI_OK) return rc;
+    if (cache->cfg.squat_rank <= 0) return fail(KIVI_E_INVAL, "the cache was made with squat_rank = 0");
+    if (!q || !aligned16(q)) return fail(KIVI_E_INVAL, "q must be a 16-byte aligned device pointer");
+    if (q_dtype != KIVI_F16 && q_dtype != KIVI_BF16) return fail(KIVI_E_INVAL, "q_dtype must be KIVI_F16 or KIVI_BF16");
+    if (n_q < 1) return fail(KIVI_E_INVAL, "n_q must be >= 1");
+    if (!(lambda > 0.0f) || !std::isfinite(lambda)) return fail(KIVI_E_INVAL, "lambda must be a positive finite number");
+    kivi::SquatBuildArgs a;
+    a.g = geom(cache);
+    a.q = static_cast<const uint16_t*>(q);
+    a.q_bf16 = q_dtype == KIVI_BF16;
+    a.n_q = n_q;
+    a.rank = cache->cfg.squat_rank;
+    a.lambda = lambda;
+    (void)hipGetLastError();
+    hipError_t e = kivi::launch_squat_build(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(cache, "squat build launch", e);
+    cache->squat_ready = true;
     return KIVI_OK;
 }
 

@@ -30,6 +30,9 @@ struct CacheGeom {
     const int32_t* table;
     int64_t table_stride;
     int32_t n_pages;
+    // SQuat-style key coder: per unit a head_dim x head_dim fp32 matrix (the
+    // update coefficients) at off_squat + u * head_dim^2 * 4
+    size_t off_squat;
 };
 
 // Paged blocks: the table entry of batch row b's key block j, read through
@@ -165,6 +168,20 @@ __host__ __device__ inline RowCounts row_counts(const AttendArgs& a, int64_t b) 
     return c;
 }
 
+// Largest query-subspace rank of the SQuat-style key coder.
+constexpr int kSquatMaxRank = 32;
+
+// Builds every unit's update coefficients from n_q past queries per query
+// head (q: [B][Hq][n_q][head_dim] fp16 or bf16), rank-`rank` subspace, lambda.
+struct SquatBuildArgs {
+    CacheGeom g;
+    const uint16_t* q;
+    int32_t q_bf16;
+    int64_t n_q;
+    int32_t rank;
+    float lambda;
+};
+
 // The library's static split-partial scratch on the current device
 // (kivi_attend_decode_noalloc): its device address, looked up once per device.
 hipError_t static_scratch(void** ptr);
@@ -172,5 +189,10 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// SQuat-style key coder (head_dim 64 or 128): the coefficients, and the key
+// codes of the blocks a QuantArgs launch just quantized (after it, before the
+// ring write of the same call).
+hipError_t launch_squat_build(const SquatBuildArgs& a, hipStream_t s);
+hipError_t launch_squat_codes(const QuantArgs& a, hipStream_t s);
 
 }  // namespace kivi

@@ -74,6 +74,14 @@ inline int validate_config(const kivi_config* c, std::string& err) {
         err = "paged blocks need batch <= " + std::to_string(KIVI_MAX_RAGGED_BATCH);
         return KIVI_E_UNSUPPORTED;
     }
+    if (c->squat_rank < 0) {
+        err = "squat_rank must be >= 0";
+        return KIVI_E_INVAL;
+    }
+    if (c->squat_rank > 0 && (c->head_dim > 128 || c->squat_rank > 32 || c->squat_rank > c->head_dim)) {
+        err = "the SQuat-style key coder needs head_dim 64 or 128 and squat_rank <= min(32, head_dim)";
+        return KIVI_E_UNSUPPORTED;
+    }
     const int64_t W = (int64_t)c->head_dim * c->bits / 32;
     const int64_t block_bytes = 2 * 32 * W * 4 + (int64_t)c->head_dim * 8 + 32 * (c->head_dim / 32) * 8;
     if ((int64_t)(c->max_tokens / c->k_block) * block_bytes > (int64_t)0xffffffff) {
@@ -111,8 +119,9 @@ inline void compute_layout(const kivi_config* c, kivi_layout* L) {
     L->off_partial = align_up(L->off_ring + (size_t)units * L->ring_unit_stride);
     L->max_splits = c->max_splits ? c->max_splits : kDefaultMaxSplits;
     L->partial_stride = (d + 4) * 4;
-    L->total_bytes = align_up(L->off_partial + (size_t)c->batch * c->n_q_heads *
-                                                   (size_t)L->max_splits * L->partial_stride);
+    L->off_squat = align_up(L->off_partial + (size_t)c->batch * c->n_q_heads * (size_t)L->max_splits *
+                                                 L->partial_stride);
+    L->total_bytes = L->off_squat + (c->squat_rank > 0 ? align_up((size_t)units * d * d * 4) : 0);
 }
 
 // What one kivi_append(ntok) does, as closed forms of the token-by-token rule.

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(native):
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(native.EXPORTED)
-    assert native.kivi_abi_version() == 3
+    assert native.kivi_abi_version() == 4
     nm = subprocess.run(["nm", "-D", "--defined-only", native.library_path()], capture_output=True, text=True).stdout
     for name in declared:
         assert re.search(r"\bT " + name + r"\b", nm), name
@@ -64,6 +64,9 @@ def _cfg(native, **kw):
     (dict(residual=100), "KIVI_E_INVAL"),
     (dict(max_splits=1), "KIVI_E_INVAL"),
     (dict(batch=70000, n_kv_heads=1, n_q_heads=1), "KIVI_E_INVAL"),
+    (dict(squat_rank=-1), "KIVI_E_INVAL"),
+    (dict(squat_rank=33), "KIVI_E_UNSUPPORTED"),
+    (dict(squat_rank=4, head_dim=256), "KIVI_E_UNSUPPORTED"),
 ])
 def test_config_validation(native, bad, status):
     with pytest.raises(native.KiviError) as e:
@@ -90,6 +93,33 @@ def test_layout_closed_form(native, bits, d):
     assert L.partial_stride == (d + 4) * 4 and L.max_splits == 256
     assert L.total_bytes >= L.off_partial + 2 * 8 * 256 * L.partial_stride
     assert native.kivi_cache_bytes(cfg) == L.total_bytes
+    assert L.off_squat == L.total_bytes  # no coefficient region without the SQuat-style coder
+    sq = native.kivi_cache_layout(_cfg(native, bits=bits, head_dim=d, max_tokens=4096, squat_rank=8)) \
+        if d <= 128 else None
+    if sq is not None:
+        assert sq.off_squat % 256 == 0 and sq.off_squat >= L.total_bytes - 255
+        assert sq.total_bytes == sq.off_squat + -(-units * d * d * 4 // 256) * 256
+
+
+def test_squat_build_refusals(native):
+    """Host-side checks of kivi_squat_build (nothing is launched)."""
+    import ctypes
+    lib = native.load_library()
+    buf = ctypes.create_string_buffer(8 << 20)
+    mem = (ctypes.addressof(buf) + 255) // 256 * 256  # a host address: only validated, never launched on
+    plain = _cfg(native, max_tokens=64)
+    sq = _cfg(native, max_tokens=64, squat_rank=4)
+    for cfg, q, n_q, lam, want in [(plain, 256, 8, 0.1, -1), (sq, 0, 8, 0.1, -1), (sq, 257, 8, 0.1, -1),
+                                   (sq, 256, 0, 0.1, -1), (sq, 256, 8, 0.0, -1), (sq, 256, 8, float("inf"), -1),
+                                   (sq, 256, 8, float("nan"), -1)]:
+        assert native.kivi_cache_bytes(cfg) <= (8 << 20) - 256
+        h = native.kivi_cache_create(cfg, mem, (8 << 20) - 256)
+        try:
+            rc = lib.kivi_squat_build(ctypes.c_void_p(h), ctypes.c_void_p(q), 0, n_q, lam, None)
+            assert rc == want, (rc, native.kivi_last_error())
+            assert native.kivi_last_error()
+        finally:
+            native.kivi_cache_destroy(h)
 
 
 def test_create_and_host_only_calls(native):
