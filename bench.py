@@ -144,6 +144,8 @@ def _cpu_baseline(cfg, seconds=8.0):
     workload's: every (batch row, KV head) unit costs the oracle the same, so
     bytes, tokens and time all scale by the same unit count. Reported in the
     GPU line's units."""
+    import numpy as np
+
     import oracle
     from kivi_inputs import KVWorkload
 
@@ -156,9 +158,21 @@ def _cpu_baseline(cfg, seconds=8.0):
     q = wl.q(Hq, dtype=torch.bfloat16 if q_bf16 else torch.float16)
     n_all = oracle.num_threads()
 
+    gs = None
+    if cfg.get("squat_rank"):
+        # the SQuat-style coder: the oracle's coefficients from the sample's past queries (set-up, not timed)
+        from oracle import squat
+        from kivi_inputs import query_history
+        qh = query_history(wl, Hq, cfg["squat_queries"], rank=cfg["squat_rank"]).float().numpy()
+        group = Hq // Hkv
+        gs = np.stack([squat.unit_coefficients(qh[0, h * group:(h + 1) * group].reshape(-1, d),
+                                               cfg["squat_rank"], cfg["squat_lambda"]) for h in range(Hkv)])
+
     def run(threads, secs):
         oracle.set_num_threads(threads)
         oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
+        if gs is not None:
+            oc.set_squat(gs)
         t0 = time.perf_counter()
         oc.append(k, v)
         oc.flush()
@@ -291,6 +305,77 @@ def _stream_probe(dev, nbytes=256 << 20):
             "sum_read_gbs": round(nbytes / (best_sum * 1e-3) / 1e9, 1), "how": "torch copy_ / sum, best of 5"}
 
 
+PEAK_FP32_TFLOPS = 157.3
+
+
+def _squat_measure(kv, cfg, dev, caches, prefill_inputs, reps=8):
+    """The SQuat-style key coder on the workload's first layer: the build of
+    the coefficients (HIP events), and the prefill (append(T) + flush into an
+    empty cache) with the coder against the same prefill on a cache without
+    it; the difference is the code kernel's time (the launches are otherwise
+    the same). Its algorithmic work, in the subspace's coordinates, is 2 r
+    fused multiply-adds per element (the correction it receives and the update
+    it makes), 2 flops each, against the fp32 vector peak; it also reads the
+    fp16 key rows again and writes the key codes."""
+    import torch
+
+    import kv_cache_compression_kivi_amd as kvm
+    from kivi_inputs import KVWorkload, query_history
+
+    B, Hkv, Hq, d, T = cfg["batch"], cfg["n_kv_heads"], cfg["n_q_heads"], cfg["head_dim"], cfg["T"]
+    bits, rank, lam, nqh = cfg.get("bits", 2), cfg["squat_rank"], cfg["squat_lambda"], cfg["squat_queries"]
+    k, v = prefill_inputs[min(prefill_inputs)]
+    qh = query_history(KVWorkload(B, Hkv, d, seed=cfg["seed"], device=dev), Hq, nqh, rank=rank)
+    sq = kvm.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=dev, squat_rank=rank)
+    plain = kvm.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    def prefill(c):
+        c.reset()
+        c.append(k, v)
+        c.flush()
+
+    sq.squat_build(qh, lam)  # warm
+    torch.cuda.synchronize()
+    build_us = min(timed(lambda: sq.squat_build(qh, lam)) for _ in range(3))
+    prefill(sq)
+    prefill(plain)
+    t_sq, t_pl = [], []
+    for _ in range(reps):
+        t_sq.append(timed(lambda: prefill(sq)))
+        t_pl.append(timed(lambda: prefill(plain)))
+    us_sq, us_pl = sum(t_sq) / reps, sum(t_pl) / reps
+    nq = sq.state()[1]
+    # per quantized token per unit: the correction u_c . a and the update a += delta w_c, r FMAs
+    # each, for each of the d elements (2 flops per FMA); the key row read (fp16) and the codes written
+    flops = 2.0 * B * Hkv * nq * d * 2 * rank
+    nbytes = B * Hkv * nq * (2 * d + d * bits // 8)
+    codes_us = us_sq - us_pl
+    tf = flops / (codes_us * 1e-6) / 1e12
+    return {
+        "rank": rank, "lambda": lam, "past_queries_per_head": nqh,
+        "build_us": round(build_us, 2),
+        "prefill_us": round(us_sq, 2), "prefill_plain_us": round(us_pl, 2),
+        "prefill_tokens_per_s": round(B * T / (us_sq * 1e-6), 1),
+        "prefill_plain_tokens_per_s": round(B * T / (us_pl * 1e-6), 1),
+        "codes_us": round(codes_us, 2),
+        "codes_gbs": round(nbytes / (codes_us * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "alu", "kernel": "squat_codes_kernel (fp32 FMAs of the element-by-element walk)",
+                     "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                     "how": "prefill with the coder minus the same prefill without it, HIP events"},
+    }
+
+
 def _profile_prefill(workload, n):
     """n prefills of the workload's first layer into one cache, each timed with
     its own pair of HIP events (for a profile of the quantizer alone)."""
@@ -306,7 +391,10 @@ def _profile_prefill(workload, n):
     dev = torch.device("cuda:0")
     wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], device=dev)
     k, v = wl.kv(0, T)
-    c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=dev)
+    c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=dev, squat_rank=cfg.get("squat_rank", 0))
+    if cfg.get("squat_rank"):
+        from kivi_inputs import query_history
+        c.squat_build(query_history(wl, Hq, cfg["squat_queries"], rank=cfg["squat_rank"]), cfg["squat_lambda"])
     stream = torch.cuda.current_stream()
     ts = []
     for _ in range(n):
@@ -336,7 +424,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="full_stack",
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
-                             "gqa_ragged", "gqa_paged"])
+                             "gqa_ragged", "gqa_paged", "llama2_7b_layer_squat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="N",
@@ -363,7 +451,7 @@ def main():
     import torch
 
     import kv_cache_compression_kivi_amd as kv
-    from kivi_inputs import CONFIGS, KVWorkload, page_order, row_lengths
+    from kivi_inputs import CONFIGS, KVWorkload, page_order, query_history, row_lengths
 
     lib = kv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -402,7 +490,12 @@ def main():
                 c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev, n_pages=B * mb)
                 c.set_block_table(page_order(B * mb, cfg["seed"] + 1000 * len(caches)).reshape(B, mb).to(dev))
             else:
-                c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev)
+                c = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=dev,
+                                 squat_rank=cfg.get("squat_rank", 0))
+            if cfg.get("squat_rank"):
+                # the SQuat-style coder's coefficients from the layer's past queries, before the prefill
+                c.squat_build(query_history(wl, Hq, cfg["squat_queries"], rank=cfg["squat_rank"]),
+                              cfg["squat_lambda"])
             if cfg.get("ragged"):
                 c.append_rows(k, v, lens)
             else:
@@ -552,6 +645,7 @@ def main():
         fl_gbs = (sum(flush_bytes(units, d, caches[i].cfg.bits, 32) for i in pf_idx) / len(pf_idx) /
                   (fl_us * 1e-6) / 1e9)
 
+    squat_line = _squat_measure(kv, cfg, dev, caches, prefill_inputs) if cfg.get("squat_rank") else None
     probe = _stream_probe(dev)
     traffic = _traffic_from_profile(args.workload)
     if by_bits:
@@ -606,6 +700,7 @@ def main():
             "by_bits": by_bits or None,
         },
         "stream_probe": probe,
+        "squat": squat_line,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

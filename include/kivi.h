@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KIVI_ABI_VERSION 4
+#define KIVI_ABI_VERSION 5
 
 typedef enum {
     KIVI_OK = 0,
@@ -127,9 +127,12 @@ typedef struct {
     int32_t max_splits;
     int32_t n_pages;    /* pages in the pool (0: not paged) */
     size_t page_bytes;  /* Hkv * block_bytes (paged) */
-    size_t off_squat;   /* squat_rank > 0: unit u's head_dim x head_dim fp32 update coefficients at
-                           off_squat + u * head_dim^2 * 4 (row c, column j: the move of key element
-                           j per unit error of element c; 0 for j <= c) */
+    size_t off_squat;   /* squat_rank > 0: unit u's coder coefficients at off_squat + u * squat_unit_bytes:
+                           U [head_dim][squat_r8] then W [head_dim][squat_r8] fp32 (row c: u_c, w_c;
+                           columns past squat_rank are 0). Key element j moves by -delta * (u_j . w_c)
+                           per error delta of an earlier element c. */
+    int32_t squat_r8;   /* squat_rank rounded up to a multiple of 8 (0 without the coder) */
+    size_t squat_unit_bytes;
 } kivi_layout;
 
 /* Counters of a cache. Tokens [0, n_quant) are quantized, [n_quant, n_tokens)

@@ -145,6 +145,10 @@ CONFIGS = {
                           decode_steps=256),
     "full_stack": dict(batch=128, n_kv_heads=8, n_q_heads=32, head_dim=128, T=4096, seed=5,
                        layers=32, layer_bits=[2] * 16 + [4] * 16, q_dtype="bf16"),
+    # The Llama-2-7B-shaped layer with the SQuat-style key coder: a rank-8 query
+    # subspace from 512 past queries per head, lambda 0.1.
+    "llama2_7b_layer_squat": dict(batch=8, n_kv_heads=32, n_q_heads=32, head_dim=128, T=4096, bits=2, seed=2,
+                                  squat_rank=8, squat_lambda=0.1, squat_queries=512),
     # A serving batch: the GQA shape above with each sequence at its own length,
     # uniform over [512, 8192] tokens (T is the longest possible).
     "gqa_ragged": dict(batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=6,

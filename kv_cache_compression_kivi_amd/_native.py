@@ -7,6 +7,8 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkivi.so")
+# KIVI_ABI_VERSION of include/kivi.h that the structures below mirror
+ABI_VERSION = 5
 
 KIVI_F16 = 0
 KIVI_BF16 = 1
@@ -42,7 +44,7 @@ class kivi_layout(ctypes.Structure):
         ("off_partial", ctypes.c_size_t), ("partial_stride", ctypes.c_size_t),
         ("max_splits", ctypes.c_int32),
         ("n_pages", ctypes.c_int32), ("page_bytes", ctypes.c_size_t),
-        ("off_squat", ctypes.c_size_t),
+        ("off_squat", ctypes.c_size_t), ("squat_r8", ctypes.c_int32), ("squat_unit_bytes", ctypes.c_size_t),
     ]
 
 
@@ -97,6 +99,9 @@ def load_library():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.kivi_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.kivi_abi_version()}, the binding expects "
+                               f"{ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -368,12 +373,14 @@ class KiviCache:
         kivi_squat_build(self.handle, q_hist.data_ptr(), KIVI_BF16 if q_hist.dtype == torch.bfloat16 else KIVI_F16,
                          q_hist.shape[2], float(lam), self._stream(stream))
 
-    def squat_coefficients(self, unit):
-        """Unit's update coefficients [head_dim, head_dim] as the device holds them (fp32)."""
+    def squat_factors(self, unit):
+        """Unit's coder coefficients as the device holds them: (U, W), each
+        [head_dim, squat_r8] fp32 (row c: u_c, w_c)."""
         import torch
-        d = self.cfg.head_dim
-        start = self.layout.off_squat + unit * d * d * 4
-        return self.memory[start:start + d * d * 4].view(torch.float32).reshape(d, d)
+        d, r8 = self.cfg.head_dim, self.layout.squat_r8
+        start = self.layout.off_squat + unit * self.layout.squat_unit_bytes
+        f = self.memory[start:start + self.layout.squat_unit_bytes].view(torch.float32).reshape(2, d, r8)
+        return f[0], f[1]
 
     def reset(self):
         kivi_cache_reset(self.handle)

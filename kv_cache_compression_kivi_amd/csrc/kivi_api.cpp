@@ -76,6 +76,7 @@ kivi::CacheGeom geom(const kivi_cache* c) {
     g.table_stride = c->table_stride;
     g.n_pages = c->cfg.n_pages;
     g.off_squat = c->L.off_squat;
+    g.squat_r8 = c->L.squat_r8;
     return g;
 }
 

@@ -30,9 +30,10 @@ struct CacheGeom {
     const int32_t* table;
     int64_t table_stride;
     int32_t n_pages;
-    // SQuat-style key coder: per unit a head_dim x head_dim fp32 matrix (the
-    // update coefficients) at off_squat + u * head_dim^2 * 4
+    // SQuat-style key coder: per unit U [head_dim][squat_r8] then W
+    // [head_dim][squat_r8] fp32 at off_squat + u * 2 * head_dim * squat_r8 * 4
     size_t off_squat;
+    int32_t squat_r8;
 };
 
 // Paged blocks: the table entry of batch row b's key block j, read through
@@ -189,9 +190,9 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_ring_write(const RingArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-// SQuat-style key coder (head_dim 64 or 128): the coefficients, and the key
-// codes of the blocks a QuantArgs launch just quantized (after it, before the
-// ring write of the same call).
+// SQuat-style key coder (head_dim 64 or 128): the coefficients (one work-group
+// per unit), and the key codes of the blocks a QuantArgs launch just quantized
+// (after it, before the ring write of the same call).
 hipError_t launch_squat_build(const SquatBuildArgs& a, hipStream_t s);
 hipError_t launch_squat_codes(const QuantArgs& a, hipStream_t s);
 

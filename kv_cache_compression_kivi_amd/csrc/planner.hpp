@@ -121,7 +121,9 @@ inline void compute_layout(const kivi_config* c, kivi_layout* L) {
     L->partial_stride = (d + 4) * 4;
     L->off_squat = align_up(L->off_partial + (size_t)c->batch * c->n_q_heads * (size_t)L->max_splits *
                                                  L->partial_stride);
-    L->total_bytes = L->off_squat + (c->squat_rank > 0 ? align_up((size_t)units * d * d * 4) : 0);
+    L->squat_r8 = (c->squat_rank + 7) / 8 * 8;
+    L->squat_unit_bytes = (size_t)2 * d * (size_t)L->squat_r8 * 4;
+    L->total_bytes = L->off_squat + align_up((size_t)units * L->squat_unit_bytes);
 }
 
 // What one kivi_append(ntok) does, as closed forms of the token-by-token rule.

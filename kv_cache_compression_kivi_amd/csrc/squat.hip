@@ -11,16 +11,23 @@
 //
 // Reading taken (the page gives the steps in prose only):
 //   - subspace: the r eigenvectors of C = sum_q q q^T (the queries of the
-//     query heads that read the KV head) with the largest eigenvalues;
-//   - objective of a key's error e: ||U^T e||^2 + lambda ||e||^2 (U the
-//     subspace basis). After fixing element c with error delta, the optimal
-//     move of element j > c is -delta * g[c][j], g[c][j] = T[c][j] / T[c][c],
-//     T the upper Cholesky factor of (U U^T + lambda I)^-1
-//     = (1/lambda) I - (1/lambda - 1/(1 + lambda)) U U^T;
+//     query heads that read the KV head) with the largest eigenvalues, basis
+//     U (rows u_c, one r-vector per channel);
+//   - objective of a key's error e: ||U^T e||^2 + lambda ||e||^2. After fixing
+//     element c with error delta, the optimal move of every later element j
+//     (the optimal-brain-surgeon step on H = U U^T + lambda I restricted to
+//     the elements still free) is -delta * g[c][j];
 //   - the codes: channel order, each element with its block's KIVI (s_c, z_c)
 //     (KIVI page, section 量子化アルゴリズム): code = clamp(rint((x - z) / s),
-//     0, 2^b - 1) in IEEE fp32, delta = x - fma(s, code, z), and
-//     x_j = fma(-delta, g[c][j], x_j).
+//     0, 2^b - 1) in IEEE fp32, delta = x - fma(s, code, z).
+//
+// Computed here in the subspace's own coordinates. With M_c = lambda I +
+// sum_{i > c} u_i u_i^T (r x r), the Woodbury identity gives g[c][j] =
+// u_j . w_c with w_c = -M_c^-1 u_c, so the correction element c receives from
+// all earlier ones is u_c . a, a = sum_{c' < c} delta_c' w_c' (an r-vector per
+// key): per element 2 r fused multiply-adds instead of one per later element.
+// The w_c come from c = d - 1 down to 0, M_c^-1 kept by Sherman-Morrison
+// (M_{c-1}^-1 from M_c^-1 and u_c), in fp64.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -33,70 +40,11 @@ namespace {
 
 constexpr int kG = 32;  // tokens per key block
 
-// Unit u's d x d fp32 matrix in the coder's region (the Gram matrix until the
-// factor kernel replaces it with the update coefficients g).
-__device__ __forceinline__ float* squat_matrix(const CacheGeom& g, int64_t u) {
-    return reinterpret_cast<float*>(g.base + g.off_squat) + (size_t)u * g.head_dim * g.head_dim;
+// Unit u's coefficients in the coder's region: U [d][r8] then W [d][r8] fp32,
+// r8 = the rank rounded up to a multiple of 8 (padding columns are 0).
+__device__ __forceinline__ float* squat_coef(const CacheGeom& g, int64_t u) {
+    return reinterpret_cast<float*>(g.base + g.off_squat) + (size_t)u * 2 * g.head_dim * g.squat_r8;
 }
-
-// ------------------------------------------------------------------ Gram matrix
-
-// One work-group of 256 threads per unit: C = sum over the unit's query heads
-// and their n_q past queries of q q^T, in fp32. Thread (a, b) of a 16 x 16
-// grid accumulates the (D/16) x (D/16) tile of rows a*D/16.., columns b*D/16...
-template <int D>
-__global__ __launch_bounds__(256) void squat_gram_kernel(const SquatBuildArgs a) {
-    constexpr int TS = D / 16;   // tile side
-    constexpr int CH = 32;       // queries staged at a time
-    __shared__ __align__(16) float sq[CH][D];
-    const CacheGeom& g = a.g;
-    const int tid = threadIdx.x;
-    const int64_t u = blockIdx.x;
-    const int64_t b = u / g.n_kv_heads, h = u % g.n_kv_heads;
-    const int group = g.n_q_heads / g.n_kv_heads;
-    const int r0 = (tid / 16) * TS, c0 = (tid % 16) * TS;
-    float acc[TS][TS];
-#pragma unroll
-    for (int i = 0; i < TS; ++i)
-#pragma unroll
-        for (int k = 0; k < TS; ++k) acc[i][k] = 0.0f;
-    const int64_t nvec = (int64_t)group * a.n_q;
-    for (int64_t v0 = 0; v0 < nvec; v0 += CH) {
-        __syncthreads();
-        for (int idx = tid; idx < CH * D; idx += 256) {
-            const int vv = idx / D, c = idx % D;
-            const int64_t v = v0 + vv;
-            float x = 0.0f;
-            if (v < nvec) {
-                const int64_t head = h * group + v / a.n_q, t = v % a.n_q;
-                const uint16_t bits = a.q[((b * g.n_q_heads + head) * a.n_q + t) * D + c];
-                x = a.q_bf16 ? __uint_as_float((uint32_t)bits << 16) : __half2float(__ushort_as_half(bits));
-            }
-            sq[vv][c] = x;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int vv = 0; vv < CH; ++vv) {
-            float ra[TS], rb[TS];
-#pragma unroll
-            for (int i = 0; i < TS; ++i) {
-                ra[i] = sq[vv][r0 + i];
-                rb[i] = sq[vv][c0 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < TS; ++i)
-#pragma unroll
-                for (int k = 0; k < TS; ++k) acc[i][k] = fmaf(ra[i], rb[k], acc[i][k]);
-        }
-    }
-    float* C = squat_matrix(g, u);
-#pragma unroll
-    for (int i = 0; i < TS; ++i)
-#pragma unroll
-        for (int k = 0; k < TS; ++k) C[(r0 + i) * D + c0 + k] = acc[i][k];
-}
-
-// ------------------------------------------------------------------ coefficients
 
 // A fixed pseudo-random start for the subspace iteration (splitmix of the index).
 __device__ __forceinline__ double start_value(uint32_t i) {
@@ -107,45 +55,93 @@ __device__ __forceinline__ double start_value(uint32_t i) {
     return (double)(x >> 11) * 0x1p-53 * 2.0 - 1.0;
 }
 
-// One work-group of 256 threads per unit:
-//   1. the top-r subspace of C by subspace iteration in fp64: W = C V, then V
-//      = W R^-1 with R the Cholesky factor of W^T W (twice per step), from a
-//      fixed pseudo-random start, kSquatIters steps;
-//   2. Hinv = (1/lambda) I - (1/lambda - 1/(1 + lambda)) V V^T, its upper
-//      Cholesky factor T in place (fp32), and g[c][j] = T[c][j] / T[c][c]
-//      for j > c (0 elsewhere), written over C.
 constexpr int kSquatIters = 48;
 
+// One work-group of 256 threads per unit:
+//   1. C = sum over the unit's query heads and their n_q past queries of
+//      q q^T in fp32 (thread (a, b) of a 16 x 16 grid owns a (D/16)^2 tile);
+//   2. the top-r subspace of C by subspace iteration in fp64: W = C V, then V =
+//      W R^-1 with R the Cholesky factor of W^T W, from a fixed pseudo-random
+//      start, kSquatIters steps, and one more orthonormalisation;
+//   3. w_c = -M_c^-1 u_c for c = d - 1 .. 0 with M_c^-1 by Sherman-Morrison;
+//   4. U and W (fp32, zero-padded to r8 columns) to the unit's coefficients.
 template <int D>
-__global__ __launch_bounds__(256) void squat_factor_kernel(const SquatBuildArgs a) {
+__global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a) {
     constexpr int RM = kSquatMaxRank;
-    __shared__ __align__(16) float sa[D][D];     // C, then Hinv and its factor
-    __shared__ __align__(16) double sv[D][RM];   // V
-    __shared__ __align__(16) double sw[D][RM];   // W
-    __shared__ double sm[RM][RM];                // W^T W and its factor
+    constexpr int TS = D / 16;  // Gram tile side
+    constexpr int CH = 32;      // queries staged at a time
+    __shared__ __align__(16) float sa[D][D];     // C
+    __shared__ __align__(16) double sv[D][RM];   // V (the queries' staging buffer before)
+    __shared__ __align__(16) double sw[D][RM];   // W, then the w_c
+    __shared__ double sm[RM][RM];                // W^T W and its factor, then M^-1
+    __shared__ double sz[RM];
+    static_assert(CH * D * sizeof(float) <= sizeof(sv), "the staged queries fit V's space");
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
     const int64_t u = blockIdx.x;
     const int r = a.rank;
-    float* C = squat_matrix(g, u);
-    for (int idx = tid; idx < D * D; idx += 256) sa[idx / D][idx % D] = C[idx];
+    const int64_t b = u / g.n_kv_heads, h = u % g.n_kv_heads;
+    const int group = g.n_q_heads / g.n_kv_heads;
+
+    // 1. Gram matrix
+    {
+        float(*sq)[D] = reinterpret_cast<float(*)[D]>(&sv[0][0]);
+        const int r0 = (tid / 16) * TS, c0 = (tid % 16) * TS;
+        float acc[TS][TS];
+#pragma unroll
+        for (int i = 0; i < TS; ++i)
+#pragma unroll
+            for (int k = 0; k < TS; ++k) acc[i][k] = 0.0f;
+        const int64_t nvec = (int64_t)group * a.n_q;
+        for (int64_t v0 = 0; v0 < nvec; v0 += CH) {
+            __syncthreads();
+            for (int idx = tid; idx < CH * D; idx += 256) {
+                const int vv = idx / D, c = idx % D;
+                const int64_t v = v0 + vv;
+                float x = 0.0f;
+                if (v < nvec) {
+                    const int64_t head = h * group + v / a.n_q, t = v % a.n_q;
+                    const uint16_t bits = a.q[((b * g.n_q_heads + head) * a.n_q + t) * D + c];
+                    x = a.q_bf16 ? __uint_as_float((uint32_t)bits << 16) : __half2float(__ushort_as_half(bits));
+                }
+                sq[vv][c] = x;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int vv = 0; vv < CH; ++vv) {
+                float ra[TS], rb[TS];
+#pragma unroll
+                for (int i = 0; i < TS; ++i) {
+                    ra[i] = sq[vv][r0 + i];
+                    rb[i] = sq[vv][c0 + i];
+                }
+#pragma unroll
+                for (int i = 0; i < TS; ++i)
+#pragma unroll
+                    for (int k = 0; k < TS; ++k) acc[i][k] = fmaf(ra[i], rb[k], acc[i][k]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TS; ++i)
+#pragma unroll
+            for (int k = 0; k < TS; ++k) sa[r0 + i][c0 + k] = acc[i][k];
+        __syncthreads();
+    }
     for (int idx = tid; idx < D * r; idx += 256) sv[idx / r][idx % r] = start_value((uint32_t)idx);
-    __syncthreads();
     // C + eps I has C's eigenvectors; the shift (1e-7 of the mean eigenvalue)
     // keeps W = C V of full rank when the queries span fewer than r directions
     if (tid == 0) {
         double tr = 0.0;
         for (int c = 0; c < D; ++c) tr += sa[c][c];
-        sm[0][0] = tr;
+        sz[0] = tr;
     }
     __syncthreads();
-    const float eps = (float)(1e-7 * sm[0][0] / D) + 1e-30f;
+    const float eps = (float)(1e-7 * sz[0] / D) + 1e-30f;
     __syncthreads();
     for (int c = tid; c < D; c += 256) sa[c][c] += eps;
     __syncthreads();
 
-    // V <- orthonormal basis of the columns of W (Cholesky-QR): M = W^T W,
-    // R = chol(M) (upper), V = W R^-1
+    // 2. V <- orthonormal basis of the columns of src (Cholesky-QR)
     auto orthonormalize = [&](double (*src)[RM]) {
         for (int idx = tid; idx < r * r; idx += 256) {
             const int i = idx / r, k = idx % r;
@@ -154,8 +150,7 @@ __global__ __launch_bounds__(256) void squat_factor_kernel(const SquatBuildArgs 
             sm[i][k] = s;
         }
         __syncthreads();
-        // r x r Cholesky, upper, in place (right-looking)
-        for (int k = 0; k < r; ++k) {
+        for (int k = 0; k < r; ++k) {  // r x r Cholesky, upper, in place (right-looking)
             if (tid == 0) sm[k][k] = sqrt(sm[k][k] > 0.0 ? sm[k][k] : 1e-300);
             __syncthreads();
             for (int j = k + 1 + tid; j < r; j += 256) sm[k][j] /= sm[k][k];
@@ -167,8 +162,7 @@ __global__ __launch_bounds__(256) void squat_factor_kernel(const SquatBuildArgs 
             }
             __syncthreads();
         }
-        // each row of V solves x R = w (forward over the columns)
-        for (int c = tid; c < D; c += 256) {
+        for (int c = tid; c < D; c += 256) {  // each row of V solves x R = w
             for (int k = 0; k < r; ++k) {
                 double s = src[c][k];
                 for (int i = 0; i < k; ++i) s -= sv[c][i] * sm[i][k];
@@ -178,200 +172,271 @@ __global__ __launch_bounds__(256) void squat_factor_kernel(const SquatBuildArgs 
         __syncthreads();
     };
     orthonormalize(sv);
-    for (int it = 0; it < kSquatIters; ++it) {
-        for (int idx = tid; idx < D * r; idx += 256) {
-            const int c = idx / r, k = idx % r;
-            double s = 0.0;
-            for (int e = 0; e < D; ++e) s += (double)sa[c][e] * sv[e][k];
-            sw[c][k] = s;
+    for (int it = 0; it <= kSquatIters; ++it) {
+        if (it < kSquatIters) {
+            for (int idx = tid; idx < D * r; idx += 256) {
+                const int c = idx / r, k = idx % r;
+                double s = 0.0;
+                for (int e = 0; e < D; ++e) s += (double)sa[c][e] * sv[e][k];
+                sw[c][k] = s;
+            }
+        } else {  // a second pass restores orthogonality to fp64 rounding
+            for (int idx = tid; idx < D * r; idx += 256) sw[idx / r][idx % r] = sv[idx / r][idx % r];
         }
         __syncthreads();
         orthonormalize(sw);
-        if (it + 1 == kSquatIters) {  // a second pass restores orthogonality to fp64 rounding
-            for (int idx = tid; idx < D * r; idx += 256) sw[idx / r][idx % r] = sv[idx / r][idx % r];
-            __syncthreads();
-            orthonormalize(sw);
-        }
     }
 
-    // Hinv = (1/lambda) I - kappa V V^T
-    const double lam = (double)a.lambda;
-    const double kappa = 1.0 / lam - 1.0 / (1.0 + lam);
-    for (int idx = tid; idx < D * D; idx += 256) {
-        const int i = idx / D, j = idx % D;
-        double p = 0.0;
-        for (int k = 0; k < r; ++k) p += sv[i][k] * sv[j][k];
-        sa[i][j] = (float)((i == j ? 1.0 / lam : 0.0) - kappa * p);
-    }
+    // 3. w_c = -M_c^-1 u_c, M_c = lambda I + sum_{i > c} u_i u_i^T, from c = D - 1 down
+    for (int idx = tid; idx < r * r; idx += 256) sm[idx / r][idx % r] = idx / r == idx % r ? 1.0 / (double)a.lambda : 0.0;
     __syncthreads();
-    // upper Cholesky factor in place (right-looking): after step k, row k holds T[k][k..]
-    for (int k = 0; k < D; ++k) {
-        if (tid == 0) sa[k][k] = sqrtf(sa[k][k]);
-        __syncthreads();
-        for (int j = k + 1 + tid; j < D; j += 256) sa[k][j] /= sa[k][k];
-        __syncthreads();
-        const int m = D - 1 - k;  // trailing (i, j), k < i <= j
-        for (int idx = tid; idx < m * m; idx += 256) {
-            const int i = k + 1 + idx / m, j = k + 1 + idx % m;
-            if (j >= i) sa[i][j] = fmaf(-sa[k][i], sa[k][j], sa[i][j]);
+    for (int c = D - 1; c >= 0; --c) {
+        if (tid < r) {  // z = M_c^-1 u_c
+            double s = 0.0;
+            for (int k = 0; k < r; ++k) s += sm[tid][k] * sv[c][k];
+            sz[tid] = s;
         }
         __syncthreads();
+        if (tid < r) sw[c][tid] = -sz[tid];
+        double den = 1.0;
+        for (int k = 0; k < r; ++k) den += sv[c][k] * sz[k];
+        // M_{c-1}^-1 = M_c^-1 - z z^T / (1 + u_c . z)
+        for (int idx = tid; idx < r * r; idx += 256) sm[idx / r][idx % r] -= sz[idx / r] * sz[idx % r] / den;
+        __syncthreads();
     }
-    for (int idx = tid; idx < D * D; idx += 256) {
-        const int c = idx / D, j = idx % D;
-        C[idx] = j > c ? sa[c][j] / sa[c][c] : 0.0f;
+
+    // 4. U and W, zero-padded to r8 columns
+    const int r8 = g.squat_r8;
+    float* out = squat_coef(g, u);
+    for (int idx = tid; idx < D * r8; idx += 256) {
+        const int c = idx / r8, k = idx % r8;
+        out[idx] = k < r ? (float)sv[c][k] : 0.0f;
+        out[D * r8 + idx] = k < r ? (float)sw[c][k] : 0.0f;
     }
 }
 
 // ------------------------------------------------------------------ codes
 
-// One wave per two key blocks of a unit (lane l: token l % 32 of block
-// 2 * blockIdx.x + l / 32, with a row table counted from the unit's row's j0).
-// The blocks' records already hold the KIVI statistics (written by the
-// quantize launch just before, on the same stream); this kernel rewrites their
-// key codes. Each lane walks its key in channel order, 16 channels at a time:
-// the 16 in registers take the updates among themselves, then every later
-// channel (kept in LDS) takes the 16 errors, in the order of the channels that
-// made them, so each element receives its updates in channel order.
-template <int D, int BITS>
-__global__ __launch_bounds__(64) void squat_codes_kernel(const QuantArgs a) {
-    constexpr int NB = D / 16;        // channel blocks of 16
+// One work-group of four waves per 8 TPL key blocks of a unit quantized by the
+// launch, TPL tokens per lane: wave w takes blocks 8 TPL blockIdx.x + 2 TPL w
+// .. + 2 TPL - 1 (with a row table counted from the unit's row's j0), lane l
+// tokens l % L + L p (p < TPL, L = 32 / TPL) of the wave's block l / L. The
+// blocks' records already hold the KIVI statistics (written by the quantize
+// launch just before, on the same stream); this kernel rewrites their key
+// codes. U, W and the blocks' (s, z, rcp s) are staged in LDS once and read as
+// broadcasts; each lane walks its fp16 key rows in channel order, 16 channels
+// a step with the next step's bytes in flight, keeping -a = -sum_{c' < c}
+// delta_c' w_c' (R8 floats) per token.
+//
+// The broadcasts cost LDS bandwidth per lane, whatever the address: with one
+// token per lane they bound the walk (measured). Two tokens per lane halve
+// the LDS bytes per element, since each broadcast of u_c, w_c and the
+// statistics serves both; a launch of at most two blocks per unit (a flush
+// during decode) keeps one token per lane, as there the walk's latency sets
+// the time.
+//
+// The codes are those of the IEEE steps, computed faster, as in the plain
+// quantizer: p = (x - z) rcp(s), clamped to [0, 2^b - 1], is within
+// (2^b - 1/2) 2^-22 of the IEEE quotient there (rcp within 1 ulp), so rint(p)
+// is the IEEE code unless p lies within a margin four times that of a
+// half-integer; then the wave takes the IEEE division for that channel.
+// -delta is fma(s, code, -(x - z)), one rounding of the same difference.
+template <int TPL>
+constexpr int squat_blocks_per_wave() { return 64 * TPL / kG; }
+template <int TPL>
+constexpr int squat_blocks_per_wg() { return 4 * squat_blocks_per_wave<TPL>(); }
+
+// u * a + k with k the fp16 half HI of `pair`, widened exactly inside one
+// fused multiply-add (v_fma_mix_f32): fma(u, a, (float)k), one rounding.
+template <int HI>
+__device__ __forceinline__ float half_fma(float u, float a, uint32_t pair) {
+    float r;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(r) : "v"(u), "v"(a), "v"(pair));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,0,1]" : "=v"(r) : "v"(u), "v"(a), "v"(pair));
+    return r;
+}
+
+template <int D, int BITS, int R8, int TPL>
+__global__ __launch_bounds__(256) void squat_codes_kernel(const QuantArgs a) {
+    constexpr int LPB = kG / TPL;  // lanes per block
+    constexpr int BPW = squat_blocks_per_wave<TPL>();
+    constexpr int BPG = squat_blocks_per_wg<TPL>();
     constexpr int W = D * BITS / 32;  // key words per token
-    constexpr int PER = 32 / BITS;
+    constexpr int H = 16 / BITS;      // codes per 16-bit accumulator
     constexpr float kQmax = float((1 << BITS) - 1);
-    __shared__ __align__(16) float sx[D / 4][64][4];  // lane's x[4 m .. 4 m + 3] at sx[m][lane]
-    __shared__ __align__(16) float2 ssz[2][D];        // (s, z) per channel of the two blocks
+    constexpr float kMargin = 0.5f - float(1 << BITS) * 0x1p-20f;
+    // a block's statistics row, padded where LDS allows: the four blocks a
+    // wave reads at once then start 4 banks apart
+    constexpr int SQ = 2 * D * R8 * 4 + BPG * (D + 1) * 16 <= 65536 ? D + 1 : D;
+    __shared__ __align__(16) float suw[2][D][R8];                // u_c, then w_c
+    __shared__ __align__(16) float4 ssz[BPG][SQ];  // (s, z, rcp s) per channel and block
+    static_assert(sizeof(suw) + sizeof(ssz) <= 65536, "one work-group's LDS");
 
     const CacheGeom& g = a.g;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64;
     const int64_t u = blockIdx.y;
     const int brow = (int)((uint32_t)blockIdx.y / (uint32_t)g.n_kv_heads);
     const int64_t jrow0 = a.rows.n ? a.rows.j0[brow] : a.j0;
     const int64_t jrow1 = a.rows.n ? a.rows.j1[brow] : a.j1;
     const int64_t ring_end = a.rows.n ? a.rows.ring_end[brow] : a.ring_end;
-    const int half = lane / 32, t = lane % 32;
-    const int64_t jb0 = jrow0 + 2 * (int64_t)blockIdx.x;
-    if (jb0 >= jrow1) return;  // the whole wave
-    const int64_t jb = jb0 + half;
+    const int64_t jw0 = jrow0 + (int64_t)BPG * blockIdx.x;
+    if (jw0 >= jrow1) return;  // the whole work-group
+    const int bw = lane / LPB, t0 = lane % LPB;
+    const int64_t jb = jw0 + BPW * wave + bw;
     const bool valid = jb < jrow1;
+    const int64_t jl = valid ? jb : jw0;  // a block that exists, for the loads of a lane past the end
 
-    // statistics of both blocks (the second may not exist: then the first's again)
-    for (int idx = lane; idx < 2 * D; idx += 64) {
-        const int hb = idx / D, c = idx % D;
-        const int64_t j = jb0 + hb < jrow1 ? jb0 + hb : jb0;
-        const uint8_t* rec = g.base + record_offset(g, u, j);
-        ssz[hb][c] = reinterpret_cast<const float2*>(rec + g.rec_ksz)[c];
-    }
-    // this lane's key row, fp16 -> fp32, into its LDS column
-    {
-        const int64_t tok = (valid ? jb : jb0) * kG + t;
-        const uint16_t* row;
+    // this lane's key rows (fp16): 32 bytes (16 channels) of each per step, the next step's in flight
+    const uint4* row[TPL];
+    uint4 nx[TPL][2];
+#pragma unroll
+    for (int p = 0; p < TPL; ++p) {
+        const int64_t tok = jl * kG + t0 + LPB * p;
         if (tok < ring_end)
-            row = reinterpret_cast<const uint16_t*>(g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
+            row[p] = reinterpret_cast<const uint4*>(g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
                                                     (size_t)((uint32_t)tok % (uint32_t)g.ring_slots) * 4 * D);
         else
-            row = a.k + (u * a.ntok + (tok - ring_end)) * D;
-#pragma unroll
-        for (int m = 0; m < D / 8; ++m) {
-            const uint4 x = reinterpret_cast<const uint4*>(row)[m];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[2 * e] = __half2float(__ushort_as_half((uint16_t)(w[e] & 0xffffu)));
-                f[2 * e + 1] = __half2float(__ushort_as_half((uint16_t)(w[e] >> 16)));
-            }
-            *reinterpret_cast<float4*>(sx[2 * m][lane]) = make_float4(f[0], f[1], f[2], f[3]);
-            *reinterpret_cast<float4*>(sx[2 * m + 1][lane]) = make_float4(f[4], f[5], f[6], f[7]);
-        }
+            row[p] = reinterpret_cast<const uint4*>(a.k + (u * a.ntok + (tok - ring_end)) * D);
+        nx[p][0] = row[p][0];
+        nx[p][1] = row[p][1];
+    }
+    // the unit's U and W, and the statistics of the work-group's blocks (a
+    // block past the end: the first block's again)
+    const float* coef = squat_coef(g, u);
+    for (int idx = tid; idx < 2 * D * R8 / 4; idx += 256)
+        reinterpret_cast<float4*>(&suw[0][0][0])[idx] = reinterpret_cast<const float4*>(coef)[idx];
+    for (int idx = tid; idx < BPG * D; idx += 256) {
+        const int hb = idx / D, c = idx % D;
+        const int64_t j = jw0 + hb < jrow1 ? jw0 + hb : jw0;
+        const float2 sz = reinterpret_cast<const float2*>(g.base + record_offset(g, u, j) + g.rec_ksz)[c];
+        ssz[hb][c] = make_float4(sz.x, sz.y, __builtin_amdgcn_rcpf(sz.x), 0.0f);
     }
     __syncthreads();
 
-    typedef const __attribute__((address_space(4))) float* const_f32;
-    const const_f32 G = (const_f32)squat_matrix(g, u);  // wave-uniform: scalar loads
-    uint32_t words[W];
+    const float4* sz_mine = ssz[BPW * wave + bw];
+    float acc[TPL][R8];  // -a of each token
 #pragma unroll
-    for (int w = 0; w < W; ++w) words[w] = 0;
-    for (int kb = 0; kb < NB; ++kb) {
-        float xr[16], dl[16];
+    for (int p = 0; p < TPL; ++p)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float4 v = *reinterpret_cast<const float4*>(sx[4 * kb + m][lane]);
-            xr[4 * m] = v.x;
-            xr[4 * m + 1] = v.y;
-            xr[4 * m + 2] = v.z;
-            xr[4 * m + 3] = v.w;
+        for (int k = 0; k < R8; ++k) acc[p][k] = 0.0f;
+    uint32_t words[TPL][W];
+#pragma unroll
+    for (int p = 0; p < TPL; ++p)
+#pragma unroll
+        for (int w = 0; w < W; ++w) words[p][w] = 0;
+#pragma unroll 1
+    for (int cb = 0; cb < D / 16; ++cb) {
+        uint32_t hw[TPL][8];
+#pragma unroll
+        for (int p = 0; p < TPL; ++p) {
+            const uint4 p0 = nx[p][0], p1 = nx[p][1];
+            hw[p][0] = p0.x, hw[p][1] = p0.y, hw[p][2] = p0.z, hw[p][3] = p0.w;
+            hw[p][4] = p1.x, hw[p][5] = p1.y, hw[p][6] = p1.z, hw[p][7] = p1.w;
+            if (cb + 1 < D / 16) {
+                nx[p][0] = row[p][2 * cb + 2];
+                nx[p][1] = row[p][2 * cb + 3];
+            }
         }
-        uint32_t wd[16 / PER > 0 ? 16 / PER : 1] = {};
+        float hf[TPL][BITS];  // the step's codes, 16 bits per accumulator
+#pragma unroll
+        for (int p = 0; p < TPL; ++p)
+#pragma unroll
+            for (int e = 0; e < BITS; ++e) hf[p][e] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int c = kb * 16 + i;
-            const float2 sz = ssz[half][c];
-            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf((xr[i] - sz.y) / sz.x), 0.0f, kQmax);
-            wd[i / PER] |= (uint32_t)r << (BITS * (i % PER));
-            dl[i] = xr[i] - __builtin_fmaf(sz.x, r, sz.y);
+            const int c = cb * 16 + i;
+            const float* uc = suw[0][c];
+            const float* wc = suw[1][c];
+            const float4 q = sz_mine[c];  // (s, z, rcp s, -)
+            float t[TPL], r[TPL];
+            bool tie = false;
 #pragma unroll
-            for (int i2 = i + 1; i2 < 16; ++i2) xr[i2] = __builtin_fmaf(-dl[i], G[c * D + kb * 16 + i2], xr[i2]);
-        }
-        // the block's 16 codes are whole words (16 / PER of them) at word kb * 16 / PER
+            for (int p = 0; p < TPL; ++p) {
+                // x = k_c + u_c . (-a), the fp16 k_c widened inside the first fma;
+                // two chains of R8 / 2 terms
+                float x0 = (i & 1) ? half_fma<1>(uc[0], acc[p][0], hw[p][i / 2])
+                                   : half_fma<0>(uc[0], acc[p][0], hw[p][i / 2]);
+                float x1 = uc[R8 / 2] * acc[p][R8 / 2];
 #pragma unroll
-        for (int e = 0; e < 16 / PER; ++e)
+                for (int k = 1; k < R8 / 2; ++k) {
+                    x0 = __builtin_fmaf(uc[k], acc[p][k], x0);
+                    x1 = __builtin_fmaf(uc[R8 / 2 + k], acc[p][R8 / 2 + k], x1);
+                }
+                t[p] = (x0 + x1) - q.y;
+                const float pc = __builtin_amdgcn_fmed3f(t[p] * q.z, 0.0f, kQmax);
+                r[p] = __builtin_rintf(pc);
+                tie = tie || fabsf(pc - r[p]) > kMargin;
+            }
+            if (__builtin_amdgcn_ballot_w64(tie)) {
 #pragma unroll
-            for (int w = 0; w < W; ++w)
-                if (w == kb * (16 / PER) + e) words[w] = wd[e];
-        for (int kb2 = kb + 1; kb2 < NB; ++kb2) {
-            float xl[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float4 v = *reinterpret_cast<const float4*>(sx[4 * kb2 + m][lane]);
-                xl[4 * m] = v.x;
-                xl[4 * m + 1] = v.y;
-                xl[4 * m + 2] = v.z;
-                xl[4 * m + 3] = v.w;
+                for (int p = 0; p < TPL; ++p) r[p] = __builtin_amdgcn_fmed3f(__builtin_rintf(t[p] / q.x), 0.0f, kQmax);
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
+            for (int p = 0; p < TPL; ++p) {
+                hf[p][i / H] = __builtin_fmaf(r[p], (float)(1 << (BITS * (i % H))), hf[p][i / H]);
+                // -delta = s code - (x - z), then -a += -delta w_c
+                const float ndl = __builtin_fmaf(q.x, r[p], -t[p]);
 #pragma unroll
-                for (int i2 = 0; i2 < 16; ++i2)
-                    xl[i2] = __builtin_fmaf(-dl[i], G[(kb * 16 + i) * D + kb2 * 16 + i2], xl[i2]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<float4*>(sx[4 * kb2 + m][lane]) =
-                    make_float4(xl[4 * m], xl[4 * m + 1], xl[4 * m + 2], xl[4 * m + 3]);
+                for (int k = 0; k < R8; ++k) acc[p][k] = __builtin_fmaf(ndl, wc[k], acc[p][k]);
+            }
         }
+        // the step's 16 codes are whole words (BITS / 2 of them) at word cb * BITS / 2
+#pragma unroll
+        for (int p = 0; p < TPL; ++p)
+#pragma unroll
+            for (int e = 0; e < BITS / 2; ++e)
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    if (w == cb * (BITS / 2) + e)
+                        words[p][w] = (uint32_t)hf[p][2 * e] | (uint32_t)hf[p][2 * e + 1] << 16;
     }
     if (valid) {
-        uint32_t* kw = reinterpret_cast<uint32_t*>(g.base + record_offset(g, u, jb) + g.rec_kcode) + t * W;
 #pragma unroll
-        for (int w = 0; w < W; w += 4)
-            *reinterpret_cast<uint4*>(kw + w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+        for (int p = 0; p < TPL; ++p) {
+            uint32_t* kw =
+                reinterpret_cast<uint32_t*>(g.base + record_offset(g, u, jb) + g.rec_kcode) + (t0 + LPB * p) * W;
+#pragma unroll
+            for (int w = 0; w < W; w += 4)
+                *reinterpret_cast<uint4*>(kw + w) = make_uint4(words[p][w], words[p][w + 1], words[p][w + 2], words[p][w + 3]);
+        }
     }
 }
 
-template <int D>
-hipError_t squat_build_d(const SquatBuildArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
-    squat_gram_kernel<D><<<grid, 256, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    squat_factor_kernel<D><<<grid, 256, 0, s>>>(a);
+template <int D, int BITS, int TPL>
+hipError_t squat_codes_dbt(const QuantArgs& a, hipStream_t s) {
+    constexpr int BPG = squat_blocks_per_wg<TPL>();
+    const dim3 grid((unsigned)((a.j1 - a.j0 + BPG - 1) / BPG), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
+    switch (a.g.squat_r8) {
+        case 8: squat_codes_kernel<D, BITS, 8, TPL><<<grid, 256, 0, s>>>(a); break;
+        case 16: squat_codes_kernel<D, BITS, 16, TPL><<<grid, 256, 0, s>>>(a); break;
+        case 24: squat_codes_kernel<D, BITS, 24, TPL><<<grid, 256, 0, s>>>(a); break;
+        default: squat_codes_kernel<D, BITS, 32, TPL><<<grid, 256, 0, s>>>(a); break;
+    }
     return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t squat_codes_db(const QuantArgs& a, hipStream_t s) {
+    return a.j1 - a.j0 <= 2 ? squat_codes_dbt<D, BITS, 1>(a, s) : squat_codes_dbt<D, BITS, 2>(a, s);
 }
 
 template <int D>
 hipError_t squat_codes_d(const QuantArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((a.j1 - a.j0 + 1) / 2), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
-    if (a.g.bits == 2)
-        squat_codes_kernel<D, 2><<<grid, 64, 0, s>>>(a);
-    else
-        squat_codes_kernel<D, 4><<<grid, 64, 0, s>>>(a);
-    return hipGetLastError();
+    return a.g.bits == 2 ? squat_codes_db<D, 2>(a, s) : squat_codes_db<D, 4>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_squat_build(const SquatBuildArgs& a, hipStream_t s) {
-    return a.g.head_dim == 64 ? squat_build_d<64>(a, s) : squat_build_d<128>(a, s);
+    const dim3 grid((unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
+    if (a.g.head_dim == 64)
+        squat_build_kernel<64><<<grid, 256, 0, s>>>(a);
+    else
+        squat_build_kernel<128><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_squat_codes(const QuantArgs& a, hipStream_t s) {

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(native):
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(native.EXPORTED)
-    assert native.kivi_abi_version() == 4
+    assert native.kivi_abi_version() == native.ABI_VERSION == 5
     nm = subprocess.run(["nm", "-D", "--defined-only", native.library_path()], capture_output=True, text=True).stdout
     for name in declared:
         assert re.search(r"\bT " + name + r"\b", nm), name
@@ -98,7 +98,8 @@ def test_layout_closed_form(native, bits, d):
         if d <= 128 else None
     if sq is not None:
         assert sq.off_squat % 256 == 0 and sq.off_squat >= L.total_bytes - 255
-        assert sq.total_bytes == sq.off_squat + -(-units * d * d * 4 // 256) * 256
+        assert sq.squat_r8 == 8 and sq.squat_unit_bytes == 2 * d * 8 * 4
+        assert sq.total_bytes == sq.off_squat + -(-units * sq.squat_unit_bytes // 256) * 256
 
 
 def test_squat_build_refusals(native):
