@@ -143,23 +143,29 @@ typedef struct {
 
 typedef struct kivi_cache kivi_cache;
 
-/* Bytes of device memory a cache with this config needs. */
+/* Bytes of device memory a cache with this config needs: the records of the
+ * page's codes, scales and zeros (section 量子化アルゴリズム), the fp16 residual
+ * ring (section 残差バッファ（Residual Buffer）) and the split partials. */
 int kivi_cache_bytes(const kivi_config* cfg, size_t* bytes);
 
-/* The layout above for this config. */
+/* The layout above for this config (the same regions as kivi_cache_bytes). */
 int kivi_cache_layout(const kivi_config* cfg, kivi_layout* layout);
 
 /* Make a handle over caller-owned device memory `dev_mem` of `bytes` bytes
- * (at least kivi_cache_bytes; 256-byte aligned). Launches nothing. The cache
+ * (at least kivi_cache_bytes; 256-byte aligned) for a config whose bits, group
+ * sizes and residual length are the page's QuantConfig fields (section
+ * アルゴリズム). Launches nothing. The cache
  * starts empty. dev_mem must outlive the handle. The split plans of
  * kivi_attend_decode fill the compute units of the device that is current
  * when the handle is made (256 when no device answers). */
 int kivi_cache_create(const kivi_config* cfg, void* dev_mem, size_t bytes, kivi_cache** out);
 
-/* Frees the host handle only (the device memory stays the caller's). */
+/* Frees the host handle only (the device memory stays the caller's).
+ * Bookkeeping: no step of the method. */
 int kivi_cache_destroy(kivi_cache* cache);
 
-/* Empty the cache (host counters only; launches nothing). */
+/* Empty the cache (host counters only; launches nothing): every sequence
+ * starts again with an empty residual (section 残差バッファ（Residual Buffer）). */
 int kivi_cache_reset(kivi_cache* cache);
 
 /* Append ntok >= 1 tokens to every sequence (page sections 残差バッファ（Residual
@@ -200,7 +206,8 @@ int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int3
 int kivi_set_block_table(kivi_cache* cache, const int32_t* table, int32_t stride);
 
 /* Empty sequence `row` (host counters only; launches nothing), so that a new
- * sequence can take the row. KIVI_E_UNSUPPORTED if the rows would then differ
+ * sequence can take the row, as a serving engine reuses a finished request's
+ * slot (the page's Production Deployment Guide, vLLM with KIVI). KIVI_E_UNSUPPORTED if the rows would then differ
  * in length with batch > KIVI_MAX_RAGGED_BATCH. */
 int kivi_reset_row(kivi_cache* cache, int32_t row);
 
@@ -277,31 +284,37 @@ int kivi_attend_decode_noalloc(kivi_cache* cache, const void* q, int32_t q_dtype
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
                      void* stream, int32_t* n_flushed);
 
-/* Current counters (KIVI_E_RAGGED when the rows differ: see kivi_query_row). */
+/* Current counters of the residual rule (section 残差バッファ（Residual
+ * Buffer）): quantized and fp16 tokens (KIVI_E_RAGGED when the rows differ:
+ * see kivi_query_row). */
 int kivi_cache_query(const kivi_cache* cache, kivi_state* state);
 
-/* Current counters of sequence `row`. */
+/* Current counters of sequence `row` (as kivi_cache_query, one row). */
 int kivi_query_row(const kivi_cache* cache, int32_t row, kivi_state* state);
 
-/* Counters the cache would have after kivi_append(ntok) (host only;
- * KIVI_E_RAGGED when the rows differ). */
+/* Counters the cache would have after kivi_append(ntok), by the flush rule of
+ * section 残差バッファ（Residual Buffer） (host only; KIVI_E_RAGGED when the
+ * rows differ). */
 int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after);
 
-/* Split plan kivi_attend_decode would use now: *n_split work-groups per
+/* Split plan kivi_attend_decode would use now (the split along the tokens and
+ * its merge are this library's design, not on the pages): *n_split work-groups per
  * (unit, query-head chunk) along the tokens (the last also takes the fp16
  * residual; with more than one, a merge kernel follows), and about
  * *blocks_per_split key blocks in each. */
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split);
 
-/* Force the split count of kivi_attend_decode (0 = automatic, else
+/* Force the split count of kivi_attend_decode (not on the pages, as
+ * kivi_plan_attend; 0 = automatic, else
  * 1..max_splits). Results agree up to fp32 rounding for every choice; for
  * tests and tuning. */
 int kivi_set_attend_splits(kivi_cache* cache, int32_t n_split);
 
-/* Message describing the last failing call on this thread ("" if none). */
+/* Message describing the last failing call on this thread ("" if none).
+ * Bookkeeping: no step of the method. */
 const char* kivi_last_error(void);
 
-/* KIVI_ABI_VERSION of the loaded library. */
+/* KIVI_ABI_VERSION of the loaded library. Bookkeeping: no step of the method. */
 int kivi_abi_version(void);
 
 #ifdef __cplusplus
