@@ -150,6 +150,19 @@ __device__ __forceinline__ void wait_staged(int later) {
     else wait_vmem<0>();
 }
 
+// Issue priority by the blocks a wave has left. A SIMD issues from its oldest
+// wave first, so of the two work-groups that share a CU the one dispatched
+// first runs ahead, and the other ends alone at half the CU's memory
+// parallelism (measured on MI355X: in every CU the later work-group took
+// 14-23 us longer). Near its end a wave steps its priority down, so the
+// waves of the other work-group, which have more blocks left, catch up.
+__device__ __forceinline__ void take_turn(int left) {
+    if (left >= 12) __builtin_amdgcn_s_setprio(3);
+    else if (left >= 8) __builtin_amdgcn_s_setprio(2);
+    else if (left >= 4) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Two 4-wave work-groups per CU (up to 256 VGPRs a lane: the value digit
 // sums stay in matrix-core accumulators across blocks).
 template <int D, int BITS, int NWAVES, bool RAGGED>
@@ -553,6 +566,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
                 since_fold = 0;
             }
             if (jj + NS * NWAVES < j1) stage(jj + NS * NWAVES, k);
+            take_turn((j1 - 1 - jj) / NWAVES);
         }
     }
     fold();
