@@ -122,6 +122,25 @@ __device__ __forceinline__ uint32_t pack_codes(XP xp, ZR zr, SC sc) {
     return (uint32_t)acc[0] | (uint32_t)acc[1] << 16;
 }
 
+// 16-byte chunk `idx` of the ring copy of tokens [t0, t1) of unit u (chunk
+// c16 of the key, then the value row, token by token) from input row
+// (t - in_t0) of k / v into the token's ring slot. False past the end.
+template <int D>
+__device__ __forceinline__ bool copy_ring_chunk(const CacheGeom& g, const uint16_t* k, const uint16_t* v, int64_t ntok,
+                                                int64_t u, int64_t t0, int64_t t1, int64_t in_t0, int64_t idx) {
+    constexpr int CPR = D / 8;
+    if (idx >= (t1 - t0) * 2 * CPR) return false;
+    const int c16 = (int)(idx % CPR);
+    const int kv = (int)((idx / CPR) & 1);
+    const int64_t tok = t0 + idx / (2 * CPR);
+    const int64_t row = u * ntok + (tok - in_t0);
+    const uint4* src = reinterpret_cast<const uint4*>((kv ? v : k) + row * D) + c16;
+    uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride + (size_t)(tok % g.ring_slots) * 4 * D +
+                    (size_t)kv * 2 * D;
+    reinterpret_cast<uint4*>(slot)[c16] = *src;
+    return true;
+}
+
 // One work-group per (key block j, unit): 2*D threads (with a row table, block
 // j0[row] + blockIdx.x of the unit's batch row, if below j1[row]). The block's
 // 32 key and value rows are staged in LDS, then each thread plays two roles:
@@ -159,6 +178,12 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
     const int64_t u = blockIdx.y;
+    // the ring copy's work-groups (rows that agree): 8 tokens each
+    if (a.ring_wgs && (int64_t)blockIdx.x >= a.j1 - a.j0) {
+        const int64_t idx = ((int64_t)blockIdx.x - (a.j1 - a.j0)) * NT + tid;
+        copy_ring_chunk<D>(g, a.k, a.v, a.ntok, u, a.ring_t0, a.ring_t1, a.ring_in_t0, idx);
+        return;  // the whole work-group
+    }
     // this unit's blocks and ring boundary: its batch row's, when rows differ
     // (units, rows and a sequence's tokens all fit in 32 bits)
     const int brow = (int)((uint32_t)blockIdx.y / (uint32_t)g.n_kv_heads);
@@ -272,7 +297,6 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
 // row.
 template <int D>
 __global__ __launch_bounds__(256) void ring_write_kernel(const RingArgs a) {
-    constexpr int CPR = D / 8;
     const CacheGeom& g = a.g;
     const int64_t u = blockIdx.y;
     const int64_t brow = u / g.n_kv_heads;
@@ -280,21 +304,12 @@ __global__ __launch_bounds__(256) void ring_write_kernel(const RingArgs a) {
     const int64_t t1 = a.rows.n ? a.rows.t1[brow] : a.t1;
     const int64_t in_t0 = a.rows.n ? a.rows.in_t0[brow] : a.in_t0;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n = (t1 - t0) * 2 * CPR;
-    if (idx >= n) return;
-    const int c16 = (int)(idx % CPR);
-    const int kv = (int)((idx / CPR) & 1);
-    const int64_t tok = t0 + idx / (2 * CPR);
-    const int64_t row = u * a.ntok + (tok - in_t0);
-    const uint4* src = reinterpret_cast<const uint4*>((kv ? a.v : a.k) + row * D) + c16;
-    uint8_t* slot = g.base + g.off_ring + (size_t)u * g.ring_unit_stride +
-                    (size_t)(tok % g.ring_slots) * 4 * D + (size_t)kv * 2 * D;
-    reinterpret_cast<uint4*>(slot)[c16] = *src;
+    copy_ring_chunk<D>(g, a.k, a.v, a.ntok, u, t0, t1, in_t0, idx);
 }
 
 template <int D>
 hipError_t quantize_d(const QuantArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.j1 - a.j0), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
+    const dim3 grid((unsigned)(a.j1 - a.j0 + a.ring_wgs), (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads));
     if (a.g.bits == 2)
         quantize_kernel<D, 2><<<grid, 2 * D, 0, s>>>(a);
     else

@@ -146,12 +146,21 @@ int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, i
         nblk = w.j1[b] - w.j0[b] > nblk ? w.j1[b] - w.j0[b] : nblk;
         ntk = w.t1[b] - w.t0[b] > ntk ? w.t1[b] - w.t0[b] : ntk;
     }
+    // Rows that agree, and no quantized token read from the ring (a prefill
+    // into an empty residual, say): the ring copy joins the quantize launch,
+    // as nothing the launch (or the key coder after it) reads is a ring slot
+    // the copy writes.
+    const bool fuse_ring = !ragged && nblk > 0 && ntk > 0 && w.ring_end[0] <= w.j0[0] * c->cfg.k_block;
     if (nblk > 0) {
         kivi::QuantArgs a;
         a.g = geom(c);
         a.k = static_cast<const uint16_t*>(k);
         a.v = static_cast<const uint16_t*>(v);
         a.ntok = ntok;
+        a.ring_t0 = fuse_ring ? w.t0[0] : 0;
+        a.ring_t1 = fuse_ring ? w.t1[0] : 0;
+        a.ring_in_t0 = fuse_ring ? w.in_t0[0] : 0;
+        a.ring_wgs = fuse_ring ? (int32_t)((w.t1[0] - w.t0[0] + 7) / 8) : 0;
         a.rows.n = 0;
         if (ragged) {
             a.j0 = 0;
@@ -177,7 +186,7 @@ int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, i
             if (e != hipSuccess) return device_fail(c, "squat codes launch", e);
         }
     }
-    if (ntk > 0) {
+    if (ntk > 0 && !fuse_ring) {
         kivi::RingArgs a;
         a.g = geom(c);
         a.k = static_cast<const uint16_t*>(k);

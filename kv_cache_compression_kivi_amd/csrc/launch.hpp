@@ -71,6 +71,10 @@ struct QuantRows {
     int32_t n;
     int32_t j0[kMaxRaggedRows], j1[kMaxRaggedRows], ring_end[kMaxRaggedRows];
 };
+// With ring_wgs > 0 (rows that agree, and no quantized token read from the
+// ring), the same launch also copies tokens [ring_t0, ring_t1) of every unit
+// from input rows (t - ring_in_t0) into the ring: ring_wgs more work-groups
+// per unit after the blocks' (x >= j1 - j0), 8 tokens each.
 struct QuantArgs {
     CacheGeom g;
     int64_t j0, j1;
@@ -78,6 +82,8 @@ struct QuantArgs {
     const uint16_t* k;
     const uint16_t* v;
     int64_t ntok;
+    int64_t ring_t0, ring_t1, ring_in_t0;
+    int32_t ring_wgs;
     QuantRows rows;
 };
 
