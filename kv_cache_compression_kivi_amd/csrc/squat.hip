@@ -56,13 +56,18 @@ __device__ __forceinline__ double start_value(uint32_t i) {
 }
 
 constexpr int kSquatIters = 48;
+// subspace iteration stops once r - ||V^T V'||_F^2 (the summed squared sines of
+// the angles between the subspaces of two steps) falls below this
+constexpr double kSquatTol = 1e-12;
 
 // One work-group of 256 threads per unit:
 //   1. C = sum over the unit's query heads and their n_q past queries of
 //      q q^T in fp32 (thread (a, b) of a 16 x 16 grid owns a (D/16)^2 tile);
 //   2. the top-r subspace of C by subspace iteration in fp64: W = C V, then V =
 //      W R^-1 with R the Cholesky factor of W^T W, from a fixed pseudo-random
-//      start, kSquatIters steps, and one more orthonormalisation;
+//      start, until the subspace no longer moves (the summed squared sines
+//      of the angles between two steps' subspaces below kSquatTol; kSquatIters
+//      steps at most), and one more orthonormalisation;
 //   3. w_c = -M_c^-1 u_c for c = d - 1 .. 0 with M_c^-1 by Sherman-Morrison;
 //   4. U and W (fp32, zero-padded to r8 columns) to the unit's coefficients.
 template <int D>
@@ -74,6 +79,7 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
     __shared__ __align__(16) double sv[D][RM];   // V (the queries' staging buffer before)
     __shared__ __align__(16) double sw[D][RM];   // W, then the w_c
     __shared__ double sm[RM][RM];                // W^T W and its factor, then M^-1
+    __shared__ double st[RM][RM];                // V^T W (the convergence test)
     __shared__ double sz[RM];
     static_assert(CH * D * sizeof(float) <= sizeof(sv), "the staged queries fit V's space");
     const CacheGeom& g = a.g;
@@ -93,20 +99,44 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
 #pragma unroll
             for (int k = 0; k < TS; ++k) acc[i][k] = 0.0f;
         const int64_t nvec = (int64_t)group * a.n_q;
-        for (int64_t v0 = 0; v0 < nvec; v0 += CH) {
-            __syncthreads();
-            for (int idx = tid; idx < CH * D; idx += 256) {
-                const int vv = idx / D, c = idx % D;
+        // a chunk of CH queries: 16 bytes (8 values) a lane per load, the next
+        // chunk's loads in flight while the current one is computed
+        constexpr int NL = CH * D / 8 / 256;
+        static_assert(CH * D % (8 * 256) == 0, "a chunk is a whole number of 16-byte loads a thread");
+        uint4 nx[NL];
+        auto load_chunk = [&](int64_t v0) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int idx = tid + 256 * i;
+                const int vv = idx / (D / 8), c8 = idx % (D / 8);
                 const int64_t v = v0 + vv;
-                float x = 0.0f;
                 if (v < nvec) {
                     const int64_t head = h * group + v / a.n_q, t = v % a.n_q;
-                    const uint16_t bits = a.q[((b * g.n_q_heads + head) * a.n_q + t) * D + c];
-                    x = a.q_bf16 ? __uint_as_float((uint32_t)bits << 16) : __half2float(__ushort_as_half(bits));
+                    nx[i] = *reinterpret_cast<const uint4*>(a.q + ((b * g.n_q_heads + head) * a.n_q + t) * D + 8 * c8);
+                } else {
+                    nx[i] = make_uint4(0u, 0u, 0u, 0u);
                 }
-                sq[vv][c] = x;
+            }
+        };
+        load_chunk(0);
+        for (int64_t v0 = 0; v0 < nvec; v0 += CH) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int idx = tid + 256 * i;
+                const int vv = idx / (D / 8), c8 = idx % (D / 8);
+                const uint32_t w[4] = {nx[i].x, nx[i].y, nx[i].z, nx[i].w};
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t bits = (uint16_t)(w[e / 2] >> (16 * (e & 1)));
+                    x[e] = a.q_bf16 ? __uint_as_float((uint32_t)bits << 16) : __half2float(__ushort_as_half(bits));
+                }
+                reinterpret_cast<float4*>(&sq[vv][8 * c8])[0] = make_float4(x[0], x[1], x[2], x[3]);
+                reinterpret_cast<float4*>(&sq[vv][8 * c8])[1] = make_float4(x[4], x[5], x[6], x[7]);
             }
             __syncthreads();
+            if (v0 + CH < nvec) load_chunk(v0 + CH);
 #pragma unroll 4
             for (int vv = 0; vv < CH; ++vv) {
                 float ra[TS], rb[TS];
@@ -172,20 +202,54 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
         __syncthreads();
     };
     orthonormalize(sv);
-    for (int it = 0; it <= kSquatIters; ++it) {
-        if (it < kSquatIters) {
-            for (int idx = tid; idx < D * r; idx += 256) {
-                const int c = idx / r, k = idx % r;
-                double s = 0.0;
-                for (int e = 0; e < D; ++e) s += (double)sa[c][e] * sv[e][k];
-                sw[c][k] = s;
+    for (int it = 0; it < kSquatIters; ++it) {
+        // W = C V: a thread takes row c and 8 columns; C is symmetric, so its
+        // column c is read (consecutive lanes, consecutive words), and the 8
+        // entries of V's row e are the same for the whole wave (broadcasts)
+        for (int idx = tid; idx < D * ((r + 7) / 8); idx += 256) {
+            const int c = idx % D, k0 = 8 * (idx / D);
+            double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int e = 0; e < D; ++e) {
+                const double x = (double)sa[e][c];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = fma(x, sv[e][k0 + k], acc[k]);
             }
-        } else {  // a second pass restores orthogonality to fp64 rounding
-            for (int idx = tid; idx < D * r; idx += 256) sw[idx / r][idx % r] = sv[idx / r][idx % r];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k0 + k < r) sw[c][k0 + k] = acc[k];
+        }
+        __syncthreads();
+        // T = V^T W, before V is replaced: with the new V' = W R^-1,
+        // ||V^T V'||_F^2 = ||T R^-1||_F^2 is the sum of the squared cosines of
+        // the angles between the two subspaces, r when they agree
+        for (int idx = tid; idx < r * r; idx += 256) {
+            const int i = idx / r, k = idx % r;
+            double t = 0.0;
+            for (int c = 0; c < D; ++c) t += sv[c][i] * sw[c][k];
+            st[i][k] = t;
         }
         __syncthreads();
         orthonormalize(sw);
+        if (tid < r) {  // row tid of T R^-1 (R upper, in sm), in place, and its squared norm
+            double n2 = 0.0;
+            for (int k = 0; k < r; ++k) {
+                double t = st[tid][k];
+                for (int j = 0; j < k; ++j) t -= st[tid][j] * sm[j][k];
+                st[tid][k] = t / sm[k][k];
+                n2 += st[tid][k] * st[tid][k];
+            }
+            sz[tid] = n2;
+        }
+        __syncthreads();
+        double f = 0.0;
+        for (int i = 0; i < r; ++i) f += sz[i];
+        if ((double)r - f < kSquatTol) break;  // the subspace no longer moves (uniform)
+        __syncthreads();
     }
+    // a second pass restores orthogonality to fp64 rounding
+    for (int idx = tid; idx < D * r; idx += 256) sw[idx / r][idx % r] = sv[idx / r][idx % r];
+    __syncthreads();
+    orthonormalize(sw);
 
     // 3. w_c = -M_c^-1 u_c, M_c = lambda I + sum_{i > c} u_i u_i^T, from c = D - 1 down
     for (int idx = tid; idx < r * r; idx += 256) sm[idx / r][idx % r] = idx / r == idx % r ? 1.0 / (double)a.lambda : 0.0;
