@@ -2,7 +2,8 @@
 UndefinedBehaviorSanitizer and driven through every entry point: groups of
 every size the cache uses, packing round trips, caches of several shapes fed
 in random chunks with random explicit flushes, the capacity and empty-cache
-error paths, and attention over the result. Any out-of-bounds access, leak,
+error paths, attention over the result, and the SQuat-style coder (one key's
+walk and its replay, a cache whose key blocks take the walk). Any out-of-bounds access, leak,
 signed overflow or misaligned access stops the run."""
 
 import os
@@ -83,6 +84,57 @@ static int run_cache(int B, int Hkv, int Hq, int d, int bits, int R, int T) {
     return 0;
 }
 
+/* the SQuat-style coder: one key walked and replayed along its own codes, and
+ * a cache whose key blocks take the walk, fed and read back */
+static int run_squat(int d, int bits) {
+    float* k = malloc(sizeof(float) * (size_t)d);
+    float* s = malloc(sizeof(float) * (size_t)d);
+    float* z = malloc(sizeof(float) * (size_t)d);
+    float* g = malloc(sizeof(float) * (size_t)d * (size_t)d);
+    uint8_t* codes = malloc((size_t)d);
+    uint8_t* own = malloc((size_t)d);
+    double* qq = malloc(sizeof(double) * (size_t)d);
+    for (int c = 0; c < d; ++c) {
+        k[c] = or_half_to_float(rnd_half() & 0x43ff);
+        s[c] = 0.01f + (float)(rnd() % 1000) / 100.0f;
+        z[c] = -(float)(rnd() % 500) / 100.0f;
+        for (int j = 0; j < d; ++j) g[c * d + j] = j > c ? ((float)(rnd() % 2001) - 1000.0f) / 10000.0f : 0.0f;
+    }
+    or_squat_token(k, s, z, g, d, bits, codes);
+    or_squat_replay(k, s, z, g, d, bits, codes, own, qq);
+    if (memcmp(codes, own, (size_t)d) != 0) return 30;
+    for (int c = 0; c < d; ++c)
+        if (codes[c] >= (1u << bits) || !isfinite(qq[c])) return 31;
+    or_cache* cc = or_cache_new(1, 2, 2, d, bits, 32, 32, 32, 200);
+    if (!cc) return 32;
+    float* gs = malloc(sizeof(float) * 2 * (size_t)d * (size_t)d);
+    for (int u = 0; u < 2; ++u) memcpy(gs + (size_t)u * d * d, g, sizeof(float) * (size_t)d * (size_t)d);
+    or_cache_set_squat(cc, gs);
+    free(gs);
+    uint16_t* kv = malloc(sizeof(uint16_t) * 2 * 150 * (size_t)d);
+    uint16_t* vv = malloc(sizeof(uint16_t) * 2 * 150 * (size_t)d);
+    for (int i = 0; i < 2 * 150 * d; ++i) { kv[i] = rnd_half(); vv[i] = rnd_half(); }
+    if (or_append(cc, kv, vv, 150) != 0) return 33;
+    or_flush(cc);
+    int64_t nt, nq;
+    or_state(cc, &nt, &nq);
+    uint8_t* kc = malloc((size_t)nq * d);
+    uint8_t* vc = malloc((size_t)nq * d);
+    float* ks = malloc(sizeof(float) * (size_t)(nq / 32 + 1) * d);
+    float* kz = malloc(sizeof(float) * (size_t)(nq / 32 + 1) * d);
+    float* vs = malloc(sizeof(float) * (size_t)nq * (d / 32) + 4);
+    float* vz = malloc(sizeof(float) * (size_t)nq * (d / 32) + 4);
+    for (int u = 0; u < 2; ++u) or_unit_quantized(cc, u, kc, ks, kz, vc, vs, vz);
+    uint16_t q[2 * 256];
+    double out[2 * 256];
+    for (int i = 0; i < 2 * d; ++i) q[i] = (uint16_t)(rnd_half() & 0x3fff);
+    if (or_attend(cc, q, 0, out) != 0) return 34;
+    free(kc); free(vc); free(ks); free(kz); free(vs); free(vz); free(kv); free(vv);
+    or_cache_free(cc);
+    free(k); free(s); free(z); free(g); free(codes); free(own); free(qq);
+    return 0;
+}
+
 int main(void) {
     /* groups of every size, both widths, with packing round trips */
     for (int trial = 0; trial < 2000; ++trial) {
@@ -105,6 +157,10 @@ int main(void) {
     for (int i = 0; i < 3 * 64; ++i) rows[i] = (uint8_t)(rnd() % 4);
     or_pack_rows(rows, 3, 64, 2, rw);
     int rc;
+    or_set_num_threads(2);
+    if (or_num_threads() < 1) return 40;
+    if ((rc = run_squat(64, 2))) return 500 + rc;
+    if ((rc = run_squat(128, 4))) return 600 + rc;
     if ((rc = run_cache(2, 2, 4, 64, 2, 32, 300))) return rc;
     if ((rc = run_cache(1, 1, 1, 128, 4, 0, 97))) return 100 + rc;
     if ((rc = run_cache(1, 3, 3, 256, 2, 128, 500))) return 200 + rc;
