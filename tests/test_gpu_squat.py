@@ -85,6 +85,7 @@ def _check_unit(cache, oc, gu, ou, kf, g):
     (2, 1, 4, 128, 4, 16, 300, torch.float16),
     (1, 1, 1, 128, 2, 1, 1024, torch.float16),   # one query head, rank 1
     (1, 3, 3, 128, 2, 32, 500, torch.float16),   # the largest rank
+    (1, 2, 2, 64, 2, 20, 400, torch.float16),    # d = 64, rank padded to 24 columns
 ])
 def test_squat_prefill_parity(B, Hkv, Hq, d, bits, rank, T, q_dtype):
     _announce("squat prefill", B, Hkv, Hq, d, bits, rank, T, q_dtype)
