@@ -192,3 +192,43 @@ def test_squat_before_build_and_decode_steps():
             n, worst = squat_code_check(kf[h, nq_plain:nq], s[nq_plain:], z[nq_plain:], gs[u], bits,
                                         codes[nq_plain:])
             assert nq >= nq_plain + 64 and n <= 1e-3 * (nq - nq_plain) * d, (b, h, nq, n)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_squat_degenerate_channels(bits):
+    """Key channels that are constant within a block (s floored at 1e-8, so any
+    correction saturates the code), signed zeros, fp16 subnormals, and a
+    constant token, among moderate keys: every key code a valid rounding of the
+    oracle's walk, the plain parts bit-exact, the attention within the bar and
+    finite."""
+    _announce("squat degenerate channels", bits)
+    B, Hkv, Hq, d, rank, T = 1, 1, 4, 128, 8, 32 * 6 + 128 + 5
+    wl = KVWorkload(B, Hkv, d, seed=77 + bits, device="cpu")
+    k, v = wl.kv(0, T)
+    x = k.float().numpy()
+    rng = np.random.default_rng(5 + bits)
+    x[..., 0] = 3.0                                         # constant channel
+    x[..., 1] = 0.0
+    x[..., ::2, 1] = -0.0                                   # signed zeros
+    x[..., 2] = rng.integers(1, 1024, T) * 2.0 ** -24       # fp16 subnormals
+    x[..., 9, :] = 1.5                                      # a constant token
+    k = torch.from_numpy(x.astype(np.float16))
+    qh = query_history(wl, Hq, 96, rank=rank)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV, squat_rank=rank)
+    cache.squat_build(qh.to(DEV), LAM)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    q = wl.q(Hq)
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    gs = _oracle_coefficients(qh, Hkv, rank, LAM)
+    oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T)
+    oc.set_squat(gs)
+    oc.append(k, v)
+    oc.flush()
+    kf = oracle.half_to_float(k).reshape(B * Hkv, T, d)
+    n, worst, od = _check_unit(cache, oc, 0, 0, kf[0], gs[0])
+    print(f"  key codes differing from the oracle's own: {od}; after the replay {n}", flush=True)
+    assert n <= 1e-3 * oc.state()[1] * d
+    assert_attention_close(out.cpu().numpy(), oc.attend(q))
