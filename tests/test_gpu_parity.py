@@ -560,6 +560,57 @@ def test_paged_blocks_parity(B, Hkv, Hq, d, bits, R, lens):
     assert e.value.status == "KIVI_E_INVAL"
 
 
+@pytest.mark.parametrize("B,bits,t_max,paged", [(40, 2, 700, False), (128, 4, 300, False), (40, 2, 500, True)],
+                         ids=["40rows_b2", "128rows_b4", "40rows_b2_paged"])
+def test_large_ragged_batch_parity(B, bits, t_max, paged):
+    """Serving batches with many rows of different lengths on the four-query
+    kernel: 40 rows and 128 (the largest row table) of 8 KV heads, 320 and
+    1024 units, more work-groups than one round over the CUs. Attention at
+    splits 0, 1 and 3 with bf16 queries, then decode steps whose appended
+    tokens the work-groups write to the ring. Every row against an oracle
+    cache of that row alone, bytes exact at the end."""
+    Hkv, Hq, d, R = 8, 32, 128, 128
+    rng = np.random.default_rng(B + bits)
+    lens = [int(x) for x in rng.integers(1, t_max + 1, B)]
+    _announce("large ragged batch", B, bits, t_max, "paged" if paged else "regions")
+    steps = 10
+    T = max(lens)
+    max_tokens = T + steps + 40
+    wl = KVWorkload(B, Hkv, d, seed=B * 7 + bits, device="cpu")
+    k, v = wl.kv(0, T)
+    if paged:
+        max_blocks = max_tokens // 32
+        n_pages = B * max_blocks
+        perm = rng.permutation(n_pages).astype(np.int32)
+        cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV, n_pages=n_pages)
+        cache.set_block_table(torch.from_numpy(perm.reshape(B, max_blocks)).to(DEV))
+    else:
+        cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    ocs = _row_oracles(k, v, lens, Hq, bits, max_tokens, R)
+    q = wl.q(Hq, step=0, dtype=torch.bfloat16)
+    for n in (0, 1, 3):
+        cache.set_attend_splits(n)
+        out = cache.attend(q.to(DEV))
+        torch.cuda.synchronize()
+        _check_rows(cache, ocs, out, q, q_bf16=True)
+    cache.set_attend_splits(0)
+    for i in range(steps):
+        kt, vt = wl.kv(T + i, 1)
+        qi = wl.q(Hq, step=i + 1)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), qi.to(DEV))
+        for b, oc in enumerate(ocs):
+            oc.append(kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+            nt, nq = oc.state()
+            if nt - nq >= R + 32:
+                oc.flush()
+        if i % 3 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            _check_rows(cache, ocs, out, qi)
+    torch.cuda.synchronize()
+    _check_bytes(cache, ocs)
+
+
 @pytest.mark.parametrize("paged", [False, True], ids=["regions", "paged"])
 @pytest.mark.parametrize("Hq,d,bits,R", [(2, 64, 4, 0), (8, 128, 2, 32), (4, 128, 4, 128)])
 def test_row_operations_random_walk(paged, Hq, d, bits, R):
