@@ -383,8 +383,11 @@ def _squat_measure(kv, cfg, dev, caches, prefill_inputs, reps=8):
 
 
 def _profile_prefill(workload, n):
-    """n prefills of the workload's first layer into one cache, each timed with
-    its own pair of HIP events (for a profile of the quantizer alone)."""
+    """n prefills of the workload's first layer into one cache, back to back,
+    each timed with its own pair of HIP events (for a profile of the quantizer
+    alone), after untimed ones for at least 0.5 s: measured on MI355X, a GPU
+    that starts cold runs the first tens of milliseconds of prefills up to 35%
+    slower than later ones."""
     import torch
 
     import kv_cache_compression_kivi_amd as kv
@@ -402,7 +405,15 @@ def _profile_prefill(workload, n):
         from kivi_inputs import query_history
         c.squat_build(query_history(wl, Hq, cfg["squat_queries"], rank=cfg["squat_rank"]), cfg["squat_lambda"])
     stream = torch.cuda.current_stream()
-    ts = []
+    warm, t_start = 0, time.perf_counter()
+    while time.perf_counter() - t_start < 0.5:
+        for _ in range(8):
+            c.reset()
+            c.append(k, v)
+            c.flush()
+        warm += 8
+        torch.cuda.synchronize()
+    evs = []
     for _ in range(n):
         c.reset()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -410,14 +421,16 @@ def _profile_prefill(workload, n):
         c.append(k, v)
         c.flush()
         e1.record(stream)
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
     nt, nq, _ = c.state()
     nb = prefill_bytes(B * Hkv, d, bits, nt, nq)
-    avg = sum(ts[1:]) / max(1, n - 1)
-    print(f"[bench] prefill profile {workload}: {n} prefills of B={B} x Hkv={Hkv} x T={T} (b={bits}); after the "
-          f"first, {avg:.2f} us each by HIP events, {nb} algorithmic bytes -> {nb / (avg * 1e-6) / 1e9:.1f} GB/s, "
-          f"{B * T / (avg * 1e-6):.4g} tokens/s (B*T)", file=sys.stderr, flush=True)
+    avg = sum(ts) / len(ts)
+    print(f"[bench] prefill profile {workload}: {warm} untimed then {n} timed prefills of B={B} x Hkv={Hkv} x T={T} "
+          f"(b={bits}), back to back: {avg:.2f} us each by HIP events (min {min(ts):.2f}, max {max(ts):.2f}), {nb} "
+          f"algorithmic bytes -> {nb / (avg * 1e-6) / 1e9:.1f} GB/s, {B * T / (avg * 1e-6):.4g} tokens/s (B*T)",
+          file=sys.stderr, flush=True)
 
 
 # ---------------------------------------------------------------- main
@@ -434,9 +447,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="N",
-                    help="for profiles of the quantizer: N prefills (append(T) + flush into an emptied cache) of "
-                         "the workload's first layer, each between its own HIP events, then exit (no decode steps, "
-                         "no JSON line)")
+                    help="for profiles of the quantizer: untimed prefills (append(T) + flush into an emptied "
+                         "cache) of the workload's first layer for 0.5 s, then N timed ones back to back, each "
+                         "between its own HIP events, then exit (no decode steps, no JSON line)")
     ap.add_argument("--profile", action="store_true",
                     help="for hardware-counter runs: the decode steps and attention launches of the default "
                          "run, then a plain 256 MiB device copy (the counters' calibration); no prefill "
@@ -686,6 +699,7 @@ def main():
         "quantize_append_gbs": round(pf_gbs, 2),
         "quantize_append_pct_of_peak": round(100.0 * pf_gbs / PEAK_HBM_GBS, 2),
         "quantize_append_layers_timed": pf_idx if layers > 1 else None,
+        "quantize_append_us_each": [round(a.elapsed_time(b) * 1e3, 2) for a, b in pf_ev],
         "append_1_token_us": round(ap_us, 3) if ap_us else None,
         # B tokens per call (one per sequence)
         "append_1_token_tokens_per_s": round(B / (ap_us * 1e-6), 1) if ap_us else None,
