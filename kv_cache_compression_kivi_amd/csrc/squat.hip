@@ -158,17 +158,20 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
         __syncthreads();
     }
     for (int idx = tid; idx < D * r; idx += 256) sv[idx / r][idx % r] = start_value((uint32_t)idx);
-    // C + eps I has C's eigenvectors; the shift (1e-7 of the mean eigenvalue)
-    // keeps W = C V of full rank when the queries span fewer than r directions
+    // The iteration runs on C + sigma I, which has C's eigenvectors, with sigma
+    // = 1e-5 of C's trace (at least 1e-5 of its largest eigenvalue), added in
+    // fp64 to every W = C V: when the queries span fewer than r directions, the
+    // columns of W then stay independent to within a condition number of about
+    // 1e5, which the fp64 Cholesky factor of W^T W resolves (with sigma at
+    // 1e-9 of the largest eigenvalue, a history of three exact directions drove
+    // W^T W's smallest eigenvalues below its rounding and the factor to NaN).
     if (tid == 0) {
         double tr = 0.0;
         for (int c = 0; c < D; ++c) tr += sa[c][c];
         sz[0] = tr;
     }
     __syncthreads();
-    const float eps = (float)(1e-7 * sz[0] / D) + 1e-30f;
-    __syncthreads();
-    for (int c = tid; c < D; c += 256) sa[c][c] += eps;
+    const double sigma = 1e-5 * sz[0] + 1e-30;
     __syncthreads();
 
     // 2. V <- orthonormal basis of the columns of src (Cholesky-QR)
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
     };
     orthonormalize(sv);
     for (int it = 0; it < kSquatIters; ++it) {
-        // W = C V: a thread takes row c and 8 columns; C is symmetric, so its
+        // W = (C + sigma I) V: a thread takes row c and 8 columns; C is symmetric, so its
         // column c is read (consecutive lanes, consecutive words), and the 8
         // entries of V's row e are the same for the whole wave (broadcasts)
         for (int idx = tid; idx < D * ((r + 7) / 8); idx += 256) {
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                if (k0 + k < r) sw[c][k0 + k] = acc[k];
+                if (k0 + k < r) sw[c][k0 + k] = fma(sigma, sv[c][k0 + k], acc[k]);
         }
         __syncthreads();
         // T = V^T W, before V is replaced: with the new V' = W R^-1,

@@ -232,3 +232,58 @@ def test_squat_degenerate_channels(bits):
     print(f"  key codes differing from the oracle's own: {od}; after the replay {n}", flush=True)
     assert n <= 1e-3 * oc.state()[1] * d
     assert_attention_close(out.cpu().numpy(), oc.attend(q))
+
+
+@pytest.mark.parametrize("span", [3, 0], ids=["three_directions", "all_zero"])
+def test_squat_rank_deficient_history(span):
+    """Past queries that span fewer directions than the rank: three, or none
+    (all zero). The subspace then holds free directions (any orthonormal
+    completion of the queries' span has the same top eigenvalues), so the
+    device's basis is checked for what is unique: orthonormal columns whose
+    span holds every past query. Its coefficients are checked against the
+    oracle's formula applied to that same basis, the key codes walked by the
+    oracle with those coefficients, and the attention against the bar."""
+    _announce("squat rank-deficient history", span)
+    B, Hkv, Hq, d, bits, rank, T = 1, 2, 8, 128, 2, 8, 300
+    group = Hq // Hkv
+    gen = torch.Generator().manual_seed(11 + span)
+    if span:
+        # small-integer directions and weights: every query is exact in fp16, so
+        # the history spans exactly `span` directions
+        basis = torch.randint(-1, 2, (d, span), generator=gen).float()
+        qh = (torch.randint(-4, 5, (B, Hq, 20, span), generator=gen).float() @ basis.T).half().contiguous()
+    else:
+        qh = torch.zeros(B, Hq, 20, d, dtype=torch.float16)
+    wl = KVWorkload(B, Hkv, d, seed=90 + span, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV, squat_rank=rank)
+    cache.squat_build(qh.to(DEV), LAM)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    q = wl.q(Hq)
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    gs = []
+    for u in range(B * Hkv):
+        U = cache.squat_factors(u)[0].cpu().numpy().astype(np.float64)[:, :rank]
+        assert np.abs(U.T @ U - np.eye(rank)).max() <= 1e-5, u
+        if span:
+            qu = qh[0, u * group:(u + 1) * group].reshape(-1, d).double().numpy()
+            resid = qu - (qu @ U) @ U.T
+            assert np.linalg.norm(resid) <= 1e-5 * np.linalg.norm(qu), u
+        g = squat.coefficients(U, LAM).astype(np.float32)
+        err = np.abs(_device_g(cache, u) - g).max()
+        assert err <= 1e-4 * max(np.abs(g).max(), 1e-3), (u, err)
+        gs.append(g)
+    gs = np.stack(gs)
+    oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T)
+    oc.set_squat(gs)
+    oc.append(k, v)
+    oc.flush()
+    kf = oracle.half_to_float(k).reshape(B * Hkv, T, d)
+    for u in range(B * Hkv):
+        n, worst, od = _check_unit(cache, oc, u, u, kf[u], gs[u])
+        print(f"  unit {u}: key codes differing from the oracle's own: {od}; after the replay {n}", flush=True)
+        assert n <= 1e-3 * oc.state()[1] * d
+    assert_attention_close(out.cpu().numpy(), oc.attend(q))
