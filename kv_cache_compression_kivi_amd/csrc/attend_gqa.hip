@@ -38,35 +38,6 @@
 namespace kivi {
 namespace {
 
-// Channel of byte s of a score operand, for lane group q of 64-channel chunk kc:
-// masking a token's key word by (w >> b*j) & 0x0303..03 / 0x0F0F..0F gives one
-// code per byte; these formulas follow that byte order.
-template <int BITS>
-__device__ __forceinline__ constexpr int gqa_channel(int kc, int q, int s) {
-    if constexpr (BITS == 2) {
-        return 64 * kc + 16 * q + 4 * (s % 4) + s / 4;  // word 4kc + q, s = 4j + k -> channel 4k + j
-    } else {
-        return 64 * kc + 16 * q + 8 * (s / 8) + 2 * (s % 4) + (s / 4) % 2;  // words 8kc + 2q + e, s = 8e + 4j + k
-    }
-}
-
-// Token of byte s of a value operand, for lane group q: masking a channel's
-// value word in the same way. b = 2: word q/2, bytes (w >> 2(2(q%2) + e)) ->
-// tokens 16(q/2) + 4k + 2(q%2) + e (s = 4e + k); b = 4: word q, (w >> 4e) ->
-// tokens 8q + 2k + e.
-// Score columns are assigned to tokens so that the four lanes 4c .. 4c + 3 of
-// a row (columns of one quad) hold exactly the tokens of bytes 4e .. 4e + 3 of
-// one value operand (q = 2 tt + c/2, e = c % 2): their weights then pack into
-// one word.
-template <int BITS>
-__device__ __forceinline__ constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score column m
-    if constexpr (BITS == 2) {
-        return m / 4 + 4 * (m % 4);
-    } else {
-        return 8 * ((m / 4) / 2) + (m / 4) % 2 + 2 * (m % 4);
-    }
-}
-
 // One lane's shares of a block record, read from its LDS slot before the block's math.
 template <int D, int BITS>
 struct GqaRegs {
@@ -425,7 +396,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r2 = 0; r2 < 4; ++r2) vmax = umax(vmax, __float_as_uint(r.vsz[tt][r2].x));
-        const int ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(wave_max_bits(vmax))));
+        // each row of 16 lanes reads every (token, group) scale of the block once
+        // (gqa_row_token is a permutation of a tile's 16 tokens; lane n reads
+        // group n % 4 of the tokens of columns 4 (n / 4) .. 4 (n / 4) + 3)
+        const int ev = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__uint_as_float(row_max_bits(vmax))));
         // the weights' exponent follows the block's bound when it grows, or
         // when the bound falls more than 2 below it (at most 2 of the digits'
         // 22 bits left unused)

@@ -79,6 +79,37 @@ constexpr int64_t kGqaFoldBlocks = 32768;
 constexpr int64_t kGqaBlockDigitSumMax = 128 * 15 * 32;
 static_assert(kGqaFoldBlocks * kGqaBlockDigitSumMax < (int64_t)1 << 31, "value digit sums stay in int32");
 
+// Operand layouts of the four-query kernel (attend_gqa.hip), here so that the
+// host-side tests can check them.
+// Channel of byte s of a score operand, for lane group q of 64-channel chunk kc:
+// masking a token's key word by (w >> b*j) & 0x0303..03 / 0x0F0F..0F gives one
+// code per byte; these formulas follow that byte order.
+template <int BITS>
+KIVI_HD constexpr int gqa_channel(int kc, int q, int s) {
+    if constexpr (BITS == 2) {
+        return 64 * kc + 16 * q + 4 * (s % 4) + s / 4;  // word 4kc + q, s = 4j + k -> channel 4k + j
+    } else {
+        return 64 * kc + 16 * q + 8 * (s / 8) + 2 * (s % 4) + (s / 4) % 2;  // words 8kc + 2q + e, s = 8e + 4j + k
+    }
+}
+
+// Token of byte s of a value operand, for lane group q: masking a channel's
+// value word in the same way. b = 2: word q/2, bytes (w >> 2(2(q%2) + e)) ->
+// tokens 16(q/2) + 4k + 2(q%2) + e (s = 4e + k); b = 4: word q, (w >> 4e) ->
+// tokens 8q + 2k + e.
+// Score columns are assigned to tokens so that the four lanes 4c .. 4c + 3 of
+// a row (columns of one quad) hold exactly the tokens of bytes 4e .. 4e + 3 of
+// one value operand (q = 2 tt + c/2, e = c % 2): their weights then pack into
+// one word.
+template <int BITS>
+KIVI_HD constexpr int gqa_row_token(int m) {  // token (within its 16-token tile) of score column m
+    if constexpr (BITS == 2) {
+        return m / 4 + 4 * (m % 4);
+    } else {
+        return 8 * ((m / 4) / 2) + (m / 4) % 2 + 2 * (m % 4);
+    }
+}
+
 // Key blocks wave w of nw holds out of nbw.
 KIVI_HD inline int64_t wave_blocks(int64_t nbw, int64_t nw, int64_t w) { return nbw / nw + (w < nbw % nw ? 1 : 0); }
 

@@ -286,6 +286,10 @@ void shim_plan_rows(int64_t hkv, int32_t group, int32_t d, int64_t rows, const i
     out[0] = p.n_split; out[1] = p.blocks_per_split; out[2] = p.qg; out[3] = p.nwaves;
 }
 int64_t shim_row_split_count(int64_t c, int64_t cm, int64_t n) { return kivi::row_split_count(c, cm, n); }
+int shim_gqa_row_token(int bits, int m) { return bits == 2 ? kivi::gqa_row_token<2>(m) : kivi::gqa_row_token<4>(m); }
+int shim_gqa_channel(int bits, int kc, int q, int s) {
+    return bits == 2 ? kivi::gqa_channel<2>(kc, q, s) : kivi::gqa_channel<4>(kc, q, s);
+}
 int64_t shim_unit_cost(int64_t nb, int64_t nres) { return kivi::unit_cost(nb, nres); }
 int64_t shim_gqa_fold_blocks() { return kivi::kGqaFoldBlocks; }
 int64_t shim_gqa_block_digit_sum_max() { return kivi::kGqaBlockDigitSumMax; }
@@ -317,6 +321,8 @@ def planner(tmp_path_factory):
     lib.shim_residual_wave.restype = i64
     lib.shim_plan_rows.argtypes = [i64, i32, i32, i64, ctypes.c_void_p, i64, i32, i32, i32, ctypes.c_void_p,
                                    ctypes.c_void_p]
+    lib.shim_gqa_row_token.argtypes = [ctypes.c_int] * 2
+    lib.shim_gqa_channel.argtypes = [ctypes.c_int] * 4
     lib.shim_row_split_count.argtypes = [i64] * 3
     lib.shim_row_split_count.restype = i64
     lib.shim_unit_cost.argtypes = [i64] * 2
@@ -499,6 +505,34 @@ def test_ragged_split_plan(planner):
             if n < cap:
                 more = sum(int(planner.shim_row_split_count(int(c), cmax, n + 1)) for c in cost) * hkv * (group // qg)
                 assert more > target, (n, more, target)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_four_query_operand_layouts(planner, bits):
+    """The four-query kernel's lane-to-data maps: a score operand's bytes over
+    the four lane groups cover each 64-channel chunk once; score columns map
+    onto a tile's 16 tokens one to one, so each row of 16 lanes reads every
+    (token, value group) scale of a block once; and the four columns of a quad
+    hold exactly the tokens of bytes 4e .. 4e + 3 of value operand q = 2 tt + c / 2
+    (e = c % 2), whose byte s = 4e + k holds token 16 (q / 2) + 4k + 2 (q % 2) + e
+    at b = 2 and 8q + 2k + e at b = 4."""
+    for kc in range(2):
+        ch = sorted(planner.shim_gqa_channel(bits, kc, q, s_) for q in range(4) for s_ in range(16))
+        assert ch == list(range(64 * kc, 64 * kc + 64))
+    rt = [planner.shim_gqa_row_token(bits, m) for m in range(16)]
+    assert sorted(rt) == list(range(16))
+    # lane n of a row reads group n % 4 of the tokens of columns 4 (n // 4) + r
+    pairs = sorted((16 * tt + rt[4 * (n // 4) + r], n % 4) for n in range(16) for r in range(4) for tt in range(2))
+    assert pairs == [(t, g) for t in range(32) for g in range(4)]
+    for tt in range(2):
+        for c in range(4):
+            q, e = 2 * tt + c // 2, c % 2
+            cols = {16 * tt + rt[4 * c + i] for i in range(4)}
+            if bits == 2:
+                want = {16 * (q // 2) + 4 * k + 2 * (q % 2) + e for k in range(4)}
+            else:
+                want = {8 * q + 2 * k + e for k in range(4)}
+            assert cols == want, (bits, tt, c)
 
 
 SANITIZED_MAIN = r"""
