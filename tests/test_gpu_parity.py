@@ -13,7 +13,7 @@ import torch
 
 import kv_cache_compression_kivi_amd as kv
 import oracle
-from kivi_inputs import CONFIGS, KVWorkload
+from kivi_inputs import CONFIGS, KVWorkload, page_order, row_lengths
 from kivi_testlib import assert_attention_close, compare_unit
 
 pytestmark = pytest.mark.gpu
@@ -327,6 +327,64 @@ def test_gqa_streaming_full_size():
     torch.cuda.synchronize()
     for u in units:
         compare_unit(cache, ocs[u], u, 0)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["regions", "paged"])
+def test_serving_batch_full_size(paged):
+    """The serving-batch workloads at full size, built as the benchmark builds
+    them (64 rows at their seeded lengths; paged: every row's pages in the
+    seeded random order), then 40 steps through kivi_decode_step, whose flushes
+    fall on different steps per row. The longest, the shortest and a middling
+    row, KV heads 0 and 7, against their oracle caches at several steps; their
+    bytes at the end."""
+    cfg = CONFIGS["gqa_paged" if paged else "gqa_ragged"]
+    _announce("serving batch", "paged" if paged else "regions")
+    B, Hkv, Hq, d, T, bits = (cfg[x] for x in ("batch", "n_kv_heads", "n_q_heads", "head_dim", "T", "bits"))
+    group = Hq // Hkv
+    steps = 40
+    lens = row_lengths(B, cfg["ragged"][0], cfg["ragged"][1], cfg["seed"])
+    max_tokens = T + steps + 64
+    wl = KVWorkload(B, Hkv, d, seed=cfg["seed"], device=DEV)
+    k, v = wl.kv(0, T)
+    if paged:
+        mb = max_tokens // 32
+        cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=DEV, n_pages=B * mb)
+        cache.set_block_table(page_order(B * mb, cfg["seed"]).reshape(B, mb).to(DEV))
+    else:
+        cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, device=DEV)
+    cache.append_rows(k, v, lens)
+    cache.flush()
+    order = sorted(range(B), key=lambda r: lens[r])
+    rows = [order[-1], order[0], order[B // 2]]
+    units = [(r, h) for r in rows for h in (0, Hkv - 1)]
+    ocs = {}
+    for r, h in units:
+        oc = oracle.OracleCache(1, 1, group, d, bits, max_tokens=max_tokens)
+        oc.append(k[r:r + 1, h:h + 1, :lens[r]].cpu(), v[r:r + 1, h:h + 1, :lens[r]].cpu())
+        nt, nq = oc.state()
+        if nt - nq >= 128 + 32:
+            oc.flush()
+        ocs[(r, h)] = oc
+    del k, v
+    for i in range(1, steps + 1):
+        kt, vt = wl.kv(T + i - 1, 1)
+        q = wl.q(Hq, step=i)
+        out = cache.decode_step(kt, vt, q)
+        for r, h in units:
+            ocs[(r, h)].append(kt[r:r + 1, h:h + 1].cpu(), vt[r:r + 1, h:h + 1].cpu())
+            nt, nq = ocs[(r, h)].state()
+            if nt - nq >= 128 + 32:
+                ocs[(r, h)].flush()
+        if i in (1, 17, 33, steps):
+            torch.cuda.synchronize()
+            for r, h in units:
+                assert cache.row_state(r)[:2] == ocs[(r, h)].state(), (r, cache.row_state(r), ocs[(r, h)].state())
+                ref = ocs[(r, h)].attend(_unit_rows(q.cpu(), r, h, group))
+                got = out[r:r + 1, h * group:(h + 1) * group].cpu().numpy()
+                assert_attention_close(got, ref)
+    torch.cuda.synchronize()
+    for r, h in units:
+        compare_unit(cache, ocs[(r, h)], r * Hkv + h, 0)
 
 
 @pytest.mark.parametrize("layer", [0, 31])
