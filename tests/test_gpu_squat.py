@@ -121,6 +121,40 @@ def test_squat_prefill_parity(B, Hkv, Hq, d, bits, rank, T, q_dtype):
     assert_attention_close(out.cpu().numpy(), oc.attend(q))
 
 
+@pytest.mark.parametrize("lam", [1e-2, 10.0])
+def test_squat_lambda_range(lam):
+    """The objective's weight lambda away from the 0.1 of the other cases: 1e-2
+    (larger corrections) and 10 (codes close to the plain coder's).
+    Coefficients within 1e-4 of the oracle's, key codes valid by replay,
+    attention within the bar."""
+    _announce("squat lambda", lam)
+    B, Hkv, Hq, d, bits, rank, T = 1, 2, 8, 128, 2, 8, 400
+    wl = KVWorkload(B, Hkv, d, seed=61, device="cpu")
+    k, v = wl.kv(0, T)
+    qh = query_history(wl, Hq, 96, rank=rank)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV, squat_rank=rank)
+    cache.squat_build(qh.to(DEV), lam)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    q = wl.q(Hq)
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    gs = _oracle_coefficients(qh, Hkv, rank, lam)
+    for u in range(B * Hkv):
+        err = np.abs(_device_g(cache, u) - gs[u]).max()
+        assert err <= 1e-4 * max(np.abs(gs[u]).max(), 1e-3), (u, err)
+    oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T)
+    oc.set_squat(gs)
+    oc.append(k, v)
+    oc.flush()
+    kf = oracle.half_to_float(k).reshape(B * Hkv, T, d)
+    for u in range(B * Hkv):
+        n, worst, od = _check_unit(cache, oc, u, u, kf[u], gs[u])
+        print(f"  unit {u}: key codes differing from the oracle's own: {od}; after the replay {n}", flush=True)
+        assert n <= 1e-3 * oc.state()[1] * d
+    assert_attention_close(out.cpu().numpy(), oc.attend(q))
+
+
 def test_squat_coefficients_closed_form():
     """Past queries all along the all-ones direction: rank-1 subspace u = 1/sqrt(d),
     and g[c][j] = -1 / (lambda d + d - 1 - c) for j > c."""
