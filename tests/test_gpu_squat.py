@@ -321,3 +321,64 @@ def test_squat_rank_deficient_history(span):
         print(f"  unit {u}: key codes differing from the oracle's own: {od}; after the replay {n}", flush=True)
         assert n <= 1e-3 * oc.state()[1] * d
     assert_attention_close(out.cpu().numpy(), oc.attend(q))
+
+
+def test_squat_paged_rows():
+    """The SQuat-style coder on a paged cache whose rows differ in length: the
+    coefficients built first, a ragged prefill whose blocks land on scrambled
+    pages, then decode steps whose flushes (R = 32) code new blocks on further
+    pages. Each row against an oracle cache of that row alone with the oracle's
+    own coefficients: key codes valid by replay, the plain parts bit-exact,
+    attention within the bar at several steps."""
+    _announce("squat paged rows")
+    B, Hkv, Hq, d, bits, rank, R = 3, 2, 8, 128, 2, 8, 32
+    lens = [300, 77, 520]
+    steps = 40
+    T = max(lens)
+    max_tokens = T + steps + 40
+    mb = max_tokens // 32
+    n_pages = B * mb + 5
+    rng = np.random.default_rng(9)
+    table = rng.permutation(n_pages).astype(np.int32)[:B * mb].reshape(B, mb)
+    wl = KVWorkload(B, Hkv, d, seed=123, device="cpu")
+    k, v = wl.kv(0, T)
+    qh = query_history(wl, Hq, 96, rank=rank)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV, n_pages=n_pages,
+                         squat_rank=rank)
+    cache.set_block_table(torch.from_numpy(table).to(DEV))
+    cache.squat_build(qh.to(DEV), LAM)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    gs = _oracle_coefficients(qh, Hkv, rank, LAM)
+    ocs = []
+    for b in range(B):
+        oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R)
+        oc.set_squat(gs[b * Hkv:(b + 1) * Hkv])
+        oc.append(k[b:b + 1, :, :lens[b]].contiguous(), v[b:b + 1, :, :lens[b]].contiguous())
+        ocs.append(oc)
+    new_k = []
+    for i in range(steps):
+        kt, vt = wl.kv(T + i, 1)
+        q = wl.q(Hq, step=i + 1)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), q.to(DEV))
+        new_k.append(kt)
+        for b, oc in enumerate(ocs):
+            oc.append(kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+            nt, nq = oc.state()
+            if nt - nq >= R + 32:
+                oc.flush()
+        if i % 13 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            for b, oc in enumerate(ocs):
+                assert cache.row_state(b)[:2] == oc.state(), (b, cache.row_state(b), oc.state())
+                assert_attention_close(out[b:b + 1].cpu().numpy(), oc.attend(q[b:b + 1]))
+    torch.cuda.synchronize()
+    kn = torch.cat(new_k, dim=2)
+    total = diff = 0
+    for b, oc in enumerate(ocs):
+        for h in range(Hkv):
+            kf = oracle.half_to_float(torch.cat([k[b, h, :lens[b]], kn[b, h]], dim=0).contiguous())
+            n, worst, od = _check_unit(cache, oc, b * Hkv + h, h, kf, gs[b * Hkv + h])
+            total += oc.state()[1] * d
+            diff += n
+    print(f"  key codes differing after the replay: {diff} of {total}", flush=True)
+    assert diff <= 1e-3 * total
