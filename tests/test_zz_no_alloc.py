@@ -73,6 +73,36 @@ def test_noalloc_matches_attend_decode_twice():
     assert np.array_equal(ref3.view(np.uint32), got3.view(np.uint32))
 
 
+@pytest.mark.parametrize("Hq", [8, 2], ids=["four_query", "mha"])
+def test_noalloc_on_paged_rows(Hq):
+    """A paged cache whose rows differ in length (the kernels built with a row
+    table; short rows see idle splits) at 5 forced splits: the allocation-free
+    call bit for bit against kivi_attend_decode, and each row against an oracle
+    cache of that row alone."""
+    print(f"\n[case] noalloc paged rows: B3 kv2 q{Hq} d128 b2 lens 700/33/1200 splits 5", flush=True)
+    B, Hkv, d, bits = 3, 2, 128, 2
+    lens = [700, 33, 1200]
+    T = max(lens)
+    mb = T // 32 + 1
+    n_pages = B * mb + 3
+    table = np.random.default_rng(44).permutation(n_pages).astype(np.int32)[:B * mb].reshape(B, mb)
+    wl = KVWorkload(B, Hkv, d, seed=44, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV, n_pages=n_pages)
+    cache.set_block_table(torch.from_numpy(table).to(DEV))
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    cache.flush()
+    cache.set_attend_splits(5)
+    q = wl.q(Hq)
+    ref, got = _both(cache, q.to(DEV))
+    assert np.array_equal(ref.view(np.uint32), got.view(np.uint32))
+    for b in range(B):
+        oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
+        oc.append(k[b:b + 1, :, :lens[b]].contiguous(), v[b:b + 1, :, :lens[b]].contiguous())
+        oc.flush()
+        assert_attention_close(got[b:b + 1], oc.attend(q[b:b + 1]))
+
+
 def test_noalloc_refuses_partials_beyond_the_scratch():
     print("\n[case] noalloc too large: B64 kv8 q32 d128 splits 256", flush=True)
     B, Hkv, Hq, d = 64, 8, 32, 128
