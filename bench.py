@@ -43,6 +43,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# prefill sweeps timed back to back (each cache's median counts)
+PF_REPS = 5
 PEAK_HBM_GBS = 8000.0
 METRIC = "decode-attention effective HBM GB/s (% of peak) + quantize-append tokens/s"
 
@@ -613,26 +615,32 @@ def main():
         return
 
     # prefill quantize-append: append(T) + flush into an empty cache, on the
-    # first and last layer of each bit width (the first and last input kept)
+    # first and last layer of each bit width (the first and last input kept),
+    # PF_REPS sweeps back to back; each cache's median prefill counts
     pf_idx = pf_layers if layers > 1 else list(range(min(len(caches), max(4, n_rot))))
-    pf_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in pf_idx]
+    pf_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in pf_idx]
+             for _ in range(PF_REPS)]
     pf_bytes = pf_tokens = pf_unit_tokens = 0
-    for e, i in zip(pf_ev, pf_idx):
-        c = caches[i]
-        k, v = prefill_inputs.get(i % layers, prefill_inputs[min(prefill_inputs)])
-        c.reset()
-        e[0].record(stream)
-        if cfg.get("ragged"):
-            c.append_rows(k, v, lens)
-        else:
-            c.append(k, v)
-        c.flush()
-        e[1].record(stream)
-        pf_bytes += sum(prefill_bytes(Hkv * w, d, c.cfg.bits, nt, nq) for nt, nq, _, w in row_groups(c))
-        pf_tokens += sum(lens)
-        pf_unit_tokens += Hkv * sum(lens)
+    for rep in range(PF_REPS):
+        for e, i in zip(pf_ev[rep], pf_idx):
+            c = caches[i]
+            k, v = prefill_inputs.get(i % layers, prefill_inputs[min(prefill_inputs)])
+            c.reset()
+            e[0].record(stream)
+            if cfg.get("ragged"):
+                c.append_rows(k, v, lens)
+            else:
+                c.append(k, v)
+            c.flush()
+            e[1].record(stream)
+            if rep == 0:
+                pf_bytes += sum(prefill_bytes(Hkv * w, d, c.cfg.bits, nt, nq) for nt, nq, _, w in row_groups(c))
+                pf_tokens += sum(lens)
+                pf_unit_tokens += Hkv * sum(lens)
     torch.cuda.synchronize()
-    pf_ms = sum(a.elapsed_time(b) for a, b in pf_ev)
+    pf_us_each = [sorted(pf_ev[rep][j][0].elapsed_time(pf_ev[rep][j][1]) * 1e3 for rep in range(PF_REPS))
+                  for j in range(len(pf_idx))]
+    pf_ms = sum(t[len(t) // 2] for t in pf_us_each) * 1e-3
     pf_tok_s = pf_tokens / (pf_ms * 1e-3)
     pf_gbs = pf_bytes / (pf_ms * 1e-3) / 1e9
 
@@ -699,7 +707,8 @@ def main():
         "quantize_append_gbs": round(pf_gbs, 2),
         "quantize_append_pct_of_peak": round(100.0 * pf_gbs / PEAK_HBM_GBS, 2),
         "quantize_append_layers_timed": pf_idx if layers > 1 else None,
-        "quantize_append_us_each": [round(a.elapsed_time(b) * 1e3, 2) for a, b in pf_ev],
+        "quantize_append_us_each": [[round(x, 2) for x in t] for t in pf_us_each],
+        "quantize_append_reps": PF_REPS,
         "append_1_token_us": round(ap_us, 3) if ap_us else None,
         # B tokens per call (one per sequence)
         "append_1_token_tokens_per_s": round(B / (ap_us * 1e-6), 1) if ap_us else None,

@@ -18,6 +18,7 @@
 
 #include <cstdint>
 
+#include "codec_math.hpp"
 #include "launch.hpp"
 
 namespace kivi {
@@ -54,12 +55,13 @@ __device__ __forceinline__ void minmax_pairs(const uint32_t (&p)[N], float& mn, 
     mx = fmaxf((float)hi[0], (float)hi[1]);
 }
 
-// Scale and zero of a group from its extremes (IEEE division, no contraction),
-// and the reciprocal the fast code path multiplies by.
+// Scale and zero of a group from its extremes (the correctly rounded quotient
+// of IEEE division, no contraction), and the reciprocal the fast code path
+// multiplies by.
 template <int BITS>
 __device__ __forceinline__ void group_stats(float mn, float mx, float& s, float& z, float& rs) {
     constexpr float kQmax = float((1 << BITS) - 1);
-    s = (mx - mn) / kQmax;
+    s = div_by_levels(mx - mn, kQmax, 1.0f / kQmax);
     if (!(s >= 1e-8f)) s = 1e-8f;
     z = mn + 0.0f;  // -0 -> +0
     rs = __builtin_amdgcn_rcpf(s);

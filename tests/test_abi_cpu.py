@@ -535,6 +535,48 @@ def test_four_query_operand_layouts(planner, bits):
             assert cols == want, (bits, tt, c)
 
 
+DIV_CHECK_MAIN = r"""
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include "codec_math.hpp"
+int main() {
+    const float ys[2] = {3.0f, 15.0f};
+    unsigned long long bad = 0, n = 0;
+    for (float y : ys) {
+        for (uint32_t u = 0x33800000u; u <= 0x48000000u; ++u) {  // every fp32 in [2^-24, 2^17]
+            float x;
+            std::memcpy(&x, &u, 4);
+            const float want = x / y;
+            const float got = kivi::div_by_levels(x, y, 1.0f / y);
+            ++n;
+            if (std::memcmp(&want, &got, 4) != 0) ++bad;
+        }
+        const float z = kivi::div_by_levels(0.0f, y, 1.0f / y);
+        ++n;
+        if (z != 0.0f || std::signbit(z)) ++bad;
+    }
+    std::printf("%llu %llu\n", n, bad);
+    return 0;
+}
+"""
+
+
+def test_quantizer_division_is_exact(tmp_path):
+    """The quantizer's scale (max - min) / (2^b - 1) without a division
+    (codec_math.hpp: div_by_levels, the code the kernel runs) equals IEEE fp32
+    division for every possible range: 0 and every fp32 in [2^-24, 2^17], for
+    b = 2 and 4."""
+    src = tmp_path / "divcheck.cpp"
+    src.write_text(DIV_CHECK_MAIN)
+    exe = tmp_path / "divcheck"
+    subprocess.check_call(["g++", "-std=c++17", "-O2", "-ffp-contract=off",
+                           "-I", os.path.join(ROOT, "kv_cache_compression_kivi_amd", "csrc"), str(src), "-o", str(exe)])
+    n, bad = (int(x) for x in subprocess.check_output([str(exe)], timeout=300).split())
+    assert n == 2 * (0x48000000 - 0x33800000 + 2)
+    assert bad == 0
+
+
 SANITIZED_MAIN = r"""
 #include <cstdio>
 #include <cstdlib>
