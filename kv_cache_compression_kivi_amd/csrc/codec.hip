@@ -59,15 +59,31 @@ __device__ __forceinline__ void minmax_pairs(const uint32_t (&p)[N], float& mn, 
 }
 
 // Scale and zero of a group from its extremes (the correctly rounded quotient
-// of IEEE division, no contraction), and the reciprocal the fast code path
-// multiplies by.
+// of IEEE division, no contraction), and the two terms of the fast code path
+// below: p = x rf + cf, with rf = rcp(s) and cf = -z rf rounded once. When
+// |cf| > 32 that sum is not close enough to (x - z) / s for the path's tie
+// test, and the group takes rf = 0, cf = 1/2 instead: every p is then exactly
+// a half-integer, so each word with such a code takes the division path. A
+// group of one value (max = min, also +0 and -0) takes rf = cf = 0: its
+// codes are 0, as (x - z) / s = 0 says.
 template <int BITS>
-__device__ __forceinline__ void group_stats(float mn, float mx, float& s, float& z, float& rs) {
+__device__ __forceinline__ void group_stats(float mn, float mx, float& s, float& z, float& rf, float& cf) {
     constexpr float kQmax = float((1 << BITS) - 1);
     s = div_by_levels(mx - mn, kQmax, 1.0f / kQmax);
     if (!(s >= 1e-8f)) s = 1e-8f;
     z = mn + 0.0f;  // -0 -> +0
-    rs = __builtin_amdgcn_rcpf(s);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float c = -z * rs;
+    if (mx == mn) {
+        rf = 0.0f;
+        cf = 0.0f;
+    } else if (fabsf(c) <= 32.0f) {
+        rf = rs;
+        cf = c;
+    } else {
+        rf = 0.0f;
+        cf = 0.5f;
+    }
 }
 
 // x - z for the fp16 half `hi` (0: bits 0..15, 1: bits 16..31) of `pair`,
@@ -84,23 +100,38 @@ __device__ __forceinline__ float half_minus(uint32_t pair, float z) {
     return r;
 }
 
+// x rf + cf for the fp16 half `hi` of `pair`, rounded once to fp32 (the half
+// widened exactly).
+template <int HI>
+__device__ __forceinline__ float half_fma(uint32_t pair, float rf, float cf) {
+    float r;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(rf), "v"(cf));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(rf), "v"(cf));
+    return r;
+}
+
 // One packed word of N codes: code i = clamp(rint((x_i - z_i) / s_i), 0, 2^b - 1)
 // at bits [b i, b i + b). xp(i) gives a 32-bit word whose half (i & 1) is the
-// fp16 value x_i, zr(i) the pair (z_i, rcp(s_i)), sc(i) the scale s_i.
+// fp16 value x_i, fr(i) the fast path's pair (cf_i, rf_i) and sz(i) the pair
+// (s_i, z_i).
 //
-// The bytes are those of the IEEE steps, computed faster: t = x - z, then
-// p = t rcp(s). With rcp within 1 ulp of 1/s, p differs from the IEEE
-// quotient q by at most (2^-23 + 2^-24) 15.5 + 2^-20 < 2^-18 (codes <= 15),
-// so rint(p) = rint(q) unless p lies within 2^-18 of a half integer.
-// |p - rint(p)| is exact and at most 1/2; when its largest value over the
-// word exceeds 1/2 - 2^-15 in some lane (ties included), the wave redoes the
-// word by true division.
-// The clamp of the definition never binds on this path: 0 <= t <= max - min,
-// so 0 <= p <= (2^b - 1)(1 + 2^-22) and rint(p) is in [0, 2^b - 1] (with s
-// floored at 1e-8, p is smaller still). The division path keeps it.
+// The bytes are those of the IEEE steps (q = RN(RN(x - z) / s), then rint),
+// computed faster: p = RN(x rf + cf) in one mixed-precision fma. With rf
+// within 1 ulp of 1/s, cf within 2^-24 |cf| <= 2^-19 of -z rf, and codes up
+// to 15.5, p differs from (x - z)/s by at most 15.5 2^-23 + 2^-19 + 2^-20,
+// and q from (x - z)/s by at most 15.5 2^-23: |p - q| < 2^-17. So rint(p) =
+// rint(q) unless p lies within 2^-17 of a half integer. |p - rint(p)| is
+// exact and at most 1/2; when its largest value over the word exceeds
+// 1/2 - 2^-15 in some lane (ties included), the wave redoes the word by true
+// division.
+// The clamp of the definition never binds on this path: (x - z)/s lies in
+// [0, 2^b - 1], so p lies within 2^-17 of that range and rint(p) in it (a
+// p just below 0 rounds to -0, code 0). The division path keeps the clamp.
 // Codes accumulate exactly in fp32, 16 bits per accumulator.
-template <int BITS, int N, class XP, class ZR, class SC>
-__device__ __forceinline__ uint32_t pack_codes(XP xp, ZR zr, SC sc) {
+template <int BITS, int N, class XP, class FR, class SZ>
+__device__ __forceinline__ uint32_t pack_codes(XP xp, FR fr, SZ sz) {
     constexpr float kQmax = float((1 << BITS) - 1);
     constexpr int H = 16 / BITS;  // codes per accumulator
     static_assert(N == 2 * H, "a word is two 16-bit halves");
@@ -108,9 +139,8 @@ __device__ __forceinline__ uint32_t pack_codes(XP xp, ZR zr, SC sc) {
     float dmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const float2 q = zr(i);
-        const float t = (i & 1) ? half_minus<1>(xp(i), q.x) : half_minus<0>(xp(i), q.x);
-        const float p = t * q.y;
+        const float2 q = fr(i);
+        const float p = (i & 1) ? half_fma<1>(xp(i), q.y, q.x) : half_fma<0>(xp(i), q.y, q.x);
         const float r = __builtin_rintf(p);
         dmax = fmaxf(dmax, fabsf(p - r));
         acc[i / H] = __builtin_fmaf(r, (float)(1 << (BITS * (i % H))), acc[i / H]);
@@ -119,8 +149,9 @@ __device__ __forceinline__ uint32_t pack_codes(XP xp, ZR zr, SC sc) {
         acc[0] = acc[1] = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const float t = (i & 1) ? half_minus<1>(xp(i), zr(i).x) : half_minus<0>(xp(i), zr(i).x);
-            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t / sc(i)), 0.0f, kQmax);
+            const float2 w = sz(i);
+            const float t = (i & 1) ? half_minus<1>(xp(i), w.y) : half_minus<0>(xp(i), w.y);
+            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t / w.x), 0.0f, kQmax);
             acc[i / H] = __builtin_fmaf(r, (float)(1 << (BITS * (i % H))), acc[i / H]);
         }
     }
@@ -171,14 +202,15 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
     constexpr int DP = D + 8;
     __shared__ __align__(16) uint16_t sk[kG * DP];
     __shared__ __align__(16) uint16_t sv[kG * DP];
-    // statistics for the codes: key (z, rcp s) of channel c at kzr[c + 2 (c / 32)]
-    // (the 32-channel groups, read together by the lanes of a wave, start on
-    // different banks), key s; value (z, rcp s) and s per group and token (rows
-    // padded apart for the same reason)
+    // statistics for the codes: the fast path's key (cf, rf) of channel c at
+    // kzr[c + 2 (c / 32)] (the 32-channel groups, read together by the lanes
+    // of a wave, start on different banks), key (s, z) for the division path;
+    // value (cf, rf) and (s, z) per group and token (rows padded apart for the
+    // same reason)
     __shared__ __align__(16) float2 kzr[D + 2 * NG];
-    __shared__ __align__(16) float ks[D];
+    __shared__ __align__(16) float2 ksz[D];
     __shared__ __align__(16) float2 vzr[NG][kG + 2];
-    __shared__ __align__(16) float vs[NG][kG];
+    __shared__ __align__(16) float2 vsz[NG][kG];
 
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
@@ -237,11 +269,11 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
             const half2_t x = {hk[i * DP + c], hk[(i + 16) * DP + c]};
             p[i] = __builtin_bit_cast(uint32_t, x);
         }
-        float mn, mx, s, z, r;
+        float mn, mx, s, z, rf, cf;
         minmax_pairs(p, mn, mx);
-        group_stats<BITS>(mn, mx, s, z, r);
-        kzr[c + 2 * (c / kVG)] = make_float2(z, r);
-        ks[c] = s;
+        group_stats<BITS>(mn, mx, s, z, rf, cf);
+        kzr[c + 2 * (c / kVG)] = make_float2(cf, rf);
+        ksz[c] = make_float2(s, z);
         __builtin_nontemporal_store(nt_f2{s, z}, reinterpret_cast<nt_f2*>(rec + g.rec_ksz) + c);
     } else {
         // value group gg of token t: 32 contiguous channels
@@ -255,11 +287,11 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
             p[4 * i + 2] = x.z;
             p[4 * i + 3] = x.w;
         }
-        float mn, mx, s, z, r;
+        float mn, mx, s, z, rf, cf;
         minmax_pairs(p, mn, mx);
-        group_stats<BITS>(mn, mx, s, z, r);
-        vzr[gg][t] = make_float2(z, r);
-        vs[gg][t] = s;
+        group_stats<BITS>(mn, mx, s, z, rf, cf);
+        vzr[gg][t] = make_float2(cf, rf);
+        vsz[gg][t] = make_float2(s, z);
         __builtin_nontemporal_store(nt_f2{s, z}, reinterpret_cast<nt_f2*>(rec + g.rec_vsz) + tg);
     }
     __syncthreads();
@@ -276,7 +308,7 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
         for (int k = 0; k < NWG; ++k)
             words[k] = pack_codes<BITS, PER>(
                 [&](int i) { return (uint32_t)col[(k * PER + i) * DP] << (16 * (i & 1)); },
-                [&](int i) { return vzr[grp][k * PER + i]; }, [&](int i) { return vs[grp][k * PER + i]; });
+                [&](int i) { return vzr[grp][k * PER + i]; }, [&](int i) { return vsz[grp][k * PER + i]; });
     } else {
         const uint32_t* row = reinterpret_cast<const uint32_t*>(&sk[t * DP + gg * kVG]);
 #pragma unroll
@@ -284,7 +316,7 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(const QuantArgs a) {
             const int c0 = gg * kVG + k * PER;
             words[k] = pack_codes<BITS, PER>([&](int i) { return row[(k * PER + i) / 2]; },
                                              [&](int i) { return kzr[c0 + i + 2 * gg]; },
-                                             [&](int i) { return ks[c0 + i]; });
+                                             [&](int i) { return ksz[c0 + i]; });
         }
     }
     // channel c's BITS value words, or token t's BITS key words of group gg
