@@ -778,7 +778,9 @@ def test_unwritten_ring_slots_never_reach_the_output(Hq, bits):
 def test_degenerate_and_extreme_groups(bits):
     """Key channels and value groups that are constant (s floored at 1e-8), all
     zero with mixed signs of zero, at the fp16 extremes (+-65504, one range
-    spanning both), made of fp16 subnormals, or holding a single outlier.
+    spanning both), made of fp16 subnormals, holding a single outlier, or offset
+    from zero by more than, about or less than 32 of their scales (the fast
+    code path's limit).
     Codes, scales, zeros and residual rows bit-exact against the oracle; the
     attention (a zero query, so every weight is equal and the outputs stay near
     the values' means) within the bar where the values are moderate."""
@@ -794,8 +796,13 @@ def test_degenerate_and_extreme_groups(bits):
     x[:, 4] = rng.integers(1, 1024, T) * 2.0 ** -24        # fp16 subnormals
     x[:, 5] = 0.0
     x[::37, 5] = 1000.0                                    # a lone outlier per block
+    x[:, 6] = 1000.0 + rng.standard_normal(T) * 0.5        # offset far beyond the range: the division path
+    x[:, 7] = 40.0 + rng.integers(0, 4, T)                 # z / s = 40 at b = 2, beyond the fast path's 32
+    x[:, 8] = 30.0 + rng.integers(0, 4, T)                 # z / s = 30 at b = 2, inside it
+    x[:, 9] = -32.0 + rng.integers(0, 4, T)                # z / s = -32, on its edge
     x[7, :] = 2.5                                          # a constant token (value groups)
     x[11, 32:64] = -65504.0
+    x[13, 64:96] = 500.0 + rng.standard_normal(32)         # a value group far from zero
     k = torch.from_numpy(x.astype(np.float16)).reshape(1, 1, T, d)
     v = torch.from_numpy(np.ascontiguousarray(x[::-1]).astype(np.float16)).reshape(1, 1, T, d)
     cache = kv.KiviCache(1, 1, 1, d, bits, max_tokens=T, device=DEV)
@@ -809,7 +816,9 @@ def test_degenerate_and_extreme_groups(bits):
     # attention over moderate values: zero the extreme value channels for this part
     vm = v.clone()
     vm[..., 2:4] = 0
+    vm[..., 6] = 0
     vm[0, 0, T - 1 - 11, 32:64] = 0
+    vm[0, 0, T - 1 - 13, 64:96] = 0
     cm = kv.KiviCache(1, 1, 1, d, bits, max_tokens=T, device=DEV)
     cm.append(k.to(DEV), vm.to(DEV))
     om = oracle.OracleCache(1, 1, 1, d, bits, max_tokens=T)
