@@ -59,6 +59,30 @@ constexpr int kSquatIters = 48;
 // subspace iteration stops once r - ||V^T V'||_F^2 (the summed squared sines of
 // the angles between the subspaces of two steps) falls below this
 constexpr double kSquatTol = 1e-12;
+// One-sided Jacobi, taken when the subspace iteration has not converged in
+// kSquatIters steps (the past queries' spectrum does not fall off after the
+// r-th eigenvalue): a pair of columns is rotated unless |m_p . m_q| <=
+// kJacobiTol ||m_p|| ||m_q||; the sweeps stop after one with no rotation, or
+// after kJacobiSweeps.
+constexpr double kJacobiTol = 1.5e-14;
+constexpr int kJacobiSweeps = 30;
+// M's column stride in doubles: two more than a column, so that the pairs of
+// a round spread over the LDS banks
+template <int D>
+constexpr int jacobi_stride() { return D + 2; }
+// Pair i of round k (0 <= k < D - 1) of the circle method: over D - 1 rounds
+// the D / 2 disjoint pairs of each round meet every pair of columns once.
+template <int D>
+__device__ __forceinline__ void jacobi_pair(int k, int i, int& p, int& q) {
+    constexpr int m = D - 1;
+    if (i == 0) {
+        p = k;
+        q = D - 1;
+    } else {
+        p = (k + i) % m;
+        q = (k - i + m) % m;
+    }
+}
 
 // One work-group of 256 threads per unit:
 //   1. C = sum over the unit's query heads and their n_q past queries of
@@ -67,7 +91,10 @@ constexpr double kSquatTol = 1e-12;
 //      W R^-1 with R the Cholesky factor of W^T W, from a fixed pseudo-random
 //      start, until the subspace no longer moves (the summed squared sines
 //      of the angles between two steps' subspaces below kSquatTol; kSquatIters
-//      steps at most), and one more orthonormalisation;
+//      steps at most), and one more orthonormalisation; when the iteration has
+//      not converged by then, the subspace comes from a one-sided Jacobi
+//      eigen-decomposition of C + sigma I in fp64 instead (its r columns of
+//      largest norm);
 //   3. w_c = -M_c^-1 u_c for c = d - 1 .. 0 with M_c^-1 by Sherman-Morrison;
 //   4. U and W (fp32, zero-padded to r8 columns) to the unit's coefficients.
 template <int D>
@@ -75,13 +102,20 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
     constexpr int RM = kSquatMaxRank;
     constexpr int TS = D / 16;  // Gram tile side
     constexpr int CH = 32;      // queries staged at a time
-    __shared__ __align__(16) float sa[D][D];     // C
-    __shared__ __align__(16) double sv[D][RM];   // V (the queries' staging buffer before)
-    __shared__ __align__(16) double sw[D][RM];   // W, then the w_c
+    constexpr int MS = jacobi_stride<D>();
+    // C (fp32), V and W in one pool; the Jacobi fallback's fp64 matrix M
+    // (column c at M + c MS) takes the whole pool once the iteration is over
+    constexpr int POOL_C = D * D / 2, POOL_VW = POOL_C + 2 * D * RM, POOL_M = D * MS;
+    __shared__ __align__(16) double pool[POOL_VW > POOL_M ? POOL_VW : POOL_M];
+    float(*const sa)[D] = reinterpret_cast<float(*)[D]>(pool);               // C
+    double(*const sv)[RM] = reinterpret_cast<double(*)[RM]>(pool + POOL_C);  // V (the queries' staging buffer before)
+    double(*const sw)[RM] = reinterpret_cast<double(*)[RM]>(pool + POOL_C + D * RM);  // W, then the w_c
     __shared__ double sm[RM][RM];                // W^T W and its factor, then M^-1
     __shared__ double st[RM][RM];                // V^T W (the convergence test)
     __shared__ double sz[RM];
-    static_assert(CH * D * sizeof(float) <= sizeof(sv), "the staged queries fit V's space");
+    __shared__ double snrm[D];                   // Jacobi: squared column norms
+    __shared__ int ssel[RM];                     // Jacobi: the columns of rank 0 .. r - 1
+    static_assert(CH * D * sizeof(float) <= D * RM * sizeof(double), "the staged queries fit V's space");
     const CacheGeom& g = a.g;
     const int tid = threadIdx.x;
     const int64_t u = blockIdx.x;
@@ -205,6 +239,7 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
         __syncthreads();
     };
     orthonormalize(sv);
+    bool converged = false;
     for (int it = 0; it < kSquatIters; ++it) {
         // W = (C + sigma I) V: a thread takes row c and 8 columns; C is symmetric, so its
         // column c is read (consecutive lanes, consecutive words), and the 8
@@ -246,7 +281,106 @@ __global__ __launch_bounds__(256) void squat_build_kernel(const SquatBuildArgs a
         __syncthreads();
         double f = 0.0;
         for (int i = 0; i < r; ++i) f += sz[i];
-        if ((double)r - f < kSquatTol) break;  // the subspace no longer moves (uniform)
+        if ((double)r - f < kSquatTol) {  // the subspace no longer moves (uniform)
+            converged = true;
+            break;
+        }
+        __syncthreads();
+    }
+    __syncthreads();
+    if (!converged) {
+        // 2b. One-sided Jacobi on C + sigma I, which has C's eigenvectors and
+        //     only positive eigenvalues: M = (C + sigma I) J, with J the product
+        //     of the rotations, until M's columns are mutually orthogonal; then
+        //     column c of M is (lambda_c + sigma) v_c, with v_c an eigenvector
+        //     of C, and V takes the r of largest norm, normalised.
+        double* const M = pool;
+        {
+            constexpr int PER = D * D / 256;
+            float cr[PER];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int idx = tid + 256 * e;
+                cr[e] = sa[idx / D][idx % D];
+            }
+            __syncthreads();  // C's fp32 entries are in registers; M overwrites them
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int idx = tid + 256 * e, i = idx / D, c = idx % D;
+                M[c * MS + i] = (double)cr[e] + (i == c ? sigma : 0.0);
+            }
+            __syncthreads();
+        }
+        // a round rotates D / 2 disjoint pairs; TPP consecutive lanes take a
+        // pair, lane j of them rows j, j + TPP, ... of both columns
+        constexpr int NP = D / 2, TPP = 256 / NP, RPT = D / TPP;
+        static_assert(256 % NP == 0 && (TPP & (TPP - 1)) == 0 && TPP <= 64, "a pair's lanes are a power of two in a wave");
+        const int pi = tid / TPP, j = tid % TPP;
+        for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+            int any = 0;
+            for (int k = 0; k < D - 1; ++k) {
+                int p, q;
+                jacobi_pair<D>(k, pi, p, q);
+                double mp[RPT], mq[RPT];
+                double aa = 0.0, bb = 0.0, gg = 0.0;
+#pragma unroll
+                for (int e = 0; e < RPT; ++e) {
+                    mp[e] = M[p * MS + j + TPP * e];
+                    mq[e] = M[q * MS + j + TPP * e];
+                    aa = fma(mp[e], mp[e], aa);
+                    bb = fma(mq[e], mq[e], bb);
+                    gg = fma(mp[e], mq[e], gg);
+                }
+#pragma unroll
+                for (int o = 1; o < TPP; o <<= 1) {
+                    aa += __shfl_xor(aa, o, TPP);
+                    bb += __shfl_xor(bb, o, TPP);
+                    gg += __shfl_xor(gg, o, TPP);
+                }
+                const int rot = fabs(gg) > kJacobiTol * sqrt(aa * bb);
+                if (rot) {
+                    // the rotation that zeroes m_p . m_q (Hestenes)
+                    const double zeta = (bb - aa) / (2.0 * gg);
+                    const double t = copysign(1.0, zeta) / (fabs(zeta) + sqrt(fma(zeta, zeta, 1.0)));
+                    const double cs = 1.0 / sqrt(fma(t, t, 1.0)), sn = cs * t;
+#pragma unroll
+                    for (int e = 0; e < RPT; ++e) {
+                        M[p * MS + j + TPP * e] = cs * mp[e] - sn * mq[e];
+                        M[q * MS + j + TPP * e] = sn * mp[e] + cs * mq[e];
+                    }
+                }
+                // orders this round's stores before the next round's loads
+                any |= __syncthreads_or(rot);
+            }
+            if (!any) break;  // a sweep without a rotation: uniform
+        }
+        // squared column norms; column c's rank by norm (ties by index)
+        for (int c = tid; c < D; c += 256) {
+            double n2 = 0.0;
+            for (int i = 0; i < D; ++i) n2 = fma(M[c * MS + i], M[c * MS + i], n2);
+            snrm[c] = n2;
+        }
+        __syncthreads();
+        for (int c = tid; c < D; c += 256) {
+            int rk = 0;
+            for (int c2 = 0; c2 < D; ++c2) rk += snrm[c2] > snrm[c] || (snrm[c2] == snrm[c] && c2 < c);
+            if (rk < r) ssel[rk] = c;
+        }
+        __syncthreads();
+        // V's column k = M's column ssel[k] / its norm (V overlaps M: read first)
+        constexpr int PV = D * RM / 256;
+        double vr[PV];
+#pragma unroll
+        for (int e = 0; e < PV; ++e) {
+            const int idx = tid + 256 * e, i = idx / RM, k = idx % RM;
+            vr[e] = k < r ? M[ssel[k] * MS + i] / sqrt(snrm[ssel[k]]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PV; ++e) {
+            const int idx = tid + 256 * e;
+            sv[idx / RM][idx % RM] = vr[e];
+        }
         __syncthreads();
     }
     // a second pass restores orthogonality to fp64 rounding

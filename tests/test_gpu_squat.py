@@ -268,6 +268,57 @@ def test_squat_degenerate_channels(bits):
     assert_attention_close(out.cpu().numpy(), oc.attend(q))
 
 
+@pytest.mark.parametrize("Hkv,Hq,d,bits,rank,n", [
+    (2, 8, 128, 2, 16, 100),   # 400 past queries a unit
+    (1, 4, 64, 4, 20, 75),     # d = 64, 300 past queries
+])
+def test_squat_flat_spectrum(Hkv, Hq, d, bits, rank, n):
+    """Past queries with no low-rank structure (small integers, uniform over
+    [-8, 8]): the eigenvalues of their Gram matrix fall off slowly, so 48 steps
+    of subspace iteration cannot settle on the top r directions, and the build
+    takes its Jacobi eigen-decomposition instead. Every query and every Gram
+    entry is an exact integer in fp32, so the device's Gram matrix is the
+    oracle's, and its subspace is held to the oracle's eigenvectors:
+    coefficients within 1e-4, codes valid by replay, attention within the bar."""
+    _announce("squat flat spectrum", Hkv, Hq, d, bits, rank, n)
+    B, T = 1, 400
+    group = Hq // Hkv
+    gen = torch.Generator().manual_seed(70 + d + rank)
+    qh = torch.randint(-8, 9, (B, Hq, n, d), generator=gen).half().contiguous()
+    for h in range(Hkv):
+        qu = qh[0, h * group:(h + 1) * group].reshape(-1, d).double().numpy()
+        ev = np.linalg.eigvalsh(qu.T @ qu)[::-1]
+        ratio = ev[rank] / ev[rank - 1]
+        print(f"  KV head {h}: lambda_(r+1) / lambda_r = {ratio:.4f}", flush=True)
+        # flat (the iteration's error shrinks by about ratio^2 a step) but
+        # separated (the top-r subspace is well defined)
+        assert 0.9 < ratio < 1.0 - 1e-6, ratio
+    wl = KVWorkload(B, Hkv, d, seed=80 + d, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV, squat_rank=rank)
+    cache.squat_build(qh.to(DEV), LAM)
+    cache.append(k.to(DEV), v.to(DEV))
+    cache.flush()
+    q = wl.q(Hq)
+    out = cache.attend(q.to(DEV))
+    torch.cuda.synchronize()
+    gs = _oracle_coefficients(qh, Hkv, rank, LAM)
+    for u in range(B * Hkv):
+        err = np.abs(_device_g(cache, u) - gs[u]).max()
+        print(f"  unit {u}: coefficient error {err:.3e} (largest {np.abs(gs[u]).max():.3e})", flush=True)
+        assert err <= 1e-4 * max(np.abs(gs[u]).max(), 1e-3), (u, err)
+    oc = oracle.OracleCache(B, Hkv, Hq, d, bits, max_tokens=T)
+    oc.set_squat(gs)
+    oc.append(k, v)
+    oc.flush()
+    kf = oracle.half_to_float(k).reshape(B * Hkv, T, d)
+    for u in range(B * Hkv):
+        nd, worst, od = _check_unit(cache, oc, u, u, kf[u], gs[u])
+        print(f"  unit {u}: key codes differing from the oracle's own: {od}; after the replay {nd}", flush=True)
+        assert nd <= 1e-3 * oc.state()[1] * d
+    assert_attention_close(out.cpu().numpy(), oc.attend(q))
+
+
 @pytest.mark.parametrize("span", [3, 0], ids=["three_directions", "all_zero"])
 def test_squat_rank_deficient_history(span):
     """Past queries that span fewer directions than the rank: three, or none
