@@ -271,6 +271,7 @@ def test_squat_degenerate_channels(bits):
 @pytest.mark.parametrize("Hkv,Hq,d,bits,rank,n", [
     (2, 8, 128, 2, 16, 100),   # 400 past queries a unit
     (1, 4, 64, 4, 20, 75),     # d = 64, 300 past queries
+    (1, 4, 128, 2, 32, 100),   # the largest rank
 ])
 def test_squat_flat_spectrum(Hkv, Hq, d, bits, rank, n):
     """Past queries with no low-rank structure (small integers, uniform over
