@@ -15,7 +15,10 @@ and the fused split-K decode attention over the packed cache and the fp16
 residual. `value` is the algorithmic bytes of those steps (attention reads of
 codes, scales, zeros and residual rows, query in, output out; the append and
 flush bytes) divided by the wall time of the K timed steps. Inputs are
-resident in HBM before the timed region starts.
+resident in HBM before the timed region starts. Before the W warm-up steps,
+about 50 ms of attention launches over the same caches run back to back, so
+that the timed steps see the clocks' steady state rather than the power
+manager's start-up transient.
 
 The 256 MB Infinity Cache would hold a whole llama2_7b_layer cache (147 MB),
 so steps rotate over independent caches whose total exceeds 1 GiB.
@@ -45,6 +48,9 @@ if ROOT not in sys.path:
 
 # prefill sweeps timed back to back (each cache's median counts)
 PF_REPS = 5
+# back-to-back attention launches before the warm-up steps (seconds of GPU time)
+SETTLE_S = 0.05
+SETTLE_MAX_LAUNCHES = 4000
 PEAK_HBM_GBS = 8000.0
 METRIC = "decode-attention effective HBM GB/s (% of peak) + quantize-append tokens/s"
 
@@ -233,13 +239,13 @@ def _arith_dtype(caches):
 def _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, rounds):
     """Back-to-back kivi_attend_decode launches over the caches `idx` (in
     order, `rounds` times), bracketed by one pair of HIP events on the stream
-    they run on. As many untimed launches (at least 16) go first, enqueued
-    right before the timed ones with no host wait between: after the host's
-    pause the launches run slower for some 20 ms (measured on MI355X: the
-    full stack's kernels took up to 20% longer per launch over the first four
-    rounds of its 32 caches), and the timed launches should see the steady
-    state the decode steps run in. Returns (us per launch, algorithmic bytes
-    per launch, n)."""
+    they run on. The settle launches (about 50 ms) and as many untimed
+    launches as timed ones (at least 16) go first, enqueued right before the
+    timed ones with no host wait between: after the host's pause the launches
+    run slower for some 15-20 ms (measured on MI355X: the full stack's kernels
+    took up to 20% longer per launch over the first four rounds of its 32
+    caches), and the timed launches should see the steady state the decode
+    steps run in. Returns (us per launch, algorithmic bytes per launch, n)."""
     import ctypes
 
     import torch
@@ -249,6 +255,7 @@ def _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, rounds):
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = rounds * len(idx)
+    _settle(kv, lib, [caches[i] for i in idx], qp, qd, outp, sp)
     warm = max(n, 16)
     for w in range(warm):
         rc = lib.kivi_attend_decode(handles[w % len(idx)], qp[w % len(qp)], qd, outp, sp)
@@ -263,6 +270,23 @@ def _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, rounds):
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) * 1e3 / n, sum(per) / len(per), n
+
+
+def _settle(kv, lib, caches, qp, qd, outp, sp):
+    """kivi_attend_decode over the caches in turn, back to back, for about
+    SETTLE_S of GPU time at 6 TB/s of algorithmic bytes (at most
+    SETTLE_MAX_LAUNCHES launches), with no host wait: the clocks then sit in
+    their steady state for what follows on the stream."""
+    import ctypes
+
+    handles = [ctypes.c_void_p(c.handle) for c in caches]
+    per = [cache_attend_bytes(c) for c in caches]
+    n = min(SETTLE_MAX_LAUNCHES, max(len(caches), int(SETTLE_S * 6e12 * len(per) / sum(per))))
+    for w in range(n):
+        rc = lib.kivi_attend_decode(handles[w % len(handles)], qp[w % len(qp)], qd, outp, sp)
+        if rc != 0:
+            raise kv.KiviError(rc, kv.kivi_last_error())
+    print(f"[bench] settle: {n} attention launches over {len(caches)} cache(s)", file=sys.stderr, flush=True)
 
 
 def _time_attend_single(kv, lib, caches, idx, qp, qd, outp, sp):
@@ -552,14 +576,13 @@ def main():
             if rc != 0:
                 raise kv.KiviError(rc, kv.kivi_last_error())
 
-    for i in range(args.warmup):
-        run_step(i)
-    torch.cuda.synchronize()
     # the bytes of each step follow from the host counters alone: replay the
-    # counter arithmetic before timing (checked against the caches afterwards)
+    # counter arithmetic of the warm-up and timed steps before any of them runs
+    # (so that no host pause falls between the two; checked against the caches
+    # afterwards), counting the timed steps' bytes
     bytes_total = 0
     sim_state = [row_groups(c) for c in caches]
-    for i in range(args.warmup, total_steps):
+    for i in range(total_steps):
         r = i % n_rot
         for layer in range(layers):
             ci = r * layers + layer
@@ -571,9 +594,20 @@ def main():
                     b += flush_bytes(Hkv * w, d, layer_bits[layer], 32)
                     nq, nr = nq + 32, nr - 32
                 b += attend_bytes(Hkv * w, Hq * w, d, layer_bits[layer], nq, nr)
-                bytes_total += b
+                if i >= args.warmup:
+                    bytes_total += b
                 groups.append((nt, nq, nr, w))
             sim_state[ci] = groups
+    # settle: attention launches over the caches back to back for about
+    # SETTLE_S, enqueued right before the warm-up steps. On MI355X the first
+    # ~15 ms of back-to-back work after a pause is a power-management transient
+    # (on the GQA streaming layer its launches ran 100 us for ~1.6 ms, then
+    # 121-126 us, easing back to ~103 us ~15 ms in), longer than the warm-up
+    # steps of a one-layer workload; the timed steps should see the steady
+    # state. The launches read the caches and change no state.
+    _settle(kv, lib, caches, qp, qd, outp, sp)
+    for i in range(args.warmup):
+        run_step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total_steps):
