@@ -6,7 +6,9 @@ quantize-append tokens/s.
 Default workload: the full-stack decode step (32 layers x batch 128 x 8 KV
 heads / 32 query heads x head_dim 128 x 4096 cached tokens, layers 0-15 at
 b = 2 and 16-31 at b = 4, bf16 queries), the largest configuration that fits
-one GPU; --workload picks another.
+one GPU; --workload picks another. Its line also carries the
+Llama-2-7B-shaped layer's figures (key llama2_7b_layer: the same benchmark
+of that workload, run as a child process after the full stack's).
 
 A timed step is one decode step of the whole path over one batch: append one
 token per sequence (residual ring), flush when a whole 32-token group lies
@@ -272,6 +274,31 @@ def _time_attend(kv, lib, caches, idx, qp, qd, outp, sp, out, rounds):
     return ev0.elapsed_time(ev1) * 1e3 / n, sum(per) / len(per), n
 
 
+def _side_workload(name, warmup):
+    """The benchmark of another workload, run as a child process (its own
+    caches; the parent's stay allocated but idle): the fields of its JSON line
+    that sit beside the main workload's, or the child's exit status."""
+    import subprocess
+
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-cpu-baseline",
+           "--warmup", str(warmup)]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    got = [x for x in p.stdout.splitlines() if x.startswith("{")]
+    if p.returncode != 0 or not got:
+        print(f"[bench] {name}: child run failed (exit {p.returncode})", file=sys.stderr, flush=True)
+        return {"workload": name, "error": f"exit {p.returncode}"}
+    d = json.loads(got[-1])
+    r = d["roofline"]
+    return {"workload": name, "config": d["config"], "value": d["value"], "unit": d["unit"],
+            "pct_of_peak": d["pct_of_peak"], "ms_per_step": d["ms_per_step"], "steps": d["steps"],
+            "warmup": d["warmup"], "dtype": d["dtype"],
+            "roofline": {k: r[k] for k in ("kernel", "achieved", "frac", "avg_launch_us",
+                                           "algorithmic_bytes_per_launch", "timed_launches", "traffic")},
+            "quantize_append_tokens_per_s": d["quantize_append_tokens_per_s"],
+            "quantize_append_gbs": d["quantize_append_gbs"],
+            "quantize_append_pct_of_peak": d["quantize_append_pct_of_peak"]}
+
+
 def _settle(kv, lib, caches, qp, qd, outp, sp):
     """kivi_attend_decode over the caches in turn, back to back, for about
     SETTLE_S of GPU time at 6 TB/s of algorithmic bytes (at most
@@ -471,6 +498,9 @@ def main():
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
                              "gqa_ragged", "gqa_paged", "llama2_7b_layer_squat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-workload", action="store_true",
+                    help="full_stack only: skip the Llama-2-7B-shaped layer's figures (a child run of "
+                         "--workload llama2_7b_layer) that the line otherwise carries")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="N",
                     help="for profiles of the quantizer: untimed prefills (append(T) + flush into an emptied "
@@ -766,6 +796,9 @@ def main():
         "squat": squat_line,
         "cpu_baseline": None,
     }
+    if args.workload == "full_stack" and not args.no_side_workload:
+        # the Llama-2-7B-shaped layer alongside the full stack's line
+        line["llama2_7b_layer"] = _side_workload("llama2_7b_layer", args.warmup)
     if not args.no_cpu_baseline:
         try:
             line["cpu_baseline"] = _cpu_baseline(cfg, seconds=args.cpu_seconds)
