@@ -53,7 +53,10 @@ typedef enum {
     KIVI_E_RAGGED = -8       /* the call needs every sequence to hold the same number of tokens */
 } kivi_status;
 
-/* Largest batch whose sequences may hold different numbers of tokens. */
+/* Rows per launch when the sequences of a batch hold different numbers of
+ * tokens, or the cache is paged: the rows' counters ride in the kernel
+ * arguments, so a larger batch runs as several launches of at most this many
+ * rows each. */
 #define KIVI_MAX_RAGGED_BATCH 128
 
 enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
@@ -64,8 +67,8 @@ enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
  * n_kv_heads; max_tokens >= 1; max_splits = 0 (library default, 256) or
  * 2..4096. Each sequence (batch row) keeps its own counters: kivi_append and
  * kivi_decode_step add the same number of tokens to every row, while
- * kivi_append_rows and kivi_reset_row let rows differ in length (a batch of
- * at most KIVI_MAX_RAGGED_BATCH rows then). Each row follows the same rules
+ * kivi_append_rows and kivi_reset_row let rows differ in length (such a
+ * batch runs KIVI_MAX_RAGGED_BATCH rows a launch). Each row follows the same rules
  * (residual ring, flushes) as a batch of one.
  *
  * Serving batches follow the page's Production Deployment Guide (KIVI inside a
@@ -76,7 +79,8 @@ enum { KIVI_F16 = 0, KIVI_BF16 = 1 };
  * pool of n_pages pages instead of one region per unit. A page holds one
  * key block (G tokens) of one sequence for all its KV heads, and a block
  * table that the caller owns maps (row, block) to a page; see
- * kivi_set_block_table. Requires batch <= KIVI_MAX_RAGGED_BATCH. */
+ * kivi_set_block_table. A paged cache's calls run KIVI_MAX_RAGGED_BATCH rows a
+ * launch. */
 typedef struct {
     int32_t batch;       /* B */
     int32_t n_kv_heads;  /* Hkv; a "unit" is one (batch row, KV head): unit = b * Hkv + h */
@@ -185,8 +189,7 @@ int kivi_append(kivi_cache* cache, const void* k, const void* v, int32_t ntok, v
  * tokens are its first ntok[b] of the max_ntok slots. ntok: host array of B
  * entries, each in [0, max_ntok]. For prefilling sequences of different
  * lengths, or one row (the others 0) when a new sequence takes a freed row.
- * KIVI_E_CAPACITY if a row would exceed max_tokens; KIVI_E_UNSUPPORTED if the
- * rows would differ in length with batch > KIVI_MAX_RAGGED_BATCH. */
+ * KIVI_E_CAPACITY if a row would exceed max_tokens. */
 int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int32_t* ntok, int32_t max_ntok,
                      void* stream);
 
@@ -207,8 +210,7 @@ int kivi_set_block_table(kivi_cache* cache, const int32_t* table, int32_t stride
 
 /* Empty sequence `row` (host counters only; launches nothing), so that a new
  * sequence can take the row, as a serving engine reuses a finished request's
- * slot (the page's Production Deployment Guide, vLLM with KIVI). KIVI_E_UNSUPPORTED if the rows would then differ
- * in length with batch > KIVI_MAX_RAGGED_BATCH. */
+ * slot (the page's Production Deployment Guide, vLLM with KIVI). */
 int kivi_reset_row(kivi_cache* cache, int32_t row);
 
 /* Quantize, in every row, the oldest floor((n_resid - R) / G) * G residual
@@ -265,8 +267,10 @@ int kivi_squat_build(kivi_cache* cache, const void* q, int32_t q_dtype, int32_t 
  * device scratch of KIVI_NOALLOC_SCRATCH_BYTES instead of the cache's
  * partial region. Calls no hipMalloc or other allocating routine; its first
  * call on a device looks up that device's scratch address. KIVI_E_NOMEM
- * (before any launch) when batch * n_q_heads * n_split * partial_stride
- * exceeds the scratch (a plan of one split needs none). Every call on one
+ * (before any launch) when a launch's rows * n_q_heads * n_split *
+ * partial_stride exceeds the scratch (rows: the batch, or at most
+ * KIVI_MAX_RAGGED_BATCH when the call runs several launches, which reuse the
+ * scratch in stream order; a plan of one split needs none). Every call on one
  * GPU shares that GPU's scratch, which holds the last call's partials:
  * calls that overlap on one GPU (other streams, other threads) race. */
 int kivi_attend_decode_noalloc(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream);
@@ -301,7 +305,8 @@ int kivi_plan_append(const kivi_cache* cache, int32_t ntok, kivi_state* after);
  * its merge are this library's design, not on the pages): *n_split work-groups per
  * (unit, query-head chunk) along the tokens (the last also takes the fp16
  * residual; with more than one, a merge kernel follows), and about
- * *blocks_per_split key blocks in each. */
+ * *blocks_per_split key blocks in each. When the call runs several launches
+ * (KIVI_MAX_RAGGED_BATCH rows each), the plan of the one with the most splits. */
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split);
 
 /* Force the split count of kivi_attend_decode (not on the pages, as

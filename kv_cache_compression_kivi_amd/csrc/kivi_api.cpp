@@ -14,7 +14,7 @@
 #include "launch.hpp"
 #include "planner.hpp"
 
-static_assert(kivi::kMaxRaggedRows == KIVI_MAX_RAGGED_BATCH, "row tables hold the largest ragged batch");
+static_assert(kivi::kMaxRaggedRows == KIVI_MAX_RAGGED_BATCH, "a row table holds the rows of one launch");
 // the row tables ride in the kernel arguments, whose block is at most 4 KiB
 static_assert(sizeof(kivi::QuantArgs) <= 4096 && sizeof(kivi::RingArgs) <= 4096 && sizeof(kivi::AttendArgs) <= 4096,
               "kernel arguments fit the 4 KiB argument block");
@@ -82,6 +82,28 @@ kivi::CacheGeom geom(const kivi_cache* c) {
 
 bool paged(const kivi_cache* c) { return c->cfg.n_pages > 0; }
 
+// Rows [r0, r0 + n) of the cache as a batch of their own: every per-unit
+// region (key blocks unless paged, ring, split partials, SQuat coefficients)
+// and the block table start at row r0. Launches that carry a row table cover
+// at most kMaxRaggedRows rows, so larger batches run as several of them.
+kivi::CacheGeom chunk_geom(const kivi_cache* c, int r0, int n) {
+    kivi::CacheGeom g = geom(c);
+    const size_t u0 = (size_t)r0 * (size_t)c->cfg.n_kv_heads;
+    if (!paged(c)) g.off_blocks += u0 * g.unit_stride;
+    g.off_ring += u0 * g.ring_unit_stride;
+    g.partial += (size_t)r0 * (size_t)c->cfg.n_q_heads * (size_t)g.partial_splits * g.partial_stride;
+    g.off_squat += u0 * 2 * (size_t)g.head_dim * (size_t)g.squat_r8 * sizeof(float);
+    if (g.table) g.table += (size_t)r0 * (size_t)g.table_stride;
+    g.batch = n;
+    return g;
+}
+
+// Input rows of units [r0 Hkv, ...): `per_unit` elements of 16 bits per unit.
+const void* rows_from(const void* p, int r0, int64_t units_per_row, int64_t per_unit) {
+    return p ? static_cast<const void*>(static_cast<const uint16_t*>(p) + (size_t)r0 * units_per_row * per_unit)
+             : nullptr;
+}
+
 // A paged cache's calls need the block table.
 int check_table(const kivi_cache* c) {
     if (paged(c) && !c->table) return fail(KIVI_E_INVAL, "paged cache without a block table (kivi_set_block_table)");
@@ -111,15 +133,6 @@ int64_t max_of(const std::vector<int64_t>& x) {
     return m;
 }
 
-// Batches whose sequences differ in length pass per-row counters with the
-// kernel arguments, which bounds their batch size.
-int check_ragged_batch(const kivi_cache* c) {
-    if (c->cfg.batch > kivi::kMaxRaggedRows)
-        return fail(KIVI_E_UNSUPPORTED, "sequences of different lengths need batch <= " +
-                                            std::to_string(kivi::kMaxRaggedRows) + " (batch is " +
-                                            std::to_string(c->cfg.batch) + ")");
-    return KIVI_OK;
-}
 
 // Per-row work of one append or flush: quantize key blocks [j0, j1) with
 // tokens below ring_end read from the ring (the rest from input rows t -
@@ -135,47 +148,51 @@ bool work_ragged(const RowWork& w) {
              all_same(w.in_t0));
 }
 
-// The launches of one append or flush (ntok input rows per unit in k and v).
-// The quantization goes first: its ring reads must see the slots before this
-// call's writes.
-int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, int64_t ntok, hipStream_t s) {
-    const int B = c->cfg.batch;
-    const bool ragged = work_ragged(w);
+// The launches of one append or flush over rows [r0, r0 + n) (ntok input
+// rows per unit in k and v, which start at row 0), with row tables when
+// `ragged`. The quantization goes first: its ring reads must see the slots
+// before this call's writes.
+int launch_work_rows(kivi_cache* c, const RowWork& w, int r0, int n, bool ragged, const void* k, const void* v,
+                     int64_t ntok, hipStream_t s) {
+    const int64_t hkv = c->cfg.n_kv_heads, per_unit = ntok * c->cfg.head_dim;
     int64_t nblk = 0, ntk = 0;
-    for (int b = 0; b < B; ++b) {
+    for (int b = r0; b < r0 + n; ++b) {
         nblk = w.j1[b] - w.j0[b] > nblk ? w.j1[b] - w.j0[b] : nblk;
         ntk = w.t1[b] - w.t0[b] > ntk ? w.t1[b] - w.t0[b] : ntk;
     }
+    const kivi::CacheGeom g = chunk_geom(c, r0, n);
+    const auto* kr = static_cast<const uint16_t*>(rows_from(k, r0, hkv, per_unit));
+    const auto* vr = static_cast<const uint16_t*>(rows_from(v, r0, hkv, per_unit));
     // Rows that agree, and no quantized token read from the ring (a prefill
     // into an empty residual, say): the ring copy joins the quantize launch,
     // as nothing the launch (or the key coder after it) reads is a ring slot
     // the copy writes.
-    const bool fuse_ring = !ragged && nblk > 0 && ntk > 0 && w.ring_end[0] <= w.j0[0] * c->cfg.k_block;
+    const bool fuse_ring = !ragged && nblk > 0 && ntk > 0 && w.ring_end[r0] <= w.j0[r0] * c->cfg.k_block;
     if (nblk > 0) {
         kivi::QuantArgs a;
-        a.g = geom(c);
-        a.k = static_cast<const uint16_t*>(k);
-        a.v = static_cast<const uint16_t*>(v);
+        a.g = g;
+        a.k = kr;
+        a.v = vr;
         a.ntok = ntok;
-        a.ring_t0 = fuse_ring ? w.t0[0] : 0;
-        a.ring_t1 = fuse_ring ? w.t1[0] : 0;
-        a.ring_in_t0 = fuse_ring ? w.in_t0[0] : 0;
-        a.ring_wgs = fuse_ring ? (int32_t)((w.t1[0] - w.t0[0] + 7) / 8) : 0;
+        a.ring_t0 = fuse_ring ? w.t0[r0] : 0;
+        a.ring_t1 = fuse_ring ? w.t1[r0] : 0;
+        a.ring_in_t0 = fuse_ring ? w.in_t0[r0] : 0;
+        a.ring_wgs = fuse_ring ? (int32_t)((w.t1[r0] - w.t0[r0] + 7) / 8) : 0;
         a.rows.n = 0;
         if (ragged) {
             a.j0 = 0;
             a.j1 = nblk;
             a.ring_end = 0;
-            a.rows.n = B;
-            for (int b = 0; b < B; ++b) {
-                a.rows.j0[b] = (int32_t)w.j0[b];
-                a.rows.j1[b] = (int32_t)w.j1[b];
-                a.rows.ring_end[b] = (int32_t)w.ring_end[b];
+            a.rows.n = n;
+            for (int b = 0; b < n; ++b) {
+                a.rows.j0[b] = (int32_t)w.j0[r0 + b];
+                a.rows.j1[b] = (int32_t)w.j1[r0 + b];
+                a.rows.ring_end[b] = (int32_t)w.ring_end[r0 + b];
             }
         } else {
-            a.j0 = w.j0[0];
-            a.j1 = w.j1[0];
-            a.ring_end = w.ring_end[0];
+            a.j0 = w.j0[r0];
+            a.j1 = w.j1[r0];
+            a.ring_end = w.ring_end[r0];
         }
         hipError_t e = kivi::launch_quantize(a, s);
         if (e != hipSuccess) return device_fail(c, "quantize launch", e);
@@ -188,28 +205,42 @@ int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, i
     }
     if (ntk > 0 && !fuse_ring) {
         kivi::RingArgs a;
-        a.g = geom(c);
-        a.k = static_cast<const uint16_t*>(k);
-        a.v = static_cast<const uint16_t*>(v);
+        a.g = g;
+        a.k = kr;
+        a.v = vr;
         a.ntok = ntok;
         a.rows.n = 0;
         if (ragged) {
             a.t0 = 0;
             a.t1 = ntk;
             a.in_t0 = 0;
-            a.rows.n = B;
-            for (int b = 0; b < B; ++b) {
-                a.rows.t0[b] = (int32_t)w.t0[b];
-                a.rows.t1[b] = (int32_t)(w.t1[b] > w.t0[b] ? w.t1[b] : w.t0[b]);
-                a.rows.in_t0[b] = (int32_t)w.in_t0[b];
+            a.rows.n = n;
+            for (int b = 0; b < n; ++b) {
+                a.rows.t0[b] = (int32_t)w.t0[r0 + b];
+                a.rows.t1[b] = (int32_t)(w.t1[r0 + b] > w.t0[r0 + b] ? w.t1[r0 + b] : w.t0[r0 + b]);
+                a.rows.in_t0[b] = (int32_t)w.in_t0[r0 + b];
             }
         } else {
-            a.t0 = w.t0[0];
-            a.t1 = w.t1[0];
-            a.in_t0 = w.in_t0[0];
+            a.t0 = w.t0[r0];
+            a.t1 = w.t1[r0];
+            a.in_t0 = w.in_t0[r0];
         }
         hipError_t e = kivi::launch_ring_write(a, s);
         if (e != hipSuccess) return device_fail(c, "ring write launch", e);
+    }
+    return KIVI_OK;
+}
+
+// The launches of one append or flush: one set over the whole batch when the
+// rows' work agrees, else one per kMaxRaggedRows rows, each with row tables
+// (different units, so their order does not matter).
+int launch_work(kivi_cache* c, const RowWork& w, const void* k, const void* v, int64_t ntok, hipStream_t s) {
+    const int B = c->cfg.batch;
+    if (!work_ragged(w)) return launch_work_rows(c, w, 0, B, false, k, v, ntok, s);
+    for (int r0 = 0; r0 < B; r0 += kivi::kMaxRaggedRows) {
+        const int n = B - r0 < kivi::kMaxRaggedRows ? B - r0 : kivi::kMaxRaggedRows;
+        const int rc = launch_work_rows(c, w, r0, n, true, k, v, ntok, s);
+        if (rc != KIVI_OK) return rc;
     }
     return KIVI_OK;
 }
@@ -246,22 +277,31 @@ int validate_q(const void* q, int32_t q_dtype, const float* out) {
     return KIVI_OK;
 }
 
-// The split plan; *cost_max receives the costliest row's cost (rows that differ).
-// No heap allocation: rows that differ number at most kMaxRaggedRows.
-kivi::AttendPlan attend_plan(const kivi_cache* c, int64_t* cost_max = nullptr) {
-    const int B = c->cfg.batch;
+// Whether attention launches carry a row table: paged blocks, or rows that
+// differ in length (then kMaxRaggedRows rows a launch).
+bool attend_rows_table(const kivi_cache* c) { return paged(c) || !rows_agree(c); }
+
+// The split plan of the launch over rows [r0, r0 + n) (the whole batch when
+// no row table is needed); *cost_max receives the costliest row's cost.
+// No heap allocation: a launch with a row table covers at most
+// kMaxRaggedRows rows.
+kivi::AttendPlan attend_plan(const kivi_cache* c, int r0, int n, int64_t* cost_max = nullptr) {
     const int32_t group = c->cfg.n_q_heads / c->cfg.n_kv_heads;
     const int64_t G = c->cfg.k_block;
-    if (rows_agree(c) && !paged(c)) {  // paged caches launch with a row table
+    if (!attend_rows_table(c)) {
         if (cost_max) *cost_max = kivi::unit_cost(c->nq[0] / G, c->nt[0] - c->nq[0]);
-        return kivi::plan_attend((int64_t)B * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
+        return kivi::plan_attend((int64_t)c->cfg.batch * c->cfg.n_kv_heads, group, c->cfg.head_dim, c->nq[0] / G,
                                  c->L.max_splits, c->forced_splits, c->cus);
     }
     int64_t cost[kivi::kMaxRaggedRows];
-    for (int b = 0; b < B; ++b) cost[b] = kivi::unit_cost(c->nq[b] / G, c->nt[b] - c->nq[b]);
+    int64_t nq_max = 0;
+    for (int b = 0; b < n; ++b) {
+        cost[b] = kivi::unit_cost(c->nq[r0 + b] / G, c->nt[r0 + b] - c->nq[r0 + b]);
+        nq_max = c->nq[r0 + b] > nq_max ? c->nq[r0 + b] : nq_max;
+    }
     int64_t cm = 1;
-    kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, B, cost,
-                                                max_of(c->nq) / G, c->L.max_splits, c->forced_splits, c->cus, &cm);
+    kivi::AttendPlan p = kivi::plan_attend_rows(c->cfg.n_kv_heads, group, c->cfg.head_dim, n, cost, nq_max / G,
+                                                c->L.max_splits, c->forced_splits, c->cus, &cm);
     if (cost_max) *cost_max = cm;
     return p;
 }
@@ -273,60 +313,91 @@ struct PartialBuf {
     int32_t splits;
 };
 
-// The attention launch over the counters of the handle. With k_new / v_new,
-// the newest token of each row for which appended[b] holds (its token n_t - 1)
+// The attention launch over rows [r0, r0 + n) with the counters of the
+// handle (q, out, k_new and v_new start at row 0). With k_new / v_new, the
+// newest token of each row for which appended[b] holds (its token n_t - 1)
 // was appended by this call and is not in the ring yet. No heap allocation.
-int attend_call(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
-                const void* v_new, const char* appended, const kivi::AttendPlan& p, int64_t cost_max,
-                PartialBuf pb = {nullptr, 0}) {
-    const int B = cache->cfg.batch;
+int attend_call(kivi_cache* cache, int r0, int n, const void* q, int32_t q_dtype, float* out, void* stream,
+                const void* k_new, const void* v_new, const char* appended, const kivi::AttendPlan& p,
+                int64_t cost_max, PartialBuf pb = {nullptr, 0}) {
+    const int64_t hq = cache->cfg.n_q_heads, hkv = cache->cfg.n_kv_heads, d = cache->cfg.head_dim;
     kivi::AttendArgs a;
-    a.g = geom(cache);
+    a.g = chunk_geom(cache, r0, n);
     if (pb.base) {
         a.g.partial = pb.base;
         a.g.partial_splits = pb.splits;
     }
-    a.q = static_cast<const uint16_t*>(q);
+    a.q = static_cast<const uint16_t*>(rows_from(q, r0, hq, d));
     a.q_bf16 = q_dtype == KIVI_BF16;
-    a.out = out;
+    a.out = out + (size_t)r0 * hq * d;
     a.n_split = p.n_split;
     a.qg = p.qg;
     a.nwaves = p.nwaves;
-    a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)cache->cfg.head_dim));
-    a.k_new = static_cast<const uint16_t*>(k_new);
-    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)d));
+    a.k_new = static_cast<const uint16_t*>(rows_from(k_new, r0, hkv, d));
+    a.v_new = static_cast<const uint16_t*>(rows_from(v_new, r0, hkv, d));
     auto t_new = [&](int b) -> int64_t { return appended && appended[b] ? cache->nt[b] - 1 : -1; };
-    bool t_same = true;
-    for (int b = 1; b < B && t_same; ++b) t_same = t_new(b) == t_new(0);
     a.rows.n = 0;
     a.cost_max = cost_max;
     // paged blocks are read by the kernels built with a row table
-    if (!paged(cache) && rows_agree(cache) && t_same) {
+    if (!attend_rows_table(cache)) {
+        // rows that agree (an appended token then lands in every row alike)
         a.n_tokens = cache->nt[0];
         a.n_quant = cache->nq[0];
         a.n_blocks = cache->nq[0] / cache->cfg.k_block;
         a.t_new = t_new(0);
     } else {
-        // rows that differ (or per-row appended tokens): at most kMaxRaggedRows rows
-        a.n_tokens = max_of(cache->nt);
-        a.n_quant = max_of(cache->nq);
-        a.n_blocks = a.n_quant / cache->cfg.k_block;
-        a.t_new = -1;
-        a.rows.n = B;
+        int64_t nt_max = 0, nq_max = 0;
         int64_t cost[kivi::kMaxRaggedRows];
-        for (int b = 0; b < B; ++b) {
-            a.rows.n_tokens[b] = (int32_t)cache->nt[b];
-            a.rows.n_quant[b] = (int32_t)cache->nq[b];
-            a.rows.t_new[b] = (int32_t)t_new(b);
+        a.rows.n = n;
+        for (int b = 0; b < n; ++b) {
+            const int gb = r0 + b;
+            nt_max = cache->nt[gb] > nt_max ? cache->nt[gb] : nt_max;
+            nq_max = cache->nq[gb] > nq_max ? cache->nq[gb] : nq_max;
+            a.rows.n_tokens[b] = (int32_t)cache->nt[gb];
+            a.rows.n_quant[b] = (int32_t)cache->nq[gb];
+            a.rows.t_new[b] = (int32_t)t_new(gb);
             a.rows.order[b] = b;
-            cost[b] = kivi::unit_cost(cache->nq[b] / cache->cfg.k_block, cache->nt[b] - cache->nq[b]);
+            cost[b] = kivi::unit_cost(cache->nq[gb] / cache->cfg.k_block, cache->nt[gb] - cache->nq[gb]);
         }
+        a.n_tokens = nt_max;
+        a.n_quant = nq_max;
+        a.n_blocks = nq_max / cache->cfg.k_block;
+        a.t_new = -1;
         // costliest rows first: their work-groups start in the first round
-        std::stable_sort(a.rows.order, a.rows.order + B, [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+        std::stable_sort(a.rows.order, a.rows.order + n, [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
     }
     (void)hipGetLastError();
     hipError_t e = kivi::launch_attend(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(cache, "attend launch", e);
+    return KIVI_OK;
+}
+
+// Rows per attention launch: the whole batch, or kMaxRaggedRows with a row table.
+int attend_chunk_rows(const kivi_cache* c) {
+    return attend_rows_table(c) ? kivi::kMaxRaggedRows : c->cfg.batch;
+}
+
+// Bytes of split partials that the launch over n rows with plan p writes.
+uint64_t partial_need(const kivi_cache* c, int n, const kivi::AttendPlan& p) {
+    return (uint64_t)n * (uint64_t)c->cfg.n_q_heads * (uint64_t)p.n_split * (uint64_t)c->L.partial_stride;
+}
+
+// Every attention launch of one call, in row order. With `scratch`, each
+// launch that splits writes its partials there (launches on one stream run
+// in order, so each may reuse it); the caller has checked that they fit.
+int attend_all(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream, const void* k_new,
+               const void* v_new, const char* appended, uint8_t* scratch) {
+    const int B = cache->cfg.batch, step = attend_chunk_rows(cache);
+    for (int r0 = 0; r0 < B; r0 += step) {
+        const int n = B - r0 < step ? B - r0 : step;
+        int64_t cost_max = 1;
+        const kivi::AttendPlan p = attend_plan(cache, r0, n, &cost_max);
+        PartialBuf pb = {nullptr, 0};
+        if (scratch && p.n_split > 1) pb = {scratch, p.n_split};
+        const int rc = attend_call(cache, r0, n, q, q_dtype, out, stream, k_new, v_new, appended, p, cost_max, pb);
+        if (rc != KIVI_OK) return rc;
+    }
     return KIVI_OK;
 }
 
@@ -449,14 +520,8 @@ int kivi_reset_row(kivi_cache* cache, int32_t row) {
     if (cache->poisoned) return fail(KIVI_E_STATE, "cache saw an earlier device failure; reset it");
     int rc = check_row(cache, row);
     if (rc != KIVI_OK) return rc;
-    const int64_t nt = cache->nt[row], nq = cache->nq[row];
     cache->nt[row] = 0;
     cache->nq[row] = 0;
-    if (!rows_agree(cache) && (rc = check_ragged_batch(cache)) != KIVI_OK) {
-        cache->nt[row] = nt;
-        cache->nq[row] = nq;
-        return rc;
-    }
     return KIVI_OK;
 }
 
@@ -533,8 +598,6 @@ int kivi_append_rows(kivi_cache* cache, const void* k, const void* v, const int3
     }
     std::vector<int64_t> nt1(B), nq1(B);
     const RowWork w = plan_rows(cache, ntok, nt1, nq1);
-    if ((work_ragged(w) || !(all_same(nt1) && all_same(nq1))) && (rc = check_ragged_batch(cache)) != KIVI_OK)
-        return rc;
     (void)hipGetLastError();
     rc = launch_work(cache, w, k, v, max_ntok, static_cast<hipStream_t>(stream));
     if (rc != KIVI_OK) return rc;
@@ -570,7 +633,13 @@ int kivi_flush(kivi_cache* cache, void* stream, int32_t* n_flushed) {
 
 int kivi_plan_attend(const kivi_cache* cache, int32_t* n_split, int32_t* blocks_per_split) {
     if (!cache) return fail(KIVI_E_INVAL, "cache handle is NULL");
-    kivi::AttendPlan p = attend_plan(cache);
+    // the launch with the most splits, when the call runs several
+    const int B = cache->cfg.batch, step = attend_chunk_rows(cache);
+    kivi::AttendPlan p = attend_plan(cache, 0, B < step ? B : step);
+    for (int r0 = step; r0 < B; r0 += step) {
+        const kivi::AttendPlan q = attend_plan(cache, r0, B - r0 < step ? B - r0 : step);
+        if (q.n_split > p.n_split) p = q;
+    }
     if (n_split) *n_split = p.n_split;
     if (blocks_per_split) *blocks_per_split = p.blocks_per_split;
     return KIVI_OK;
@@ -609,34 +678,36 @@ int kivi_squat_build(kivi_cache* cache, const void* q, int32_t q_dtype, int32_t 
 int kivi_attend_decode(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
     int rc = check_attend(cache, q, q_dtype, out);
     if (rc != KIVI_OK) return rc;
-    int64_t cost_max = 1;
-    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
-    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, p, cost_max);
+    return attend_all(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, nullptr);
 }
 
 int kivi_attend_decode_noalloc(kivi_cache* cache, const void* q, int32_t q_dtype, float* out, void* stream) {
     int rc = check_attend(cache, q, q_dtype, out);
     if (rc != KIVI_OK) return rc;
-    int64_t cost_max = 1;
-    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
-    PartialBuf pb = {nullptr, 0};
-    if (p.n_split > 1) {
-        // the partials of this call, n_split slots per query head, in the library's static scratch
-        const uint64_t need = (uint64_t)cache->cfg.batch * (uint64_t)cache->cfg.n_q_heads * (uint64_t)p.n_split *
-                              (uint64_t)cache->L.partial_stride;
+    // the partials of each launch, n_split slots per query head of its rows,
+    // in the library's static scratch: every launch's must fit (checked
+    // before any launch)
+    const int B = cache->cfg.batch, step = attend_chunk_rows(cache);
+    bool splits = false;
+    for (int r0 = 0; r0 < B; r0 += step) {
+        const int n = B - r0 < step ? B - r0 : step;
+        const kivi::AttendPlan p = attend_plan(cache, r0, n);
+        if (p.n_split <= 1) continue;
+        splits = true;
+        const uint64_t need = partial_need(cache, n, p);
         if (need > (uint64_t)KIVI_NOALLOC_SCRATCH_BYTES)
-            return fail(KIVI_E_NOMEM, "split partials of " + std::to_string(need) + " bytes (batch * n_q_heads * " +
-                                          std::to_string(p.n_split) + " splits * " +
+            return fail(KIVI_E_NOMEM, "split partials of " + std::to_string(need) + " bytes (" + std::to_string(n) +
+                                          " rows * n_q_heads * " + std::to_string(p.n_split) + " splits * " +
                                           std::to_string(cache->L.partial_stride) +
                                           ") exceed the static scratch of " +
                                           std::to_string((uint64_t)KIVI_NOALLOC_SCRATCH_BYTES) + " bytes");
-        void* ptr = nullptr;
+    }
+    void* ptr = nullptr;
+    if (splits) {
         hipError_t e = kivi::static_scratch(&ptr);
         if (e != hipSuccess) return fail(KIVI_E_DEVICE, std::string("static scratch: ") + hipGetErrorString(e));
-        pb.base = static_cast<uint8_t*>(ptr);
-        pb.splits = p.n_split;
     }
-    return attend_call(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, p, cost_max, pb);
+    return attend_all(cache, q, q_dtype, out, stream, nullptr, nullptr, nullptr, static_cast<uint8_t*>(ptr));
 }
 
 int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void* q, int32_t q_dtype, float* out,
@@ -679,9 +750,7 @@ int kivi_decode_step(kivi_cache* cache, const void* k, const void* v, const void
     cache->nt = nt1;
     cache->nq = nq1;
     if (n_flushed) *n_flushed = (int32_t)fmax;
-    int64_t cost_max = 1;
-    const kivi::AttendPlan p = attend_plan(cache, &cost_max);
-    return attend_call(cache, q, q_dtype, out, stream, k, v, appended.data(), p, cost_max);
+    return attend_all(cache, q, q_dtype, out, stream, k, v, appended.data(), nullptr);
 }
 
 }  // extern "C"

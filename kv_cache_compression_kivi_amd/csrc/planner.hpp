@@ -70,10 +70,6 @@ inline int validate_config(const kivi_config* c, std::string& err) {
         err = "n_pages must be >= 0";
         return KIVI_E_INVAL;
     }
-    if (c->n_pages > 0 && c->batch > KIVI_MAX_RAGGED_BATCH) {
-        err = "paged blocks need batch <= " + std::to_string(KIVI_MAX_RAGGED_BATCH);
-        return KIVI_E_UNSUPPORTED;
-    }
     if (c->squat_rank < 0) {
         err = "squat_rank must be >= 0";
         return KIVI_E_INVAL;

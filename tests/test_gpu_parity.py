@@ -618,15 +618,17 @@ def test_paged_blocks_parity(B, Hkv, Hq, d, bits, R, lens):
     assert e.value.status == "KIVI_E_INVAL"
 
 
-@pytest.mark.parametrize("B,bits,t_max,paged", [(40, 2, 700, False), (128, 4, 300, False), (40, 2, 500, True)],
-                         ids=["40rows_b2", "128rows_b4", "40rows_b2_paged"])
+@pytest.mark.parametrize("B,bits,t_max,paged", [(40, 2, 700, False), (128, 4, 300, False), (40, 2, 500, True),
+                                                 (300, 2, 200, False), (200, 4, 160, True)],
+                         ids=["40rows_b2", "128rows_b4", "40rows_b2_paged", "300rows_b2", "200rows_b4_paged"])
 def test_large_ragged_batch_parity(B, bits, t_max, paged):
     """Serving batches with many rows of different lengths on the four-query
-    kernel: 40 rows and 128 (the largest row table) of 8 KV heads, 320 and
-    1024 units, more work-groups than one round over the CUs. Attention at
-    splits 0, 1 and 3 with bf16 queries, then decode steps whose appended
-    tokens the work-groups write to the ring. Every row against an oracle
-    cache of that row alone, bytes exact at the end."""
+    kernel: 40 rows, 128 (one full row table), and 300 and 200 (paged), which
+    run as several launches of at most 128 rows; 8 KV heads, 320 to 2400
+    units, more work-groups than one round over the CUs. Attention at splits
+    0, 1 and 3 with bf16 queries, then decode steps whose appended tokens the
+    work-groups write to the ring. Every row against an oracle cache of that
+    row alone, bytes exact at the end."""
     Hkv, Hq, d, R = 8, 32, 128, 128
     rng = np.random.default_rng(B + bits)
     lens = [int(x) for x in rng.integers(1, t_max + 1, B)]

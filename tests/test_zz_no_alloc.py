@@ -103,6 +103,31 @@ def test_noalloc_on_paged_rows(Hq):
         assert_attention_close(got[b:b + 1], oc.attend(q[b:b + 1]))
 
 
+def test_noalloc_beyond_one_row_table():
+    """150 rows of different lengths: the call runs two launches (128 rows,
+    then 22), whose split partials take the scratch in turn, in stream order.
+    Bit for bit against kivi_attend_decode, twice in a row, and a sample of
+    rows against oracle caches of those rows alone."""
+    print("\n[case] noalloc 150 ragged rows: kv2 q8 d128 b2 splits 3", flush=True)
+    B, Hkv, Hq, d, bits = 150, 2, 8, 128, 2
+    rng = np.random.default_rng(45)
+    lens = [int(x) for x in rng.integers(1, 300, B)]
+    T = max(lens)
+    wl = KVWorkload(B, Hkv, d, seed=45, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=T, device=DEV)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    cache.set_attend_splits(3)
+    q = wl.q(Hq)
+    for _ in range(2):
+        ref, got = _both(cache, q.to(DEV))
+        assert np.array_equal(ref.view(np.uint32), got.view(np.uint32))
+    for b in (0, 127, 128, 149):
+        oc = oracle.OracleCache(1, Hkv, Hq, d, bits, max_tokens=T)
+        oc.append(k[b:b + 1, :, :lens[b]].contiguous(), v[b:b + 1, :, :lens[b]].contiguous())
+        assert_attention_close(got[b:b + 1], oc.attend(q[b:b + 1]))
+
+
 def test_noalloc_refuses_partials_beyond_the_scratch():
     print("\n[case] noalloc too large: B64 kv8 q32 d128 splits 256", flush=True)
     B, Hkv, Hq, d = 64, 8, 32, 128
