@@ -496,7 +496,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="full_stack",
                     choices=["tiny", "llama2_7b_layer", "long_context", "gqa_streaming", "full_stack",
-                             "gqa_ragged", "gqa_paged", "llama2_7b_layer_squat"])
+                             "gqa_ragged", "gqa_paged", "gqa_paged_256", "llama2_7b_layer_squat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side-workload", action="store_true",
                     help="full_stack only: skip the Llama-2-7B-shaped layer's figures (a child run of "

@@ -157,4 +157,9 @@ CONFIGS = {
     # shared pool, taken in a random order.
     "gqa_paged": dict(batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=6,
                       ragged=(512, 8192), paged=True),
+    # A serving batch of 256 sequences with the same length mix, paged: more
+    # rows than one launch's row table holds (128), so each call runs two
+    # launches.
+    "gqa_paged_256": dict(batch=256, n_kv_heads=8, n_q_heads=32, head_dim=128, T=8192, bits=2, seed=7,
+                          ragged=(512, 8192), paged=True),
 }
