@@ -88,3 +88,37 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "measures one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_side_workload_line(monkeypatch):
+    """The default line's llama2_7b_layer entry: the child's JSON line (its
+    last line starting with '{', after any progress output) reduced to the
+    fields that sit beside the main workload's; a failed child gives an
+    error entry, and the main line still prints."""
+    import json
+
+    child = {"metric": bench.METRIC, "value": 5250.3, "unit": "GB/s", "pct_of_peak": 65.63, "ms_per_step": 0.028,
+             "steps": 200, "warmup": 5, "dtype": "f32", "config": {"workload": "llama2_7b_layer"},
+             "quantize_append_tokens_per_s": 2.7e8, "quantize_append_gbs": 5613.5,
+             "quantize_append_pct_of_peak": 70.2,
+             "roofline": {"kernel": "attend_kernel", "achieved": 5295.3, "frac": 0.6619, "avg_launch_us": 28.4,
+                          "algorithmic_bytes_per_launch": 150355968, "timed_launches": 200, "traffic": None,
+                          "bound": "hbm", "peak": 8000.0}}
+    calls = []
+
+    def fake_run(cmd, stdout=None, text=None, timeout=None):
+        calls.append(cmd)
+        return subprocess.CompletedProcess(cmd, 0, stdout="progress\n" + json.dumps(child) + "\n")
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    got = bench._side_workload("llama2_7b_layer", 7)
+    assert calls and calls[0][-4:] == ["llama2_7b_layer", "--no-cpu-baseline", "--warmup", "7"]
+    assert got["workload"] == "llama2_7b_layer" and got["pct_of_peak"] == 65.63
+    assert got["roofline"]["frac"] == 0.6619 and "bound" not in got["roofline"]
+    assert got["quantize_append_pct_of_peak"] == 70.2
+
+    def failing_run(cmd, stdout=None, text=None, timeout=None):
+        return subprocess.CompletedProcess(cmd, 1, stdout="")
+
+    monkeypatch.setattr(subprocess, "run", failing_run)
+    assert bench._side_workload("llama2_7b_layer", 7) == {"workload": "llama2_7b_layer", "error": "exit 1"}
