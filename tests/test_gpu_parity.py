@@ -671,6 +671,41 @@ def test_large_ragged_batch_parity(B, bits, t_max, paged):
     _check_bytes(cache, ocs)
 
 
+def test_mha_batch_beyond_one_row_table():
+    """The MHA vector kernel and the quantizer on 140 rows of different
+    lengths (launches of 128 and 12 rows), d = 64, b = 4, R = 32 so that the
+    decode steps' flushes fall on different steps per row and in both
+    launches: a ragged prefill (some rows empty), then 8 decode steps at
+    splits 0 and 3 alternately. Every row against an oracle cache of that row
+    alone after every step, bytes exact at the end."""
+    B, Hkv, Hq, d, bits, R, steps = 140, 2, 2, 64, 4, 32, 8
+    rng = np.random.default_rng(140)
+    lens = [int(x) for x in rng.integers(0, 200, B)]
+    lens[0], lens[127], lens[128] = 199, 0, 64  # the launches' first and last rows
+    _announce("mha beyond one row table", B, Hkv, Hq, d, bits, R)
+    T = max(lens)
+    max_tokens = T + steps + 8
+    wl = KVWorkload(B, Hkv, d, seed=140, device="cpu")
+    k, v = wl.kv(0, T)
+    cache = kv.KiviCache(B, Hkv, Hq, d, bits, max_tokens=max_tokens, residual=R, device=DEV)
+    cache.append_rows(k.to(DEV), v.to(DEV), lens)
+    ocs = _row_oracles(k, v, lens, Hq, bits, max_tokens, R)
+    # attention needs a token in every row: the first decode step brings one to the empty rows
+    for i in range(steps):
+        kt, vt = wl.kv(T + i, 1)
+        qi = wl.q(Hq, step=i)
+        cache.set_attend_splits(3 if i % 2 else 0)
+        out = cache.decode_step(kt.to(DEV), vt.to(DEV), qi.to(DEV))
+        for b, oc in enumerate(ocs):
+            oc.append(kt[b:b + 1].contiguous(), vt[b:b + 1].contiguous())
+            nt, nq = oc.state()
+            if nt - nq >= R + 32:
+                oc.flush()
+        torch.cuda.synchronize()
+        _check_rows(cache, ocs, out, qi)
+    _check_bytes(cache, ocs)
+
+
 @pytest.mark.parametrize("paged", [False, True], ids=["regions", "paged"])
 @pytest.mark.parametrize("Hq,d,bits,R", [(2, 64, 4, 0), (8, 128, 2, 32), (4, 128, 4, 128)])
 def test_row_operations_random_walk(paged, Hq, d, bits, R):
