@@ -160,12 +160,32 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
     // matrix layout: n = column (scores) / row (values) / channel in a tile, rho = lane group
     const int n = lane & 15, rho = lane >> 4;
     const int gl = n >> 2, dq = n & 3;  // the query of score columns 4gl .. 4gl+3, and a value group
-    const int split = blockIdx.x;
-    const int64_t u = dispatch_unit<RAGGED>(a, blockIdx.y);
     const int group = g.n_q_heads / g.n_kv_heads;
+    // (split, unit, chunk of four query heads) of this work-group: with one
+    // chunk per KV head, blockIdx = (split, unit). With zc > 1 chunks the grid
+    // is flat and the zc chunks of one (split, unit), which read the same key
+    // blocks, take ids 8 apart: work-groups go to the 8 XCDs in turn, so
+    // they run on one XCD at about the same time, and the later ones find the
+    // blocks in its L2 instead of HBM (padding ids past the last pair exit).
+    const int zc = group / QG;
+    int split, zq;
+    int64_t uy;
+    if (zc == 1) {
+        split = blockIdx.x;
+        uy = blockIdx.y;
+        zq = 0;
+    } else {
+        const int64_t id = blockIdx.x, per = 8 * (int64_t)zc;
+        const int64_t pair = 8 * (id / per) + id % 8;
+        if (pair >= (int64_t)a.n_split * g.batch * g.n_kv_heads) return;
+        zq = (int)(id % per / 8);
+        split = (int)(pair % a.n_split);
+        uy = pair / a.n_split;
+    }
+    const int64_t u = dispatch_unit<RAGGED>(a, uy);
     const int64_t b = u / g.n_kv_heads;
     const int h = (int)(u % g.n_kv_heads);
-    const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)blockIdx.z * QG;
+    const size_t row0 = (size_t)b * g.n_q_heads + (size_t)h * group + (size_t)zq * QG;
     const float scale = a.scale_log2;
 
     // this unit's counters (its batch row's, when the rows differ in length)
@@ -361,7 +381,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void attend_gqa_kernel(con
     const uint8_t* rbase = g.base + g.off_ring + (size_t)u * g.ring_unit_stride;
     const int ring = (int)g.ring_slots;
     const int slot0 = (int)(cnt.n_quant % g.ring_slots);
-    if (cnt.t_new >= 0 && split == cnt.n_split - 1 && blockIdx.z == 0 && wave == 0)
+    if (cnt.t_new >= 0 && split == cnt.n_split - 1 && zq == 0 && wave == 0)
         write_new_token<D>(a, u, cnt.t_new, rbase);
     // scores, softmax, weight digits of one block
     auto key_math = [&](const R& r, int k_slot) {
@@ -718,8 +738,12 @@ template <int BITS>
 hipError_t gqa_launch(const AttendArgs& a, hipStream_t s) {
     constexpr int NW = attend_waves(4, 128);
     constexpr int NWR = attend_waves_rows(4, 128);
-    const int group = a.g.n_q_heads / a.g.n_kv_heads;
-    const dim3 grid((unsigned)a.n_split, (unsigned)((int64_t)a.g.batch * a.g.n_kv_heads), (unsigned)(group / 4));
+    const int zc = a.g.n_q_heads / a.g.n_kv_heads / 4;
+    const int64_t units = (int64_t)a.g.batch * a.g.n_kv_heads;
+    // one chunk of four query heads: (split, unit); more: flat, the chunks of a
+    // (split, unit) 8 ids apart, the pairs padded to a multiple of 8
+    const dim3 grid = zc == 1 ? dim3((unsigned)a.n_split, (unsigned)units, 1u)
+                              : dim3((unsigned)(8 * (int64_t)zc * ((a.n_split * units + 7) / 8)), 1u, 1u);
     if (a.rows.n)
         attend_gqa_kernel<128, BITS, NWR, true><<<grid, 64 * NWR, 0, s>>>(a);
     else

@@ -468,6 +468,7 @@ def _check_bytes(cache, ocs):
     (3, 1, 4, 128, 2, 32, [64, 1000, 31]),            # four-query kernel at b = 2, small residual
     (3, 2, 4, 64, 2, 64, [300, 1, 97]),               # d = 64, two query heads per KV head
     (2, 1, 2, 256, 4, 128, [129, 517]),               # d = 256
+    (3, 2, 16, 128, 2, 32, [400, 2, 1100]),           # eight query heads per KV head: two chunks on one XCD
     (2, 1, 4, 256, 2, 64, [300, 45]),                 # four query heads on the vector kernel (d = 256)
 ])
 def test_ragged_rows_parity(B, Hkv, Hq, d, bits, R, lens):
